@@ -1,0 +1,251 @@
+"""Throughput of the NVFP4 path on one MI355X.
+
+One step is the whole path over the large MLP weight (bf16 28672 x 8192, the
+largest workload): fused amax + fake-quant, fused amax + quantize-pack, and
+dequant-unpack of the packed result.  Inputs are resident in HBM before the
+timed region.  The step is issued as the library calls
+
+    nvfp4_amax(x)                    -> a1        \\ = nvfp4_fake_quant(x, amax_in=NULL)
+    nvfp4_fake_quant(x, amax_in=a1)  -> y         /
+    nvfp4_amax(x)                    -> a2        \\ = nvfp4_quantize_pack(x, amax_in=NULL)
+    nvfp4_quantize_pack(x, amax_in=a2)            /
+    nvfp4_dequant_unpack(...)        -> y2
+
+which enqueue exactly the kernels of the two fused calls, with HIP events
+recorded between them on the launch stream so every kernel is timed live.
+
+Prints one JSON line on stdout (logs go to stderr):
+  value      algorithmic GB/s of the whole step (13.125 bytes per element)
+  roofline   the dominant kernel's algorithmic GB/s against 8 TB/s HBM
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# bytes per element each op must move (read + write), from the method itself
+BYTES_PER_ELEM = {
+    "amax": 2.0,                 # read x
+    "fake_quant": 4.0,           # read x, write y (amax given)
+    "quantize_pack": 2.5625,     # read x, write 1/2 byte code + 1/16 byte scale
+    "dequant_unpack": 2.5625,    # read codes + scales, write y
+}
+STEP_BYTES_PER_ELEM = (2 * BYTES_PER_ELEM["amax"] + BYTES_PER_ELEM["fake_quant"]
+                       + BYTES_PER_ELEM["quantize_pack"] + BYTES_PER_ELEM["dequant_unpack"])
+KERNEL_NAMES = {
+    "amax": "k_amax",
+    "fake_quant": "k_fake_quant",
+    "quantize_pack": "k_quantize_pack",
+    "dequant_unpack": "k_dequant_unpack",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    with open(os.path.join(ROOT, "fp4_block_fake_amd", "csrc", "nvfp4.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch measured by rocprofv3 counters, if taken on the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(x, rows):
+    import numpy as np
+
+    import oracle
+    sample = np.ascontiguousarray(x[:rows])
+    n = sample.size
+    t0 = time.perf_counter()
+    a = oracle.amax(sample)
+    oracle.fake_quant(sample, a)
+    a = oracle.amax(sample)
+    packed, scales, gs = oracle.quantize(sample, a)
+    oracle.dequantize(packed, scales, gs, sample.shape[1])
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(STEP_BYTES_PER_ELEM * n / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "first %d of %d rows (%d elements), one step: amax+fake-quant, "
+                  "amax+quantize-pack, dequant-unpack; %.1f s single-threaded" % (rows, x.shape[0], n, dt),
+        "elements_per_s": round(n / dt, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rows", type=int, default=28672)
+    ap.add_argument("--cols", type=int, default=8192)
+    ap.add_argument("--cpu-rows", type=int, default=8192, help="rows of the oracle's CPU sample (0: skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only; this build has no multi-GPU path. Sharded "
+              "tensors would need one 4-byte max all-reduce of the amax per tensor.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp4_block_fake_amd as nv
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating c5 weight %dx%d" % (args.rows, args.cols))
+    x_host = synth.c5_weight(rows=args.rows, cols=args.cols)
+    rows, cols = x_host.shape
+    n = rows * cols
+    x = torch.from_numpy(x_host.view(np.int16)).view(torch.bfloat16).to(dev)
+    y = torch.empty_like(x)
+    y2 = torch.empty_like(x)
+    packed = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    gs = torch.empty(1, dtype=torch.float32, device=dev)
+    a1 = torch.empty(1, dtype=torch.float32, device=dev)
+    a2 = torch.empty(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    ops = ["amax", "fake_quant", "amax", "quantize_pack", "dequant_unpack"]
+
+    def step(events=None):
+        calls = [
+            lambda: nv.nvfp4_amax(x, amax=a1),
+            lambda: nv.nvfp4_fake_quant(x, y=y, amax_in=a1),
+            lambda: nv.nvfp4_amax(x, amax=a2),
+            lambda: nv.nvfp4_quantize_pack(x, amax_in=a2, packed=packed, scales=scales, global_scale=gs),
+            lambda: nv.nvfp4_dequant_unpack(packed, scales, gs, y=y2),
+        ]
+        for i, c in enumerate(calls):
+            if events is not None:
+                events[i].record(stream)
+            c()
+        if events is not None:
+            events[len(calls)].record(stream)
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(ev[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    per_op_ms = {}
+    for i, name in enumerate(ops):
+        key = name if name not in per_op_ms else name + "_2"
+        per_op_ms[key] = sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(args.steps)) / args.steps
+    op_report = {}
+    for key, ms in per_op_ms.items():
+        base = key.replace("_2", "")
+        op_report[key] = {"us": round(ms * 1e3, 2),
+                          "gbs": round(BYTES_PER_ELEM[base] * n / (ms * 1e-3) / 1e9, 1)}
+    fused_fq_ms = per_op_ms["amax"] + per_op_ms["fake_quant"]
+    fused_qp_ms = per_op_ms["amax_2"] + per_op_ms["quantize_pack"]
+    op_report["fused_amax_fake_quant"] = {"us": round(fused_fq_ms * 1e3, 2),
+                                          "gbs": round(6.0 * n / (fused_fq_ms * 1e-3) / 1e9, 1)}
+    op_report["fused_amax_quantize_pack"] = {"us": round(fused_qp_ms * 1e3, 2),
+                                             "gbs": round(4.5625 * n / (fused_qp_ms * 1e-3) / 1e9, 1)}
+
+    # dominant kernel: the single launch with the largest share of the step
+    dom = max(("fake_quant", "quantize_pack", "dequant_unpack", "amax"), key=lambda k: per_op_ms[k])
+    dom_bytes = BYTES_PER_ELEM[dom] * n
+    achieved = dom_bytes / (per_op_ms[dom] * 1e-3) / 1e9
+    traffic = read_traffic(KERNEL_NAMES[dom], "c5")
+
+    # a plain copy of the same tensor, as the practical HBM ceiling on this machine
+    for _ in range(3):
+        y.copy_(x)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        y.copy_(x)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 4.0 * n * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+
+    value = STEP_BYTES_PER_ELEM * n / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": "NVFP4 fake-quant / quantize-pack GB/s and % of HBM peak on 1 MI355X",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,0.015) with 0.01% Laplace x30 outliers)",
+        "config": {
+            "workload": "c5: bf16 MLP weight %dx%d, one step = amax+fake-quant, amax+quantize-pack, "
+                        "dequant-unpack" % (rows, cols),
+            "rows": rows, "cols": cols, "block": 16, "io": "bf16 in/out, uint8 nibbles + E4M3 scales",
+            "bytes_per_element_step": STEP_BYTES_PER_ELEM,
+            "parallelism": "single GPU",
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "elements_per_s": round(n / (ms_per_step * 1e-3), 1),
+        "ops": op_report,
+        "copy_gbs": round(copy_gbs, 1),
+        "roofline": {
+            "kernel": KERNEL_NAMES[dom],
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": dom_bytes,
+            "avg_launch_us": round(per_op_ms[dom] * 1e3, 2),
+        },
+        "cpu_baseline": None,
+    }
+    if args.cpu_rows > 0:
+        log("cpu baseline: oracle on %d rows" % args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(x_host, min(args.cpu_rows, rows))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

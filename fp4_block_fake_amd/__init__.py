@@ -1,0 +1,187 @@
+"""Python binding of libnvfp4.so: NVFP4 two-level block quantization on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``csrc/nvfp4.hip``; torch supplies device memory and the current
+stream.  The functions carry the C ABI's names and semantics (see
+``include/nvfp4.h``); outputs that are not passed in are allocated here with
+torch.  Importing this package fails when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "NVFP4Error", "OBS_STATIC_MINMAX", "OBS_EMA", "lib", "library_path",
+    "nvfp4_amax", "nvfp4_fake_quant", "nvfp4_quantize_pack", "nvfp4_dequant_unpack",
+    "nvfp4_observer_update", "nvfp4_strerror", "FakeQuantSTE",
+]
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
+
+OBS_STATIC_MINMAX = 0
+OBS_EMA = 1
+
+_EXPORTS = ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_quantize_pack", "nvfp4_dequant_unpack",
+            "nvfp4_observer_update", "nvfp4_strerror")
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s: %s (status %d)" % (what, nvfp4_strerror(status), status))
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(library_path):
+        raise ImportError("libnvfp4.so is not built (%s); run "
+                          "`python fp4_block_fake_amd/_build.py` or __graft_entry__.build()" % library_path)
+    so = ctypes.CDLL(library_path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    so.nvfp4_amax.argtypes = [P, P, I, P, I, P]
+    so.nvfp4_fake_quant.argtypes = [P, P, I64, I64, P, P, P]
+    so.nvfp4_quantize_pack.argtypes = [P, I64, I64, P, P, P, P, P, P]
+    so.nvfp4_dequant_unpack.argtypes = [P, P, P, I64, I64, P, P]
+    so.nvfp4_observer_update.argtypes = [P, P, I, ctypes.c_float, P]
+    so.nvfp4_strerror.argtypes = [I]
+    so.nvfp4_strerror.restype = ctypes.c_char_p
+    for name in _EXPORTS[:-1]:
+        getattr(so, name).restype = I
+    return so
+
+
+lib = _load()
+
+
+def nvfp4_strerror(status: int) -> str:
+    return lib.nvfp4_strerror(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise NVFP4Error(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _matrix(x: torch.Tensor, name: str):
+    if not x.is_cuda or x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("%s must be a contiguous 2-D bfloat16 CUDA tensor" % name)
+    return x.shape
+
+
+def _scalar(device, t=None, fill=None):
+    if t is None:
+        t = torch.empty(1, dtype=torch.float32, device=device)
+        if fill is not None:
+            t.fill_(fill)
+    elif not t.is_cuda or t.dtype != torch.float32 or t.numel() != 1:
+        raise ValueError("scalars are 1-element float32 CUDA tensors")
+    return t
+
+
+def nvfp4_amax(tensors, amax: torch.Tensor | None = None, accumulate: bool = False) -> torch.Tensor:
+    """max|x| over one bf16 tensor or a list of fused siblings -> 1-element fp32 device tensor."""
+    if isinstance(tensors, torch.Tensor):
+        tensors = [tensors]
+    if not tensors:
+        raise ValueError("nvfp4_amax needs at least one tensor")
+    for t in tensors:
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("amax inputs must be contiguous bfloat16 CUDA tensors")
+    dev = tensors[0].device
+    amax = _scalar(dev, amax)
+    ptrs = (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+    ns = (ctypes.c_int64 * len(tensors))(*[t.numel() for t in tensors])
+    _check(lib.nvfp4_amax(ptrs, ns, len(tensors), _ptr(amax), int(bool(accumulate)), _stream(dev)),
+           "nvfp4_amax")
+    return amax
+
+
+def nvfp4_fake_quant(x: torch.Tensor, y: torch.Tensor | None = None,
+                     amax_in: torch.Tensor | None = None,
+                     amax_out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 [R, C] -> fake-quantized bf16 [R, C].  Without amax_in the amax is computed
+    first (into amax_out, allocated when not given and then reachable as y.amax)."""
+    rows, cols = _matrix(x, "x")
+    if y is None:
+        y = torch.empty_like(x)
+    _matrix(y, "y")
+    if amax_in is not None:
+        _scalar(x.device, amax_in)
+    elif amax_out is None:
+        amax_out = _scalar(x.device)
+    _check(lib.nvfp4_fake_quant(_ptr(x), _ptr(y), rows, cols, _ptr(amax_in), _ptr(amax_out),
+                                _stream(x.device)), "nvfp4_fake_quant")
+    return y
+
+
+def nvfp4_quantize_pack(x: torch.Tensor, amax_in: torch.Tensor | None = None,
+                        amax_out: torch.Tensor | None = None, packed: torch.Tensor | None = None,
+                        scales: torch.Tensor | None = None,
+                        global_scale: torch.Tensor | None = None):
+    """bf16 [R, C] -> (packed uint8 [R, C/2], E4M3 scale bytes uint8 [R, C/16], fp32 gs [1])."""
+    rows, cols = _matrix(x, "x")
+    dev = x.device
+    if packed is None:
+        packed = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    global_scale = _scalar(dev, global_scale)
+    if amax_in is None and amax_out is None:
+        amax_out = _scalar(dev)
+    for t, shape in ((packed, (rows, cols // 2)), (scales, (rows, cols // 16))):
+        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("packed/scales must be contiguous uint8 CUDA tensors of shape %s" % (shape,))
+    _check(lib.nvfp4_quantize_pack(_ptr(x), rows, cols, _ptr(amax_in), _ptr(amax_out), _ptr(packed),
+                                   _ptr(scales), _ptr(global_scale), _stream(dev)),
+           "nvfp4_quantize_pack")
+    return packed, scales, global_scale
+
+
+def nvfp4_dequant_unpack(packed: torch.Tensor, scales: torch.Tensor, global_scale: torch.Tensor,
+                         y: torch.Tensor | None = None) -> torch.Tensor:
+    """(packed [R, C/2], scales [R, C/16], gs) -> bf16 [R, C]."""
+    if packed.dtype != torch.uint8 or packed.dim() != 2 or not packed.is_cuda or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous 2-D uint8 CUDA tensor")
+    rows, cols = packed.shape[0], packed.shape[1] * 2
+    if tuple(scales.shape) != (rows, cols // 16) or scales.dtype != torch.uint8 or not scales.is_contiguous():
+        raise ValueError("scales must be contiguous uint8 [%d, %d]" % (rows, cols // 16))
+    _scalar(packed.device, global_scale)
+    if y is None:
+        y = torch.empty((rows, cols), dtype=torch.bfloat16, device=packed.device)
+    _matrix(y, "y")
+    _check(lib.nvfp4_dequant_unpack(_ptr(packed), _ptr(scales), _ptr(global_scale), rows, cols,
+                                    _ptr(y), _stream(packed.device)), "nvfp4_dequant_unpack")
+    return y
+
+
+def nvfp4_observer_update(state: torch.Tensor, cur: torch.Tensor, mode: int = OBS_STATIC_MINMAX,
+                          decay: float = 0.01) -> torch.Tensor:
+    """One observer step on device scalars, in place on ``state`` (initialise it to -1)."""
+    _scalar(state.device, state)
+    _scalar(state.device, cur)
+    _check(lib.nvfp4_observer_update(_ptr(state), _ptr(cur), int(mode), float(decay),
+                                     _stream(state.device)), "nvfp4_observer_update")
+    return state
+
+
+class FakeQuantSTE(torch.autograd.Function):
+    """Fake-quant forward through the library; identity backward (straight-through
+    estimator, verl QATLinear page section 2)."""
+
+    @staticmethod
+    def forward(ctx, x, amax_in=None):
+        return nvfp4_fake_quant(x.contiguous(), amax_in=amax_in)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        return grad_out, None

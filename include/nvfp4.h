@@ -1,0 +1,160 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4.so: NVFP4 two-level block quantization of 2-D
+ * bf16 tensors on an AMD Instinct MI355X (gfx950).
+ *
+ * The method (what each call computes) is the one described by
+ *   - the VideoX-Fun page "videox_fun/utils/fp4_optimization.py": module
+ *     constants, quantize_weight_to_float4, dequantize_weight_from_float4,
+ *     _float4_round;
+ *   - the verl tutorial page "linear.py -- QATLinear": section 1 (FP4
+ *     fake-quant kernel), 2 (straight-through estimator), 4 (fused-sibling
+ *     weight amax), 5 (activation observer).
+ *
+ * Numerics, fixed for every call (all arithmetic IEEE binary32, no FMA
+ * contraction, subnormals kept):
+ *   amax   = max |x|                                   (raw, no clamp)
+ *   gs     = 2688 / max(amax, 1e-12f)                   2688 = 448 * 6
+ *   per 16-element block of one row:
+ *     S    = E4M3_RNE_SATURATE((block_amax / 6) * gs)   one byte
+ *     sd   = decode(S) / gs ;  sq = max(sd, 1e-12f)
+ *     q    = x / sq ;  idx = E2M1 round-to-nearest-even of min(|q|, 6)
+ *            onto {0, .5, 1, 1.5, 2, 3, 4, 6}
+ *     code = idx | 8 * (q < 0)                         4 bits
+ *   fake-quant / unpack output = bf16_RNE(LUT[code] * sd), LUT[8..15] = -LUT[0..7]
+ *
+ * Conventions shared by every call:
+ *   - Tensor pointers are DEVICE pointers; tensors are row-major and
+ *     contiguous (row stride = cols).  bf16 travels as 16-bit patterns.
+ *   - The caller owns all memory.  The library allocates nothing and keeps no
+ *     mutable state between calls; calls on different streams may run
+ *     concurrently as long as their buffers do not overlap.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and never synchronises the host; results are ready
+ *     when the stream reaches them.
+ *   - Arguments are checked on the host before anything is enqueued; a failed
+ *     check returns an error code and enqueues nothing.  A kernel that fails to
+ *     launch returns NVFP4_ERR_HIP.  Asynchronous device faults surface at the
+ *     caller's next synchronisation.
+ *   - Inputs must be finite; NaN and Inf inputs give unspecified bytes.
+ *   - Shapes: rows >= 0, cols >= 16 and cols % 16 == 0 (blocks never straddle
+ *     rows).  rows == 0 is a valid empty tensor.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nvfp4_status {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL = 1,     /* a required pointer is NULL                          */
+    NVFP4_ERR_SHAPE = 2,    /* rows < 0, cols < 16, cols % 16 != 0, size overflow  */
+    NVFP4_ERR_ALIGN = 3,    /* a pointer is not aligned as the call requires       */
+    NVFP4_ERR_OVERLAP = 4,  /* an output overlaps an input or another output       */
+    NVFP4_ERR_ARG = 5,      /* a bad mode, decay, or group count                   */
+    NVFP4_ERR_HIP = 6       /* the HIP runtime refused a launch                    */
+} nvfp4_status;
+
+enum {
+    NVFP4_OBS_STATIC_MINMAX = 0,  /* running maximum of the observed amax          */
+    NVFP4_OBS_EMA = 1             /* exponential moving average of the amax        */
+};
+
+/* Largest number of tensors one nvfp4_amax launch covers; longer lists are
+ * split into several launches on the same stream. */
+#define NVFP4_AMAX_GROUP_MAX 8
+
+/*
+ * nvfp4_amax -- per-tensor |x| maximum, or the shared maximum of fused
+ * siblings (verl QATLinear page, section 4: the max over every sibling's
+ * weight.abs().max(); VideoX-Fun page, quantize_weight_to_float4: the
+ * tensor-wide abs().amax()).
+ *
+ *   xs[i]      device pointer to numels[i] bf16 values (any shape, contiguous),
+ *              16-byte aligned; may be NULL when numels[i] == 0
+ *   numels[i]  element count of tensor i, >= 0
+ *   n          number of tensors, >= 1 (xs and numels are HOST arrays of n)
+ *   amax       device fp32 scalar, 4-byte aligned.  accumulate == 0:
+ *              *amax := max over the group (+0.0 for an all-empty group);
+ *              accumulate != 0: *amax := max(*amax, max over the group), where
+ *              a negative prior value (such as -1) counts as "none".
+ * Errors: NULL (xs, numels, amax, or xs[i] with numels[i] > 0), SHAPE
+ * (numels[i] < 0), ARG (n < 1), ALIGN, HIP.
+ */
+nvfp4_status nvfp4_amax(const void* const* xs, const int64_t* numels, int n,
+                        float* amax, int accumulate, void* stream);
+
+/*
+ * nvfp4_fake_quant -- bf16 [rows, cols] -> bf16 [rows, cols] fake-quantized
+ * values: quantize then dequantize (verl QATLinear page, section 1, the
+ * rescaled grid value; VideoX-Fun page, the divide-by-gs scale convention).
+ * Its straight-through backward (section 2) is the identity and has no call.
+ *
+ *   x, y       device bf16, 16-byte aligned.  y == x (exact in-place) is allowed;
+ *              any other overlap is an error.
+ *   amax_in    NULL: the amax is computed from x first and written to amax_out
+ *              (required then).  Non-NULL: device fp32 amax to use as is (a
+ *              shared sibling amax or an observer state); x is read once.
+ *   amax_out   device fp32, written only when amax_in is NULL; may be NULL otherwise.
+ */
+nvfp4_status nvfp4_fake_quant(const void* x, void* y, int64_t rows, int64_t cols,
+                              const float* amax_in, float* amax_out, void* stream);
+
+/*
+ * nvfp4_quantize_pack -- bf16 [rows, cols] -> packed NVFP4 (VideoX-Fun page,
+ * quantize_weight_to_float4, returning nibbles, E4M3 block scales and the
+ * fp32 per-tensor factor).
+ *
+ *   x             device bf16 [rows, cols], 16-byte aligned
+ *   amax_in/out   as for nvfp4_fake_quant
+ *   packed        device uint8 [rows, cols/2], 8-byte aligned; byte i of a row
+ *                 holds the code of column 2i in its low nibble and of column
+ *                 2i+1 in its high nibble
+ *   scales        device uint8 [rows, cols/16], E4M3 (float8_e4m3fn) bytes,
+ *                 row-major, one per block
+ *   global_scale  device fp32: gs (not the amax), 4-byte aligned
+ * Outputs must not overlap x, amax_in or each other.
+ */
+nvfp4_status nvfp4_quantize_pack(const void* x, int64_t rows, int64_t cols,
+                                 const float* amax_in, float* amax_out,
+                                 uint8_t* packed, uint8_t* scales, float* global_scale,
+                                 void* stream);
+
+/*
+ * nvfp4_dequant_unpack -- packed NVFP4 -> bf16 [rows, cols] (VideoX-Fun page,
+ * dequantize_weight_from_float4: nibble -> E2M1 value, times
+ * decode(scale) / gs, rounded to bf16).  Layouts as nvfp4_quantize_pack writes
+ * them.  packed 8-byte aligned, y 16-byte aligned; y must not overlap the inputs.
+ */
+nvfp4_status nvfp4_dequant_unpack(const uint8_t* packed, const uint8_t* scales,
+                                  const float* global_scale, int64_t rows, int64_t cols,
+                                  void* y, void* stream);
+
+/*
+ * nvfp4_observer_update -- one activation-observer step on device scalars
+ * (verl QATLinear page, section 5):
+ *   NVFP4_OBS_STATIC_MINMAX:  *state := max(*state, *cur)
+ *   NVFP4_OBS_EMA:            *state := (1 - decay) * *state + decay * *cur
+ *                             (each product and the sum rounded; 1 - decay in fp32)
+ * A negative *state (the -1 initial buffer value) means "no observation yet":
+ * the update then stores *cur for either mode.  The updated state is the amax
+ * to pass as amax_in when fake-quantizing the same activation.
+ *   state, cur  device fp32, 4-byte aligned (cur may equal state)
+ *   decay       EMA weight of the new observation, 0 < decay <= 1; ignored for
+ *               the static observer
+ * Errors: NULL, ALIGN, ARG (mode not 0/1, decay out of range), HIP.
+ */
+nvfp4_status nvfp4_observer_update(float* state, const float* cur, int mode, float decay,
+                                   void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* nvfp4_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

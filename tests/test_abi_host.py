@@ -1,0 +1,135 @@
+"""C ABI checks that need no GPU: the library loads, exports what include/nvfp4.h
+declares, and rejects bad arguments on the host before enqueuing anything.
+
+The pointers below are never dereferenced: every call here fails validation,
+which runs before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+nv = pytest.importorskip("fp4_block_fake_amd")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_OVERLAP, ERR_ARG = 0, 1, 2, 3, 4, 5
+A = 0x7F0000000000            # a 256-byte-aligned fake device address
+N = None
+
+
+def P(addr):
+    return ctypes.c_void_p(addr)
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "nvfp4.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_quantize_pack", "nvfp4_dequant_unpack",
+              "nvfp4_observer_update", "nvfp4_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    so = ctypes.CDLL(nv.library_path)
+    for name in declared_functions():
+        assert hasattr(so, name), name
+
+
+def test_strerror_names_every_status():
+    for s in range(7):
+        assert nv.nvfp4_strerror(s) and nv.nvfp4_strerror(s) != "unknown status"
+    assert nv.nvfp4_strerror(99) == "unknown status"
+
+
+def fq(x, y, rows, cols, amax_in, amax_out):
+    return nv.lib.nvfp4_fake_quant(P(x), P(y), rows, cols, P(amax_in), P(amax_out), None)
+
+
+def test_fake_quant_validation():
+    assert fq(A, A + (1 << 30), 4, 8, None, A + (2 << 30)) == ERR_SHAPE          # cols < 16
+    assert fq(A, A + (1 << 30), 4, 24, None, A + (2 << 30)) == ERR_SHAPE         # cols % 16
+    assert fq(A, A + (1 << 30), -1, 16, None, A + (2 << 30)) == ERR_SHAPE
+    assert fq(A, A + (1 << 30), 1 << 40, 1 << 40, None, A + (2 << 30)) == ERR_SHAPE  # overflow
+    assert fq(None, A, 4, 16, None, A + (2 << 30)) == ERR_NULL
+    assert fq(A, None, 4, 16, None, A + (2 << 30)) == ERR_NULL
+    assert fq(A, A + (1 << 30), 4, 16, None, None) == ERR_NULL                   # amax needed
+    assert fq(A + 2, A + (1 << 30), 4, 16, None, A + (2 << 30)) == ERR_ALIGN
+    assert fq(A, A + (1 << 30) + 8, 4, 16, None, A + (2 << 30)) == ERR_ALIGN
+    assert fq(A, A + (1 << 30), 4, 16, None, A + (2 << 30) + 1) == ERR_ALIGN
+    assert fq(A, A + 16, 4, 16, None, A + (2 << 30)) == ERR_OVERLAP             # partial overlap
+    assert fq(A, A + (1 << 30), 4, 16, None, A + 64) == ERR_OVERLAP             # amax inside x
+    assert fq(A, A + (1 << 30), 4, 16, A + (1 << 30) + 4, None) == ERR_OVERLAP  # amax_in inside y
+
+
+def test_quantize_pack_validation():
+    q = nv.lib.nvfp4_quantize_pack
+    x, p, s, g, a = A, A + (1 << 30), A + (2 << 30), A + (3 << 30), A + (4 << 30)
+    assert q(P(x), 4, 20, None, P(a), P(p), P(s), P(g), None) == ERR_SHAPE
+    assert q(P(x), 4, 16, None, None, P(p), P(s), P(g), None) == ERR_NULL
+    assert q(P(x), 4, 16, None, P(a), None, P(s), P(g), None) == ERR_NULL
+    assert q(P(x), 4, 16, None, P(a), P(p), P(s), None, None) == ERR_NULL
+    assert q(P(x), 4, 16, None, P(a), P(p + 4), P(s), P(g), None) == ERR_ALIGN
+    assert q(P(x), 4, 16, None, P(a), P(p), P(s), P(g + 2), None) == ERR_ALIGN
+    assert q(P(x), 4, 16, None, P(a), P(x + 8), P(s), P(g), None) == ERR_OVERLAP   # packed in x
+    assert q(P(x), 4, 16, None, P(a), P(p), P(p + 16), P(g), None) == ERR_OVERLAP  # scales in packed
+    assert q(P(x), 4, 16, None, P(s), P(p), P(s), P(g), None) == ERR_OVERLAP       # amax_out on scales
+    assert q(P(x), 4, 16, P(g), None, P(p), P(s), P(g), None) == ERR_OVERLAP       # gs on amax_in
+
+
+def test_dequant_unpack_validation():
+    d = nv.lib.nvfp4_dequant_unpack
+    p, s, g, y = A, A + (1 << 30), A + (2 << 30), A + (3 << 30)
+    assert d(P(p), P(s), P(g), 4, 17, P(y), None) == ERR_SHAPE
+    assert d(None, P(s), P(g), 4, 16, P(y), None) == ERR_NULL
+    assert d(P(p), P(s), P(g), 4, 16, None, None) == ERR_NULL
+    assert d(P(p + 1), P(s), P(g), 4, 16, P(y), None) == ERR_ALIGN
+    assert d(P(p), P(s), P(g), 4, 16, P(y + 8), None) == ERR_ALIGN
+    assert d(P(p), P(s), P(g), 4, 16, P(p), None) == ERR_OVERLAP
+    assert d(P(p), P(s), P(g), 4, 16, P(g - 16), None) == ERR_OVERLAP
+
+
+def test_amax_validation():
+    am = nv.lib.nvfp4_amax
+    ptrs = (ctypes.c_void_p * 2)(A, A + (1 << 30))
+    ns = (ctypes.c_int64 * 2)(64, 64)
+    assert am(None, ns, 2, P(A + (2 << 30)), 0, None) == ERR_NULL
+    assert am(ptrs, ns, 2, None, 0, None) == ERR_NULL
+    assert am(ptrs, ns, 0, P(A + (2 << 30)), 0, None) == ERR_ARG
+    bad_n = (ctypes.c_int64 * 2)(64, -1)
+    assert am(ptrs, bad_n, 2, P(A + (2 << 30)), 0, None) == ERR_SHAPE
+    nul = (ctypes.c_void_p * 2)(A, None)
+    assert am(nul, ns, 2, P(A + (2 << 30)), 0, None) == ERR_NULL
+    mis = (ctypes.c_void_p * 2)(A, A + 2)
+    assert am(mis, ns, 2, P(A + (2 << 30)), 0, None) == ERR_ALIGN
+    assert am(ptrs, ns, 2, P(A + 8), 0, None) == ERR_OVERLAP
+    assert am(ptrs, ns, 2, P(A + (2 << 30) + 2), 0, None) == ERR_ALIGN
+
+
+def test_observer_validation():
+    ob = nv.lib.nvfp4_observer_update
+    s, c = P(A), P(A + 256)
+    assert ob(None, c, 0, 0.01, None) == ERR_NULL
+    assert ob(s, None, 0, 0.01, None) == ERR_NULL
+    assert ob(P(A + 2), c, 0, 0.01, None) == ERR_ALIGN
+    assert ob(s, c, 2, 0.01, None) == ERR_ARG
+    assert ob(s, c, -1, 0.01, None) == ERR_ARG
+    for bad in (0.0, -0.5, 1.5, float("nan")):
+        assert ob(s, c, 1, bad, None) == ERR_ARG
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        nv.nvfp4_fake_quant(x)
+    with pytest.raises(ValueError):
+        nv.nvfp4_quantize_pack(x)
+    with pytest.raises(ValueError):
+        nv.nvfp4_amax([x])
