@@ -51,10 +51,62 @@
 
 namespace {
 
-constexpr int kThreads = 256;     // 4 waves of 64
-constexpr int kUnroll = 2;        // blocks per lane per iteration (4 x 16 B loads in flight)
-constexpr int kAmaxUnroll = 4;    // 16-byte vectors per lane per amax chunk
-constexpr int kWgPerCu = 8;       // persistent workgroups per CU
+// Launch shape and cache hints per kernel.  The defaults come from sweeps on
+// MI355X (c5 weight, 470 MB); the macros let a build be re-tuned without
+// editing the kernels.
+#ifndef NVFP4_UNROLL
+#define NVFP4_UNROLL 2            // blocks per lane per iteration: fake-quant, pack
+#endif
+#ifndef NVFP4_DQ_UNROLL
+#define NVFP4_DQ_UNROLL 4         // blocks per lane per iteration: unpack
+#endif
+#ifndef NVFP4_AMAX_UNROLL
+#define NVFP4_AMAX_UNROLL 8       // 16-byte vectors per lane per amax chunk
+#endif
+#ifndef NVFP4_AMAX_WG_PER_CU
+#define NVFP4_AMAX_WG_PER_CU 4    // persistent workgroups per CU
+#endif
+#ifndef NVFP4_FQ_WG_PER_CU
+#define NVFP4_FQ_WG_PER_CU 32
+#endif
+#ifndef NVFP4_QP_WG_PER_CU
+#define NVFP4_QP_WG_PER_CU 32
+#endif
+#ifndef NVFP4_DQ_WG_PER_CU
+#define NVFP4_DQ_WG_PER_CU 64
+#endif
+// 1: the quantizing passes walk the tensor from its end, so they start on the
+// data the amax pass read last.  This pays only when the amax pass leaves x in
+// the Infinity Cache, i.e. with NVFP4_AMAX_NT 0; streaming amax loads win more.
+#ifndef NVFP4_REVERSE
+#define NVFP4_REVERSE 0
+#endif
+// non-temporal (streaming) hints on loads (LD) and stores (ST)
+#ifndef NVFP4_AMAX_NT
+#define NVFP4_AMAX_NT 1
+#endif
+#ifndef NVFP4_FQ_NT_LD
+#define NVFP4_FQ_NT_LD 0
+#endif
+#ifndef NVFP4_FQ_NT_ST
+#define NVFP4_FQ_NT_ST 0
+#endif
+#ifndef NVFP4_QP_NT_LD
+#define NVFP4_QP_NT_LD 1
+#endif
+#ifndef NVFP4_QP_NT_ST
+#define NVFP4_QP_NT_ST 1
+#endif
+#ifndef NVFP4_DQ_NT_ST
+#define NVFP4_DQ_NT_ST 0
+#endif
+
+constexpr int kThreads = 256;                    // 4 waves of 64
+constexpr int kUnroll = NVFP4_UNROLL;
+constexpr int kDqUnroll = NVFP4_DQ_UNROLL;
+constexpr int kAmaxUnroll = NVFP4_AMAX_UNROLL;
+constexpr bool kReverse = NVFP4_REVERSE != 0;
+
 constexpr float kEps = 1e-12f;    // clamp of the amax and of the block scale
 constexpr float kGsNumerator = 2688.0f;  // E4M3 max 448 times E2M1 max 6
 
@@ -75,6 +127,35 @@ __device__ __forceinline__ uint32_t pk_top(uint32_t a) { return w32(h2(a) >> (u1
 __device__ __forceinline__ uint32_t pk_mad(uint32_t a, uint32_t b, uint32_t c)
 {
     return w32(h2(a) * h2(b) + h2(c));
+}
+
+// ---------------------------------------------------------------- memory helpers
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint4* p)
+{
+    if (NT)
+        return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+    return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void store16(uint4* p, uint4 v)
+{
+    if (NT)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+    else
+        *p = v;
+}
+template <bool NT>
+__device__ __forceinline__ void store8(uint2* p, uint2 v)
+{
+    if (NT)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x2, v), reinterpret_cast<u32x2*>(p));
+    else
+        *p = v;
 }
 
 // ---------------------------------------------------------------- scalar number formats
@@ -257,6 +338,14 @@ __device__ __forceinline__ void unpack8(const uint4& a, const uint4& b, uint32_t
 
 // ---------------------------------------------------------------- kernels
 
+// i-th block of a pass (or -1 past the end); the pass runs backwards when kReverse.
+__device__ __forceinline__ int64_t walk(int64_t i, int64_t nblocks)
+{
+    if (i >= nblocks)
+        return -1;
+    return kReverse ? nblocks - 1 - i : i;
+}
+
 __global__ void k_set_scalar(float* p, float v) { *p = v; }
 
 struct AmaxGroup {
@@ -276,18 +365,25 @@ __global__ __launch_bounds__(kThreads) void k_amax(AmaxGroup g, float* out)
     constexpr int64_t kChunk = (int64_t)kThreads * kAmaxUnroll;
     uint32_t mx = 0;
     const int64_t total = g.chunk_end[g.count - 1];
+    // chunks only grow along the loop, so the current tensor is cached and
+    // advanced instead of searched for on every chunk
+    int t = 0;
+    int64_t begin = 0, end = g.chunk_end[0], n = g.nvec[0];
+    const uint4* __restrict__ src = g.vec[0];
     for (int64_t c = blockIdx.x; c < total; c += gridDim.x) {
-        int t = 0;
-        while (c >= g.chunk_end[t])
+        while (c >= end) {
             ++t;
-        const int64_t first = (c - (t ? g.chunk_end[t - 1] : 0)) * kChunk + threadIdx.x;
-        const uint4* __restrict__ src = g.vec[t];
-        const int64_t n = g.nvec[t];
+            begin = end;
+            end = g.chunk_end[t];
+            n = g.nvec[t];
+            src = g.vec[t];
+        }
+        const int64_t first = (c - begin) * kChunk + threadIdx.x;
         uint4 v[kAmaxUnroll];
 #pragma unroll
         for (int u = 0; u < kAmaxUnroll; ++u) {
             const int64_t i = first + (int64_t)u * kThreads;
-            v[u] = i < n ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+            v[u] = i < n ? load16<NVFP4_AMAX_NT != 0>(src + i) : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int u = 0; u < kAmaxUnroll; ++u) {
@@ -336,16 +432,16 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant(const uint4* __restrict
         uint4 v[kUnroll][2];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t b = base + (int64_t)u * kThreads;
-            if (b < nblocks) {
-                v[u][0] = x[2 * b];
-                v[u][1] = x[2 * b + 1];
+            const int64_t b = walk(base + (int64_t)u * kThreads, nblocks);
+            if (b >= 0) {
+                v[u][0] = load16<NVFP4_FQ_NT_LD != 0>(x + 2 * b);
+                v[u][1] = load16<NVFP4_FQ_NT_LD != 0>(x + 2 * b + 1);
             }
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t b = base + (int64_t)u * kThreads;
-            if (b < nblocks) {
+            const int64_t b = walk(base + (int64_t)u * kThreads, nblocks);
+            if (b >= 0) {
                 uint32_t w[8];
                 unpack8(v[u][0], v[u][1], w);
                 const Entry e = load_entry(table, block_scale_byte(w, gs), true);
@@ -353,8 +449,8 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant(const uint4* __restrict
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     o[i] = fake_quant_pair(w[i], e);
-                y[2 * b] = make_uint4(o[0], o[1], o[2], o[3]);
-                y[2 * b + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+                store16<NVFP4_FQ_NT_ST != 0>(y + 2 * b, make_uint4(o[0], o[1], o[2], o[3]));
+                store16<NVFP4_FQ_NT_ST != 0>(y + 2 * b + 1, make_uint4(o[4], o[5], o[6], o[7]));
             }
         }
     }
@@ -381,16 +477,16 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack(const uint4* __restr
         uint4 v[kUnroll][2];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t b = base + (int64_t)u * kThreads;
-            if (b < nblocks) {
-                v[u][0] = x[2 * b];
-                v[u][1] = x[2 * b + 1];
+            const int64_t b = walk(base + (int64_t)u * kThreads, nblocks);
+            if (b >= 0) {
+                v[u][0] = load16<NVFP4_QP_NT_LD != 0>(x + 2 * b);
+                v[u][1] = load16<NVFP4_QP_NT_LD != 0>(x + 2 * b + 1);
             }
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t b = base + (int64_t)u * kThreads;
-            if (b < nblocks) {
+            const int64_t b = walk(base + (int64_t)u * kThreads, nblocks);
+            if (b >= 0) {
                 uint32_t w[8];
                 unpack8(v[u][0], v[u][1], w);
                 const uint32_t s = block_scale_byte(w, gs);
@@ -399,8 +495,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack(const uint4* __restr
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     c[i] = code_byte(w[i], e);
-                packed[b] = make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
-                                       c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+                store8<NVFP4_QP_NT_ST != 0>(packed + b, make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
+                                                        c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24));
                 scales[b] = (uint8_t)s;
             }
         }
@@ -450,13 +546,13 @@ __global__ __launch_bounds__(kThreads) void k_dequant_unpack(const uint2* __rest
         build_unpack_entry(threadIdx.x, gs, table + threadIdx.x);
     __syncthreads();
 
-    const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
-    for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < nblocks;
+    const int64_t stride = (int64_t)gridDim.x * kThreads * kDqUnroll;
+    for (int64_t base = (int64_t)blockIdx.x * kThreads * kDqUnroll + threadIdx.x; base < nblocks;
          base += stride) {
-        uint2 p[kUnroll];
-        uint32_t s[kUnroll];
+        uint2 p[kDqUnroll];
+        uint32_t s[kDqUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kDqUnroll; ++u) {
             const int64_t b = base + (int64_t)u * kThreads;
             if (b < nblocks) {
                 p[u] = packed[b];
@@ -464,15 +560,15 @@ __global__ __launch_bounds__(kThreads) void k_dequant_unpack(const uint2* __rest
             }
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < kDqUnroll; ++u) {
             const int64_t b = base + (int64_t)u * kThreads;
             if (b < nblocks) {
                 const uint4 t = table[s[u] & 0x7Fu];
                 uint32_t o[8];
                 unpack_dword(p[u].x, t, o);
                 unpack_dword(p[u].y, t, o + 4);
-                y[2 * b] = make_uint4(o[0], o[1], o[2], o[3]);
-                y[2 * b + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+                store16<NVFP4_DQ_NT_ST != 0>(y + 2 * b, make_uint4(o[0], o[1], o[2], o[3]));
+                store16<NVFP4_DQ_NT_ST != 0>(y + 2 * b + 1, make_uint4(o[4], o[5], o[6], o[7]));
             }
         }
     }
@@ -515,14 +611,14 @@ nvfp4_status check_matrix(int64_t rows, int64_t cols, int64_t* numel)
     return NVFP4_OK;
 }
 
-unsigned persistent_grid(int64_t items, int64_t items_per_wg)
+unsigned persistent_grid(int64_t items, int64_t items_per_wg, int wg_per_cu)
 {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
     const int64_t need = (items + items_per_wg - 1) / items_per_wg;
-    const int64_t cap = (int64_t)cus * kWgPerCu;
+    const int64_t cap = (int64_t)cus * wg_per_cu;
     return (unsigned)(need < 1 ? 1 : (need < cap ? need : cap));
 }
 
@@ -547,7 +643,7 @@ nvfp4_status enqueue_amax(const void* const* xs, const int64_t* numels, int n, f
         chunks += (g.nvec[i] + kChunk - 1) / kChunk;
         g.chunk_end[i] = chunks;
     }
-    k_amax<<<persistent_grid(chunks, 1), kThreads, 0, stream>>>(g, amax);
+    k_amax<<<persistent_grid(chunks, 1, NVFP4_AMAX_WG_PER_CU), kThreads, 0, stream>>>(g, amax);
     return launched();
 }
 
@@ -656,7 +752,7 @@ nvfp4_status nvfp4_fake_quant(const void* x, void* y, int64_t rows, int64_t cols
     if (n == 0)
         return NVFP4_OK;
     const int64_t nblocks = n / 16;
-    k_fake_quant<<<persistent_grid(nblocks, (int64_t)kThreads * kUnroll), kThreads, 0, s>>>(
+    k_fake_quant<<<persistent_grid(nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
         static_cast<const uint4*>(x), static_cast<uint4*>(y), nblocks, a);
     return launched();
 }
@@ -695,7 +791,7 @@ nvfp4_status nvfp4_quantize_pack(const void* x, int64_t rows, int64_t cols,
         a = amax_out;
     }
     const int64_t nblocks = n / 16;
-    k_quantize_pack<<<persistent_grid(nblocks, (int64_t)kThreads * kUnroll), kThreads, 0, s>>>(
+    k_quantize_pack<<<persistent_grid(nblocks, (int64_t)kThreads * kUnroll, NVFP4_QP_WG_PER_CU), kThreads, 0, s>>>(
         static_cast<const uint4*>(x), reinterpret_cast<uint2*>(packed), scales, global_scale,
         nblocks, a);
     return launched();
@@ -722,7 +818,7 @@ nvfp4_status nvfp4_dequant_unpack(const uint8_t* packed, const uint8_t* scales,
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     const int64_t nblocks = n / 16;
-    k_dequant_unpack<<<persistent_grid(nblocks, (int64_t)kThreads * kUnroll), kThreads, 0, s>>>(
+    k_dequant_unpack<<<persistent_grid(nblocks, (int64_t)kThreads * kDqUnroll, NVFP4_DQ_WG_PER_CU), kThreads, 0, s>>>(
         reinterpret_cast<const uint2*>(packed), scales, global_scale, static_cast<uint4*>(y), nblocks);
     return launched();
 }
