@@ -166,18 +166,6 @@ __device__ __forceinline__ float global_scale_of(float amax)
     return kGsNumerator / a;          // IEEE binary32 divide (no fast-math in this build)
 }
 
-// Non-negative binary32 -> E4M3 byte, round-to-nearest-even, saturating at 0x7E (448).
-__device__ __forceinline__ uint32_t e4m3_encode(float v)
-{
-    uint32_t u = __float_as_uint(v);
-    // normal E4M3 (v >= 2^-6): round the binary32 significand to 3 bits, rebias 127 -> 7
-    uint32_t normal = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
-    // subnormal E4M3: multiples of 2^-9; v * 512 is exact, rint rounds half to even
-    uint32_t sub = (uint32_t)__builtin_rintf(v * 512.0f);
-    uint32_t s = v < 0x1p-6f ? sub : normal;
-    return s < 0x7Eu ? s : 0x7Eu;
-}
-
 // E4M3 byte 0..0x7F (sign clear) -> value.  0x7F (NaN) never reaches here as a scale.
 __device__ __forceinline__ float e4m3_decode(uint32_t s)
 {
@@ -227,16 +215,59 @@ __device__ __forceinline__ uint32_t first_at_or_above(double t)
 
 // ---------------------------------------------------------------- per-scale-byte table
 //
-// Entry for scale byte S (12 dwords, three 16-byte LDS reads):
-//   [0] t4 | t4<<16            [1] t6 | t6<<16           [2] (t2-t6) | (t2-t6)<<16
-//   [3] (t0-1) | (t0-1)<<16    [4] t7 | t5<<16           [5] t3 | t1<<16
-//   [6..9] low and high bytes of the eight bf16 outputs, ordered by k = 7 - idx
-//   [10..11] unused
+// Everything a block needs beyond its own data depends only on its E4M3 scale
+// byte S (0..0x7E), so each workgroup tabulates it once, for all 128 bytes, in
+// LDS.  Entry for S (12 dwords, 48 bytes):
+//   [0]  r = 1 / sq (binary32 bits), the multiplier of the fast path
+//   [1]  bit 0: the fast path is exact for every bf16 input under this S
+//   [2]  t4 | t4<<16    [3] t6 | t6<<16    [4] (t2-t6) | (t2-t6)<<16
+//   [5]  (t0-1) | (t0-1)<<16    [6] t7 | t5<<16    [7] t3 | t1<<16
+//   [8..11] low bytes of the eight bf16 outputs bf16(M_i * sd), i = 0..3 and
+//        4..7, then their high bytes (the unpack table layout)
 // t_i (i = 1..7) is the smallest magnitude bit pattern whose E2M1 index is >= i;
 // t0 the smallest whose quotient is nonzero.
-constexpr int kEntryVec = 3;   // uint4 per entry
+//
+// Fast path: q' = fl(x * r) goes through the gfx950 FP4 converter, which rounds
+// a binary32 value to E2M1 with ties to even (checked on every binary32 input).
+// q' can differ from the exact quotient fl(x / sq) in its last bits, and the
+// code differs only if some bf16 magnitude lands on different sides of a
+// decision boundary.  Both decisions are monotone in |x|, so comparing them at
+// the two bf16 values around each exact threshold t_i settles it for every
+// input; an S that fails (or whose t0 is not 1) keeps the threshold path.
+constexpr int kEntryWords = 12;
+constexpr uint32_t kFastExact = 1u;
 
-__device__ void build_entry(uint32_t s, float gs, uint4* dst)
+__device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// Does the fast path pass boundary b (strictly, or at-or-above) for magnitude bits m?
+__device__ __forceinline__ bool fast_passes(uint32_t m, float r, float b, bool strict)
+{
+    const float q = bf16_value(m) * r;
+    return strict ? q > b : q >= b;
+}
+
+// The fast decision agrees with the exact threshold t for every bf16 input.
+__device__ __forceinline__ bool fast_agrees(uint32_t t, float r, float b, bool strict)
+{
+    return fast_passes(t, r, b, strict) && !fast_passes(t - 1u, r, b, strict);
+}
+
+// The eight outputs bf16(M_i * sd) as the unpack table entry: low bytes of
+// i = 0..3, of i = 4..7, then the high bytes in the same order.
+__device__ __forceinline__ uint4 output_entry(float sd)
+{
+    const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        o[i] = bf16_bits(mag[i] * sd);
+    return make_uint4((o[0] & 0xFFu) | (o[1] & 0xFFu) << 8 | (o[2] & 0xFFu) << 16 | (o[3] & 0xFFu) << 24,
+                      (o[4] & 0xFFu) | (o[5] & 0xFFu) << 8 | (o[6] & 0xFFu) << 16 | (o[7] & 0xFFu) << 24,
+                      (o[0] >> 8) | (o[1] >> 8) << 8 | (o[2] >> 8) << 16 | (o[3] >> 8) << 24,
+                      (o[4] >> 8) | (o[5] >> 8) << 8 | (o[6] >> 8) << 16 | (o[7] >> 8) << 24);
+}
+
+__device__ void build_entry(uint32_t s, float gs, uint32_t* dst)
 {
     const float sd = e4m3_decode(s) / gs;          // decoded block scale
     const float sq = sd < kEps ? kEps : sd;        // the divisor of the elements
@@ -249,73 +280,95 @@ __device__ void build_entry(uint32_t s, float gs, uint4* dst)
     const uint32_t t5 = first_above((2.5 + 0x1p-23) * q);
     const uint32_t t6 = first_at_or_above((3.5 - 0x1p-23) * q);
     const uint32_t t7 = first_above((5.0 + 0x1p-22) * q);
-    // outputs by k = 7 - idx: magnitudes 6, 4, 3, 2, 1.5, 1, 0.5, 0 times sd
-    const uint32_t o0 = bf16_bits(6.0f * sd), o1 = bf16_bits(4.0f * sd);
-    const uint32_t o2 = bf16_bits(3.0f * sd), o3 = bf16_bits(2.0f * sd);
-    const uint32_t o4 = bf16_bits(1.5f * sd), o5 = bf16_bits(1.0f * sd);
-    const uint32_t o6 = bf16_bits(0.5f * sd), o7 = bf16_bits(0.0f * sd);
-    const uint32_t d26 = (t2 - t6) & 0xFFFFu;
-    dst[0] = make_uint4(t4 * 0x10001u, t6 * 0x10001u, d26 * 0x10001u, (t0 - 1u) * 0x10001u);
-    dst[1] = make_uint4(t7 | (t5 << 16), t3 | (t1 << 16),
-                        (o0 & 0xFFu) | (o1 & 0xFFu) << 8 | (o2 & 0xFFu) << 16 | (o3 & 0xFFu) << 24,
-                        (o4 & 0xFFu) | (o5 & 0xFFu) << 8 | (o6 & 0xFFu) << 16 | (o7 & 0xFFu) << 24);
-    dst[2] = make_uint4((o0 >> 8) | (o1 >> 8) << 8 | (o2 >> 8) << 16 | (o3 >> 8) << 24,
-                        (o4 >> 8) | (o5 >> 8) << 8 | (o6 >> 8) << 16 | (o7 >> 8) << 24, 0u, 0u);
+    const float r = 1.0f / sq;
+    const bool fast = t0 == 1u &&
+                      fast_agrees(t1, r, 0.25f, true) && fast_agrees(t2, r, 0.75f, false) &&
+                      fast_agrees(t3, r, 1.25f, true) && fast_agrees(t4, r, 1.75f, false) &&
+                      fast_agrees(t5, r, 2.5f, true) && fast_agrees(t6, r, 3.5f, false) &&
+                      fast_agrees(t7, r, 5.0f, true);
+    const uint4 out = output_entry(sd);
+    dst[0] = __float_as_uint(r);
+    dst[1] = fast ? kFastExact : 0u;
+    dst[2] = t4 * 0x10001u;
+    dst[3] = t6 * 0x10001u;
+    dst[4] = ((t2 - t6) & 0xFFFFu) * 0x10001u;
+    dst[5] = (t0 - 1u) * 0x10001u;
+    dst[6] = t7 | (t5 << 16);
+    dst[7] = t3 | (t1 << 16);
+    dst[8] = out.x;
+    dst[9] = out.y;
+    dst[10] = out.z;
+    dst[11] = out.w;
 }
 
-struct Entry {
-    uint32_t t4, t6, d26, t0m1, tab_lo, tab_hi, lo_a, lo_b, hi_a, hi_b;
-};
-
-__device__ __forceinline__ Entry load_entry(const uint4* table, uint32_t s, bool with_outputs)
+// Threshold path: idx for the two magnitudes m (15-bit fields) of one dword,
+// a three-step search over the seven sorted thresholds.
+__device__ __forceinline__ uint32_t threshold_index(uint32_t m, const uint32_t* e)
 {
-    const uint4* e = table + s * kEntryVec;
-    uint4 a = e[0], b = e[1];
-    Entry r{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, 0u, 0u};
-    if (with_outputs) {
-        uint4 c = e[2];
-        r.hi_a = c.x;
-        r.hi_b = c.y;
+    const uint32_t n4 = pk_top(pk_sub(m, e[2]));                // [m < t4]
+    const uint32_t ta = pk_mad(n4, e[4], e[3]);                 // n4 ? t2 : t6
+    const uint32_t na = pk_top(pk_sub(m, ta));
+    const uint32_t j = pk_mad(n4, 0x00020002u, na);             // 0..3
+    const uint32_t sel = pk_mad(j, 0x02020202u, 0x01000100u);   // bytes 2j, 2j+1 per half
+    const uint32_t tb = __builtin_amdgcn_perm(e[7], e[6], sel); // t7, t5, t3, t1 by j
+    const uint32_t nb = pk_top(pk_sub(m, tb));
+    return pk_mad(j, 0x00020002u, nb) ^ 0x00070007u;           // 7 - (2j + nb)
+}
+
+// Codes of four bf16 pairs (8 elements) as one dword of nibbles, threshold path.
+__device__ __forceinline__ uint32_t codes_threshold(const uint32_t* w, const uint32_t* e)
+{
+    uint32_t out = 0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t m = w[p] & 0x7FFF7FFFu;
+        // sign when x < 0 and |x| >= t0 (the quotient does not underflow to zero)
+        const uint32_t neg = w[p] & pk_sub(e[5], m) & 0x80008000u;
+        const uint32_t c = threshold_index(m, e) | (neg >> 12);
+        out |= ((c | (c >> 12)) & 0xFFu) << (8 * p);
     }
-    return r;
+    return out;
 }
 
-// k = 7 - idx for the two magnitudes m (15-bit fields) of one dword
-__device__ __forceinline__ uint32_t reversed_index(uint32_t m, const Entry& e)
-{
-    uint32_t n4 = pk_top(pk_sub(m, e.t4));                   // [m < t4]
-    uint32_t ta = pk_mad(n4, e.d26, e.t6);                   // n4 ? t2 : t6
-    uint32_t na = pk_top(pk_sub(m, ta));
-    uint32_t j = pk_mad(n4, 0x00020002u, na);                // 0..3
-    uint32_t sel = pk_mad(j, 0x02020202u, 0x01000100u);      // bytes 2j, 2j+1 per half
-    uint32_t tb = __builtin_amdgcn_perm(e.tab_hi, e.tab_lo, sel);  // t7, t5, t3, t1 by j
-    uint32_t nb = pk_top(pk_sub(m, tb));
-    return pk_mad(j, 0x00020002u, nb);
-}
-
-// Sign bits (15 and 31) of the two codes: x negative and |x| >= t0.
-__device__ __forceinline__ uint32_t code_signs(uint32_t w, uint32_t m, const Entry& e)
-{
-    return w & pk_sub(e.t0m1, m) & 0x80008000u;
-}
-
-// Two bf16 inputs -> two fake-quantized bf16 outputs.
-__device__ __forceinline__ uint32_t fake_quant_pair(uint32_t w, const Entry& e)
+// Codes of one bf16 pair into byte P of `out`, fast path (converter).
+template <int P>
+__device__ __forceinline__ uint32_t code_pair_fast(uint32_t out, uint32_t w, float r)
 {
     const uint32_t m = w & 0x7FFF7FFFu;
-    const uint32_t k = reversed_index(m, e);
-    const uint32_t sel = k | (k << 8);
-    const uint32_t lo = __builtin_amdgcn_perm(e.lo_b, e.lo_a, sel);
-    const uint32_t hi = __builtin_amdgcn_perm(e.hi_b, e.hi_a, sel);
-    return (hi & 0xFF00FF00u) | (lo & 0x00FF00FFu) | code_signs(w, m, e);
+    // -0.0 must give code 0 (its quotient is not below zero): clear the sign of
+    // a zero magnitude; the packed add sets bit 15 of a half exactly when m != 0
+    const uint32_t v = w & (w32(h2(m) + h2(0x7FFF7FFFu)) | 0x7FFF7FFFu);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, __uint_as_float(v << 16) * r,
+                                                    __uint_as_float(v & 0xFFFF0000u) * r, 1.0f, P);
 }
 
-// Two bf16 inputs -> one byte: code of the first in the low nibble, second in the high.
-__device__ __forceinline__ uint32_t code_byte(uint32_t w, const Entry& e)
+// Codes of four bf16 pairs as one dword of nibbles, fast path.
+__device__ __forceinline__ uint32_t codes_fast(const uint32_t* w, float r)
 {
-    const uint32_t m = w & 0x7FFF7FFFu;
-    const uint32_t c = (reversed_index(m, e) ^ 0x00070007u) | (code_signs(w, m, e) >> 12);
-    return (c | (c >> 12)) & 0xFFu;
+    uint32_t out = 0;
+    out = code_pair_fast<0>(out, w[0], r);
+    out = code_pair_fast<1>(out, w[1], r);
+    out = code_pair_fast<2>(out, w[2], r);
+    out = code_pair_fast<3>(out, w[3], r);
+    return out;
+}
+
+// Eight codes (one dword of nibbles, even element low) -> eight bf16 values in
+// four dwords, through the output entry t of their block.
+__device__ __forceinline__ void decode_dword(uint32_t p, const uint4& t, uint32_t* out)
+{
+    const uint32_t lo = p & 0x07070707u;           // magnitude index of even columns
+    const uint32_t hi = (p >> 4) & 0x07070707u;    // ... of odd columns
+    const uint32_t sl = (p << 4) & 0x80808080u;    // sign of even columns at bit 7
+    const uint32_t sh = p & 0x80808080u;           // sign of odd columns at bit 7
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+        const uint32_t sel = __builtin_amdgcn_perm(hi, lo, q | q << 8 | (4u + q) << 16 | (4u + q) << 24);
+        const uint32_t vl = __builtin_amdgcn_perm(t.y, t.x, sel);
+        const uint32_t vh = __builtin_amdgcn_perm(t.w, t.z, sel);
+        const uint32_t sg = __builtin_amdgcn_perm(sh, sl, 0x0Cu | q << 8 | 0x0Cu << 16 | (4u + q) << 24);
+        out[q] = (vh & 0xFF00FF00u) | (vl & 0x00FF00FFu) | sg;
+    }
 }
 
 // Block scale byte of a block from its eight dwords.
@@ -326,8 +379,35 @@ __device__ __forceinline__ uint32_t block_scale_byte(const uint32_t (&w)[8], flo
     for (int i = 0; i < 8; ++i)
         mx = pk_max(mx, w[i] & 0x7FFF7FFFu);
     const uint32_t bm = max(mx & 0xFFFFu, mx >> 16);
-    const float bamax = __uint_as_float(bm << 16);
-    return e4m3_encode((bamax / 6.0f) * gs);
+    // bamax / 6 without a divide: a bf16 value has 8 significant bits, so its
+    // quotient by 3 never lies within 2^-52 (relative) of a binary32 rounding
+    // mid-point, and rounding the binary64 product with 1/6 once more to
+    // binary32 gives the correctly rounded quotient (checked for every bf16).
+    const float sixth = (float)((double)bf16_value(bm) * (1.0 / 6.0));
+    // binary32 -> E4M3 by the converter: round to nearest even below 448 (checked
+    // for every non-negative binary32); above it the converter gives NaN bytes,
+    // which the min turns into the saturated 0x7E
+    const uint32_t s = __builtin_amdgcn_cvt_pk_fp8_f32(sixth * gs, 0.0f, 0, false) & 0xFFu;
+    return s < 0x7Eu ? s : 0x7Eu;
+}
+
+// The 16 codes of a block (two dwords of nibbles) and its table entry.
+__device__ __forceinline__ void block_codes(const uint32_t (&w)[8], const uint32_t* e, uint32_t& c0,
+                                            uint32_t& c1)
+{
+    const uint2 head = *reinterpret_cast<const uint2*>(e);
+    if (head.y & kFastExact) {
+        const float r = __uint_as_float(head.x);
+        c0 = codes_fast(w, r);
+        c1 = codes_fast(w + 4, r);
+    } else {
+        uint32_t t[6];
+        const uint4 a = *reinterpret_cast<const uint4*>(e + 2);
+        const uint2 b = *reinterpret_cast<const uint2*>(e + 6);
+        t[0] = a.x; t[1] = a.y; t[2] = a.z; t[3] = a.w; t[4] = b.x; t[5] = b.y;
+        c0 = codes_threshold(w, t - 2);
+        c1 = codes_threshold(w + 4, t - 2);
+    }
 }
 
 __device__ __forceinline__ void unpack8(const uint4& a, const uint4& b, uint32_t (&w)[8])
@@ -420,10 +500,11 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant(const uint4* __restrict
                                                          int64_t nblocks,
                                                          const float* __restrict__ amax)
 {
-    __shared__ uint4 table[128 * kEntryVec];
+    __shared__ uint4 table[128 * kEntryWords / 4];
+    uint32_t* tab = reinterpret_cast<uint32_t*>(table);
     const float gs = global_scale_of(*amax);
     if (threadIdx.x < 128)
-        build_entry(threadIdx.x, gs, table + threadIdx.x * kEntryVec);
+        build_entry(threadIdx.x, gs, tab + threadIdx.x * kEntryWords);
     __syncthreads();
 
     const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
@@ -444,11 +525,13 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant(const uint4* __restrict
             if (b >= 0) {
                 uint32_t w[8];
                 unpack8(v[u][0], v[u][1], w);
-                const Entry e = load_entry(table, block_scale_byte(w, gs), true);
+                const uint32_t* e = tab + block_scale_byte(w, gs) * kEntryWords;
+                uint32_t c0, c1;
+                block_codes(w, e, c0, c1);
+                const uint4 t = *reinterpret_cast<const uint4*>(e + 8);
                 uint32_t o[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    o[i] = fake_quant_pair(w[i], e);
+                decode_dword(c0, t, o);
+                decode_dword(c1, t, o + 4);
                 store16<NVFP4_FQ_NT_ST != 0>(y + 2 * b, make_uint4(o[0], o[1], o[2], o[3]));
                 store16<NVFP4_FQ_NT_ST != 0>(y + 2 * b + 1, make_uint4(o[4], o[5], o[6], o[7]));
             }
@@ -463,10 +546,11 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack(const uint4* __restr
                                                             int64_t nblocks,
                                                             const float* __restrict__ amax)
 {
-    __shared__ uint4 table[128 * kEntryVec];
+    __shared__ uint4 table[128 * kEntryWords / 4];
+    uint32_t* tab = reinterpret_cast<uint32_t*>(table);
     const float gs = global_scale_of(*amax);
     if (threadIdx.x < 128)
-        build_entry(threadIdx.x, gs, table + threadIdx.x * kEntryVec);
+        build_entry(threadIdx.x, gs, tab + threadIdx.x * kEntryWords);
     if (blockIdx.x == 0 && threadIdx.x == 0)
         *gs_out = gs;
     __syncthreads();
@@ -490,48 +574,12 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack(const uint4* __restr
                 uint32_t w[8];
                 unpack8(v[u][0], v[u][1], w);
                 const uint32_t s = block_scale_byte(w, gs);
-                const Entry e = load_entry(table, s, false);
-                uint32_t c[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    c[i] = code_byte(w[i], e);
-                store8<NVFP4_QP_NT_ST != 0>(packed + b, make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
-                                                        c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24));
+                uint32_t c0, c1;
+                block_codes(w, tab + s * kEntryWords, c0, c1);
+                store8<NVFP4_QP_NT_ST != 0>(packed + b, make_uint2(c0, c1));
                 scales[b] = (uint8_t)s;
             }
         }
-    }
-}
-
-// Unpack table: per scale byte, the low and high bytes of bf16(M_i * sd), i = 0..7.
-__device__ void build_unpack_entry(uint32_t s, float gs, uint4* dst)
-{
-    const float sd = e4m3_decode(s) / gs;
-    uint32_t o[8];
-    const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        o[i] = bf16_bits(mag[i] * sd);
-    *dst = make_uint4((o[0] & 0xFFu) | (o[1] & 0xFFu) << 8 | (o[2] & 0xFFu) << 16 | (o[3] & 0xFFu) << 24,
-                      (o[4] & 0xFFu) | (o[5] & 0xFFu) << 8 | (o[6] & 0xFFu) << 16 | (o[7] & 0xFFu) << 24,
-                      (o[0] >> 8) | (o[1] >> 8) << 8 | (o[2] >> 8) << 16 | (o[3] >> 8) << 24,
-                      (o[4] >> 8) | (o[5] >> 8) << 8 | (o[6] >> 8) << 16 | (o[7] >> 8) << 24);
-}
-
-// Eight codes (one dword of packed nibbles) -> eight bf16 values in four dwords.
-__device__ __forceinline__ void unpack_dword(uint32_t p, const uint4& t, uint32_t* out)
-{
-    const uint32_t lo = p & 0x07070707u;           // magnitude index of even columns
-    const uint32_t hi = (p >> 4) & 0x07070707u;    // ... of odd columns
-    const uint32_t sl = (p << 4) & 0x80808080u;    // sign of even columns at bit 7
-    const uint32_t sh = p & 0x80808080u;           // sign of odd columns at bit 7
-#pragma unroll
-    for (uint32_t q = 0; q < 4; ++q) {
-        const uint32_t sel = __builtin_amdgcn_perm(hi, lo, q | q << 8 | (4u + q) << 16 | (4u + q) << 24);
-        const uint32_t vl = __builtin_amdgcn_perm(t.y, t.x, sel);
-        const uint32_t vh = __builtin_amdgcn_perm(t.w, t.z, sel);
-        const uint32_t sg = __builtin_amdgcn_perm(sh, sl, 0x0Cu | q << 8 | 0x0Cu << 16 | (4u + q) << 24);
-        out[q] = (vh & 0xFF00FF00u) | (vl & 0x00FF00FFu) | sg;
     }
 }
 
@@ -543,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_unpack(const uint2* __rest
     __shared__ uint4 table[128];
     const float gs = *gs_in;
     if (threadIdx.x < 128)
-        build_unpack_entry(threadIdx.x, gs, table + threadIdx.x);
+        table[threadIdx.x] = output_entry(e4m3_decode(threadIdx.x) / gs);
     __syncthreads();
 
     const int64_t stride = (int64_t)gridDim.x * kThreads * kDqUnroll;
@@ -565,8 +613,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant_unpack(const uint2* __rest
             if (b < nblocks) {
                 const uint4 t = table[s[u] & 0x7Fu];
                 uint32_t o[8];
-                unpack_dword(p[u].x, t, o);
-                unpack_dword(p[u].y, t, o + 4);
+                decode_dword(p[u].x, t, o);
+                decode_dword(p[u].y, t, o + 4);
                 store16<NVFP4_DQ_NT_ST != 0>(y + 2 * b, make_uint4(o[0], o[1], o[2], o[3]));
                 store16<NVFP4_DQ_NT_ST != 0>(y + 2 * b + 1, make_uint4(o[4], o[5], o[6], o[7]));
             }
