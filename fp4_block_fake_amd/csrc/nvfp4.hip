@@ -55,10 +55,10 @@ namespace {
 // MI355X (c5 weight, 470 MB); the macros let a build be re-tuned without
 // editing the kernels.
 #ifndef NVFP4_UNROLL
-#define NVFP4_UNROLL 2            // blocks per lane per iteration: fake-quant, pack
+#define NVFP4_UNROLL 4            // blocks per lane per iteration: fake-quant, pack
 #endif
 #ifndef NVFP4_DQ_UNROLL
-#define NVFP4_DQ_UNROLL 4         // blocks per lane per iteration: unpack
+#define NVFP4_DQ_UNROLL 8         // blocks per lane per iteration: unpack
 #endif
 #ifndef NVFP4_AMAX_UNROLL
 #define NVFP4_AMAX_UNROLL 8       // 16-byte vectors per lane per amax chunk
@@ -67,19 +67,24 @@ namespace {
 #define NVFP4_AMAX_WG_PER_CU 4    // persistent workgroups per CU
 #endif
 #ifndef NVFP4_FQ_WG_PER_CU
-#define NVFP4_FQ_WG_PER_CU 32
+#define NVFP4_FQ_WG_PER_CU 64
 #endif
 #ifndef NVFP4_QP_WG_PER_CU
-#define NVFP4_QP_WG_PER_CU 32
+#define NVFP4_QP_WG_PER_CU 64
 #endif
 #ifndef NVFP4_DQ_WG_PER_CU
-#define NVFP4_DQ_WG_PER_CU 64
+#define NVFP4_DQ_WG_PER_CU 16
 #endif
 // 1: the quantizing passes walk the tensor from its end, so they start on the
 // data the amax pass read last.  This pays only when the amax pass leaves x in
 // the Infinity Cache, i.e. with NVFP4_AMAX_NT 0; streaming amax loads win more.
 #ifndef NVFP4_REVERSE
 #define NVFP4_REVERSE 0
+#endif
+// 1: the quantizing passes keep the next iteration's loads in flight while
+// processing the current one (more registers, fewer waves)
+#ifndef NVFP4_PIPELINE
+#define NVFP4_PIPELINE 0
 #endif
 // non-temporal (streaming) hints on loads (LD) and stores (ST)
 #ifndef NVFP4_AMAX_NT
@@ -106,11 +111,14 @@ constexpr int kUnroll = NVFP4_UNROLL;
 constexpr int kDqUnroll = NVFP4_DQ_UNROLL;
 constexpr int kAmaxUnroll = NVFP4_AMAX_UNROLL;
 constexpr bool kReverse = NVFP4_REVERSE != 0;
+constexpr bool kPipeline = NVFP4_PIPELINE != 0;
 
 constexpr float kEps = 1e-12f;    // clamp of the amax and of the block scale
 constexpr float kGsNumerator = 2688.0f;  // E4M3 max 448 times E2M1 max 6
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- packed 16-bit helpers
 
@@ -172,15 +180,6 @@ __device__ __forceinline__ float e4m3_decode(uint32_t s)
     return s >= 8u ? __uint_as_float((s << 20) + (120u << 23)) : (float)s * 0x1p-9f;
 }
 
-// binary32 -> bf16 bits, round-to-nearest-even.
-__device__ __forceinline__ uint32_t bf16_bits(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return (u >> 16) | 0x40u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // Bits of the largest bf16 value <= t (t > 0, an exact binary64), and whether t is one.
 __device__ __forceinline__ uint32_t bf16_floor_bits(double t, bool& exact)
 {
@@ -217,13 +216,12 @@ __device__ __forceinline__ uint32_t first_at_or_above(double t)
 //
 // Everything a block needs beyond its own data depends only on its E4M3 scale
 // byte S (0..0x7E), so each workgroup tabulates it once, for all 128 bytes, in
-// LDS.  Entry for S (12 dwords, 48 bytes):
-//   [0]  r = 1 / sq (binary32 bits), the multiplier of the fast path
-//   [1]  bit 0: the fast path is exact for every bf16 input under this S
+// LDS.  Entry for S (8 dwords, 32 bytes):
+//   [0]  r = 1 / sq (binary32 bits), the multiplier of the fast path; the sign
+//        bit is set when the fast path is NOT exact under this S
+//   [1]  sd = decode(S) / gs (binary32 bits), the factor of the outputs
 //   [2]  t4 | t4<<16    [3] t6 | t6<<16    [4] (t2-t6) | (t2-t6)<<16
 //   [5]  (t0-1) | (t0-1)<<16    [6] t7 | t5<<16    [7] t3 | t1<<16
-//   [8..11] low bytes of the eight bf16 outputs bf16(M_i * sd), i = 0..3 and
-//        4..7, then their high bytes (the unpack table layout)
 // t_i (i = 1..7) is the smallest magnitude bit pattern whose E2M1 index is >= i;
 // t0 the smallest whose quotient is nonzero.
 //
@@ -234,8 +232,8 @@ __device__ __forceinline__ uint32_t first_at_or_above(double t)
 // decision boundary.  Both decisions are monotone in |x|, so comparing them at
 // the two bf16 values around each exact threshold t_i settles it for every
 // input; an S that fails (or whose t0 is not 1) keeps the threshold path.
-constexpr int kEntryWords = 12;
-constexpr uint32_t kFastExact = 1u;
+constexpr int kEntryWords = 8;
+constexpr uint32_t kNotFast = 0x80000000u;
 
 __device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
 
@@ -250,21 +248,6 @@ __device__ __forceinline__ bool fast_passes(uint32_t m, float r, float b, bool s
 __device__ __forceinline__ bool fast_agrees(uint32_t t, float r, float b, bool strict)
 {
     return fast_passes(t, r, b, strict) && !fast_passes(t - 1u, r, b, strict);
-}
-
-// The eight outputs bf16(M_i * sd) as the unpack table entry: low bytes of
-// i = 0..3, of i = 4..7, then the high bytes in the same order.
-__device__ __forceinline__ uint4 output_entry(float sd)
-{
-    const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
-    uint32_t o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        o[i] = bf16_bits(mag[i] * sd);
-    return make_uint4((o[0] & 0xFFu) | (o[1] & 0xFFu) << 8 | (o[2] & 0xFFu) << 16 | (o[3] & 0xFFu) << 24,
-                      (o[4] & 0xFFu) | (o[5] & 0xFFu) << 8 | (o[6] & 0xFFu) << 16 | (o[7] & 0xFFu) << 24,
-                      (o[0] >> 8) | (o[1] >> 8) << 8 | (o[2] >> 8) << 16 | (o[3] >> 8) << 24,
-                      (o[4] >> 8) | (o[5] >> 8) << 8 | (o[6] >> 8) << 16 | (o[7] >> 8) << 24);
 }
 
 __device__ void build_entry(uint32_t s, float gs, uint32_t* dst)
@@ -286,19 +269,14 @@ __device__ void build_entry(uint32_t s, float gs, uint32_t* dst)
                       fast_agrees(t3, r, 1.25f, true) && fast_agrees(t4, r, 1.75f, false) &&
                       fast_agrees(t5, r, 2.5f, true) && fast_agrees(t6, r, 3.5f, false) &&
                       fast_agrees(t7, r, 5.0f, true);
-    const uint4 out = output_entry(sd);
-    dst[0] = __float_as_uint(r);
-    dst[1] = fast ? kFastExact : 0u;
+    dst[0] = __float_as_uint(r) | (fast ? 0u : kNotFast);
+    dst[1] = __float_as_uint(sd);
     dst[2] = t4 * 0x10001u;
     dst[3] = t6 * 0x10001u;
     dst[4] = ((t2 - t6) & 0xFFFFu) * 0x10001u;
     dst[5] = (t0 - 1u) * 0x10001u;
     dst[6] = t7 | (t5 << 16);
     dst[7] = t3 | (t1 << 16);
-    dst[8] = out.x;
-    dst[9] = out.y;
-    dst[10] = out.z;
-    dst[11] = out.w;
 }
 
 // Threshold path: idx for the two magnitudes m (15-bit fields) of one dword,
@@ -353,22 +331,27 @@ __device__ __forceinline__ uint32_t codes_fast(const uint32_t* w, float r)
     return out;
 }
 
-// Eight codes (one dword of nibbles, even element low) -> eight bf16 values in
-// four dwords, through the output entry t of their block.
-__device__ __forceinline__ void decode_dword(uint32_t p, const uint4& t, uint32_t* out)
+// Two codes (byte P of `codes`, even element in the low nibble) -> two bf16
+// outputs bf16(LUT[code] * sd).  The converter turns a code into its exact
+// signed E2M1 value (checked for every byte), the product is one binary32
+// rounding, and the bf16 pack conversion rounds to nearest even (checked for
+// every binary32 input); -0 codes give -0 outputs.
+template <int P>
+__device__ __forceinline__ uint32_t decode_pair(uint32_t codes, float sd)
 {
-    const uint32_t lo = p & 0x07070707u;           // magnitude index of even columns
-    const uint32_t hi = (p >> 4) & 0x07070707u;    // ... of odd columns
-    const uint32_t sl = (p << 4) & 0x80808080u;    // sign of even columns at bit 7
-    const uint32_t sh = p & 0x80808080u;           // sign of odd columns at bit 7
-#pragma unroll
-    for (uint32_t q = 0; q < 4; ++q) {
-        const uint32_t sel = __builtin_amdgcn_perm(hi, lo, q | q << 8 | (4u + q) << 16 | (4u + q) << 24);
-        const uint32_t vl = __builtin_amdgcn_perm(t.y, t.x, sel);
-        const uint32_t vh = __builtin_amdgcn_perm(t.w, t.z, sel);
-        const uint32_t sg = __builtin_amdgcn_perm(sh, sl, 0x0Cu | q << 8 | 0x0Cu << 16 | (4u + q) << 24);
-        out[q] = (vh & 0xFF00FF00u) | (vl & 0x00FF00FFu) | sg;
-    }
+    const f32x2 m = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, P);
+    const f32x2 v = {m.x * sd, m.y * sd};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Sixteen codes (two dwords of nibbles) -> sixteen bf16 outputs in two 16-byte stores.
+template <bool NtStore>
+__device__ __forceinline__ void decode_store(uint32_t c0, uint32_t c1, float sd, uint4* y, int64_t b)
+{
+    store16<NtStore>(y + 2 * b, make_uint4(decode_pair<0>(c0, sd), decode_pair<1>(c0, sd),
+                                           decode_pair<2>(c0, sd), decode_pair<3>(c0, sd)));
+    store16<NtStore>(y + 2 * b + 1, make_uint4(decode_pair<0>(c1, sd), decode_pair<1>(c1, sd),
+                                               decode_pair<2>(c1, sd), decode_pair<3>(c1, sd)));
 }
 
 // Block scale byte of a block from its eight dwords.
@@ -395,9 +378,9 @@ __device__ __forceinline__ uint32_t block_scale_byte(const uint32_t (&w)[8], flo
 __device__ __forceinline__ void block_codes(const uint32_t (&w)[8], const uint32_t* e, uint32_t& c0,
                                             uint32_t& c1)
 {
-    const uint2 head = *reinterpret_cast<const uint2*>(e);
-    if (head.y & kFastExact) {
-        const float r = __uint_as_float(head.x);
+    const uint32_t head = e[0];
+    if (!(head & kNotFast)) {
+        const float r = __uint_as_float(head);
         c0 = codes_fast(w, r);
         c1 = codes_fast(w + 4, r);
     } else {
@@ -414,6 +397,46 @@ __device__ __forceinline__ void unpack8(const uint4& a, const uint4& b, uint32_t
 {
     w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
     w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+// Fake-quant one block (its eight input dwords) into y[2b], y[2b+1].
+template <bool NtStore>
+__device__ __forceinline__ void fake_quant_block(const uint32_t (&w)[8], const uint32_t* tab, float gs,
+                                                 uint4* y, int64_t b)
+{
+    const uint32_t* e = tab + block_scale_byte(w, gs) * kEntryWords;
+    uint32_t c0, c1;
+    block_codes(w, e, c0, c1);
+    decode_store<NtStore>(c0, c1, __uint_as_float(e[1]), y, b);
+}
+
+// Quantize-pack one block: eight code bytes into packed[b], its scale byte into scales[b].
+template <bool NtStore>
+__device__ __forceinline__ void pack_block(const uint32_t (&w)[8], const uint32_t* tab, float gs,
+                                           uint2* packed, uint8_t* scales, int64_t b)
+{
+    const uint32_t s = block_scale_byte(w, gs);
+    uint32_t c0, c1;
+    block_codes(w, tab + s * kEntryWords, c0, c1);
+    store8<NtStore>(packed + b, make_uint2(c0, c1));
+    scales[b] = (uint8_t)s;
+}
+
+// Workgroup max of the lanes' packed maxima (15-bit magnitude); valid in thread 0.
+__device__ __forceinline__ uint32_t workgroup_max(uint32_t mx, uint32_t* wave_max)
+{
+    uint32_t m = max(mx & 0xFFFFu, mx >> 16);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    if ((threadIdx.x & 63) == 0)
+        wave_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    uint32_t r = wave_max[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i)
+        r = max(r, wave_max[i]);
+    return r;
 }
 
 // ---------------------------------------------------------------- kernels
@@ -478,21 +501,64 @@ __global__ __launch_bounds__(kThreads) void k_amax(AmaxGroup g, float* out)
             if ((int)threadIdx.x < g.ntail[t])
                 mx = pk_max(mx, g.tail[t][threadIdx.x] & 0x7FFFu);
     }
-    uint32_t m = max(mx & 0xFFFFu, mx >> 16);
-    // wave reduction over 64 lanes
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
     __shared__ uint32_t wave_max[kThreads / 64];
-    if ((threadIdx.x & 63) == 0)
-        wave_max[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t r = wave_max[0];
-#pragma unroll
-        for (int i = 1; i < kThreads / 64; ++i)
-            r = max(r, wave_max[i]);
+    const uint32_t r = workgroup_max(mx, wave_max);
+    if (threadIdx.x == 0)
         atomicMax(reinterpret_cast<int*>(out), (int)(r << 16));
+}
+
+// The kUnroll blocks of one iteration of a quantizing pass, loaded into v.
+template <bool NtLd>
+__device__ __forceinline__ void load_blocks(const uint4* __restrict__ x, int64_t base, int64_t nblocks,
+                                            uint4 (&v)[kUnroll][2])
+{
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t b = walk(base + (int64_t)u * kThreads, nblocks);
+        if (b >= 0) {
+            v[u][0] = load16<NtLd>(x + 2 * b);
+            v[u][1] = load16<NtLd>(x + 2 * b + 1);
+        }
+    }
+}
+
+// A quantizing pass over all blocks with a grid stride.  The first
+// iteration's loads are issued before the workgroup builds its scale-byte
+// table, so the table build hides under their latency; with kPipeline the
+// next iteration's loads are in flight while the current blocks are processed.
+template <bool NtLd, typename Body>
+__device__ __forceinline__ void quantize_pass(const uint4* __restrict__ x, int64_t nblocks, float gs,
+                                              uint32_t* tab, Body body)
+{
+    const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
+    int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
+    uint4 v[kUnroll][2];
+    load_blocks<NtLd>(x, base, nblocks, v);
+    if (threadIdx.x < 128)
+        build_entry(threadIdx.x, gs, tab + threadIdx.x * kEntryWords);
+    __syncthreads();
+    for (; base < nblocks; base += stride) {
+        uint4 next[kUnroll][2];
+        if (kPipeline)
+            load_blocks<NtLd>(x, base + stride, nblocks, next);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t b = walk(base + (int64_t)u * kThreads, nblocks);
+            if (b >= 0) {
+                uint32_t w[8];
+                unpack8(v[u][0], v[u][1], w);
+                body(w, b);
+            }
+        }
+        if (kPipeline) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                v[u][0] = next[u][0];
+                v[u][1] = next[u][1];
+            }
+        } else {
+            load_blocks<NtLd>(x, base + stride, nblocks, v);
+        }
     }
 }
 
@@ -503,40 +569,9 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant(const uint4* __restrict
     __shared__ uint4 table[128 * kEntryWords / 4];
     uint32_t* tab = reinterpret_cast<uint32_t*>(table);
     const float gs = global_scale_of(*amax);
-    if (threadIdx.x < 128)
-        build_entry(threadIdx.x, gs, tab + threadIdx.x * kEntryWords);
-    __syncthreads();
-
-    const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
-    for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < nblocks;
-         base += stride) {
-        uint4 v[kUnroll][2];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t b = walk(base + (int64_t)u * kThreads, nblocks);
-            if (b >= 0) {
-                v[u][0] = load16<NVFP4_FQ_NT_LD != 0>(x + 2 * b);
-                v[u][1] = load16<NVFP4_FQ_NT_LD != 0>(x + 2 * b + 1);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t b = walk(base + (int64_t)u * kThreads, nblocks);
-            if (b >= 0) {
-                uint32_t w[8];
-                unpack8(v[u][0], v[u][1], w);
-                const uint32_t* e = tab + block_scale_byte(w, gs) * kEntryWords;
-                uint32_t c0, c1;
-                block_codes(w, e, c0, c1);
-                const uint4 t = *reinterpret_cast<const uint4*>(e + 8);
-                uint32_t o[8];
-                decode_dword(c0, t, o);
-                decode_dword(c1, t, o + 4);
-                store16<NVFP4_FQ_NT_ST != 0>(y + 2 * b, make_uint4(o[0], o[1], o[2], o[3]));
-                store16<NVFP4_FQ_NT_ST != 0>(y + 2 * b + 1, make_uint4(o[4], o[5], o[6], o[7]));
-            }
-        }
-    }
+    quantize_pass<NVFP4_FQ_NT_LD != 0>(x, nblocks, gs, tab, [&](const uint32_t (&w)[8], int64_t b) {
+        fake_quant_block<NVFP4_FQ_NT_ST != 0>(w, tab, gs, y, b);
+    });
 }
 
 __global__ __launch_bounds__(kThreads) void k_quantize_pack(const uint4* __restrict__ x,
@@ -549,38 +584,11 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack(const uint4* __restr
     __shared__ uint4 table[128 * kEntryWords / 4];
     uint32_t* tab = reinterpret_cast<uint32_t*>(table);
     const float gs = global_scale_of(*amax);
-    if (threadIdx.x < 128)
-        build_entry(threadIdx.x, gs, tab + threadIdx.x * kEntryWords);
     if (blockIdx.x == 0 && threadIdx.x == 0)
         *gs_out = gs;
-    __syncthreads();
-
-    const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
-    for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < nblocks;
-         base += stride) {
-        uint4 v[kUnroll][2];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t b = walk(base + (int64_t)u * kThreads, nblocks);
-            if (b >= 0) {
-                v[u][0] = load16<NVFP4_QP_NT_LD != 0>(x + 2 * b);
-                v[u][1] = load16<NVFP4_QP_NT_LD != 0>(x + 2 * b + 1);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t b = walk(base + (int64_t)u * kThreads, nblocks);
-            if (b >= 0) {
-                uint32_t w[8];
-                unpack8(v[u][0], v[u][1], w);
-                const uint32_t s = block_scale_byte(w, gs);
-                uint32_t c0, c1;
-                block_codes(w, tab + s * kEntryWords, c0, c1);
-                store8<NVFP4_QP_NT_ST != 0>(packed + b, make_uint2(c0, c1));
-                scales[b] = (uint8_t)s;
-            }
-        }
-    }
+    quantize_pass<NVFP4_QP_NT_LD != 0>(x, nblocks, gs, tab, [&](const uint32_t (&w)[8], int64_t b) {
+        pack_block<NVFP4_QP_NT_ST != 0>(w, tab, gs, packed, scales, b);
+    });
 }
 
 __global__ __launch_bounds__(kThreads) void k_dequant_unpack(const uint2* __restrict__ packed,
@@ -588,36 +596,43 @@ __global__ __launch_bounds__(kThreads) void k_dequant_unpack(const uint2* __rest
                                                              const float* __restrict__ gs_in,
                                                              uint4* __restrict__ y, int64_t nblocks)
 {
-    __shared__ uint4 table[128];
+    __shared__ float sd_of[128];                   // decode(S) / gs for every scale byte
     const float gs = *gs_in;
     if (threadIdx.x < 128)
-        table[threadIdx.x] = output_entry(e4m3_decode(threadIdx.x) / gs);
+        sd_of[threadIdx.x] = e4m3_decode(threadIdx.x) / gs;
     __syncthreads();
 
+    // software-pipelined: the next iteration's codes and scales are in flight
+    // while the current ones are decoded and stored
     const int64_t stride = (int64_t)gridDim.x * kThreads * kDqUnroll;
-    for (int64_t base = (int64_t)blockIdx.x * kThreads * kDqUnroll + threadIdx.x; base < nblocks;
-         base += stride) {
-        uint2 p[kDqUnroll];
-        uint32_t s[kDqUnroll];
+    int64_t base = (int64_t)blockIdx.x * kThreads * kDqUnroll + threadIdx.x;
+    uint2 p[kDqUnroll];
+    uint32_t s[kDqUnroll];
+#pragma unroll
+    for (int u = 0; u < kDqUnroll; ++u) {
+        const int64_t b = base + (int64_t)u * kThreads;
+        p[u] = b < nblocks ? packed[b] : make_uint2(0u, 0u);
+        s[u] = b < nblocks ? scales[b] : 0u;
+    }
+    for (; base < nblocks; base += stride) {
+        uint2 pn[kDqUnroll];
+        uint32_t sn[kDqUnroll];
 #pragma unroll
         for (int u = 0; u < kDqUnroll; ++u) {
-            const int64_t b = base + (int64_t)u * kThreads;
-            if (b < nblocks) {
-                p[u] = packed[b];
-                s[u] = scales[b];
-            }
+            const int64_t b = base + stride + (int64_t)u * kThreads;
+            pn[u] = b < nblocks ? packed[b] : make_uint2(0u, 0u);
+            sn[u] = b < nblocks ? scales[b] : 0u;
         }
 #pragma unroll
         for (int u = 0; u < kDqUnroll; ++u) {
             const int64_t b = base + (int64_t)u * kThreads;
-            if (b < nblocks) {
-                const uint4 t = table[s[u] & 0x7Fu];
-                uint32_t o[8];
-                decode_dword(p[u].x, t, o);
-                decode_dword(p[u].y, t, o + 4);
-                store16<NVFP4_DQ_NT_ST != 0>(y + 2 * b, make_uint4(o[0], o[1], o[2], o[3]));
-                store16<NVFP4_DQ_NT_ST != 0>(y + 2 * b + 1, make_uint4(o[4], o[5], o[6], o[7]));
-            }
+            if (b < nblocks)
+                decode_store<NVFP4_DQ_NT_ST != 0>(p[u].x, p[u].y, sd_of[s[u] & 0x7Fu], y, b);
+        }
+#pragma unroll
+        for (int u = 0; u < kDqUnroll; ++u) {
+            p[u] = pn[u];
+            s[u] = sn[u];
         }
     }
 }
@@ -790,6 +805,7 @@ nvfp4_status nvfp4_fake_quant(const void* x, void* y, int64_t rows, int64_t cols
         return NVFP4_ERR_OVERLAP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
+    const int64_t nblocks = n / 16;
     const float* a = amax_in;
     if (!a) {
         st = enqueue_amax_one(x, n, amax_out, s);
@@ -799,7 +815,6 @@ nvfp4_status nvfp4_fake_quant(const void* x, void* y, int64_t rows, int64_t cols
     }
     if (n == 0)
         return NVFP4_OK;
-    const int64_t nblocks = n / 16;
     k_fake_quant<<<persistent_grid(nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
         static_cast<const uint4*>(x), static_cast<uint4*>(y), nblocks, a);
     return launched();
@@ -831,6 +846,7 @@ nvfp4_status nvfp4_quantize_pack(const void* x, int64_t rows, int64_t cols,
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
+    const int64_t nblocks = n / 16;
     const float* a = amax_in;
     if (!a) {
         st = enqueue_amax_one(x, n, amax_out, s);
@@ -838,7 +854,6 @@ nvfp4_status nvfp4_quantize_pack(const void* x, int64_t rows, int64_t cols,
             return st;
         a = amax_out;
     }
-    const int64_t nblocks = n / 16;
     k_quantize_pack<<<persistent_grid(nblocks, (int64_t)kThreads * kUnroll, NVFP4_QP_WG_PER_CU), kThreads, 0, s>>>(
         static_cast<const uint4*>(x), reinterpret_cast<uint2*>(packed), scales, global_scale,
         nblocks, a);

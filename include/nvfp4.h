@@ -127,7 +127,9 @@ nvfp4_status nvfp4_quantize_pack(const void* x, int64_t rows, int64_t cols,
  * nvfp4_dequant_unpack -- packed NVFP4 -> bf16 [rows, cols] (VideoX-Fun page,
  * dequantize_weight_from_float4: nibble -> E2M1 value, times
  * decode(scale) / gs, rounded to bf16).  Layouts as nvfp4_quantize_pack writes
- * them.  packed 8-byte aligned, y 16-byte aligned; y must not overlap the inputs.
+ * them; scale bytes outside 0x00..0x7E (never written by the pack) give
+ * unspecified outputs.  packed 8-byte aligned, y 16-byte aligned; y must not
+ * overlap the inputs.
  */
 nvfp4_status nvfp4_dequant_unpack(const uint8_t* packed, const uint8_t* scales,
                                   const float* global_scale, int64_t rows, int64_t cols,

@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 import synth
+from cases import log_uniform_bf16, scale_straddle_cases, straddle_block
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -84,15 +85,6 @@ def check_all_ops(x, amax_in=None, what=""):
 def sample_rows(rows, seed, k=62):
     rng = np.random.default_rng(seed)
     return np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, k, replace=False)]))
-
-
-def log_uniform_bf16(seed, shape, lo=-133, hi=120):
-    rng = np.random.default_rng(seed)
-    mag = np.exp2(rng.uniform(lo, hi, shape))
-    blockscale = np.exp2(rng.uniform(-20, 20, (shape[0], shape[1] // 16, 1)))
-    v = (mag.reshape(shape[0], -1, 16) * blockscale).reshape(shape)
-    v = np.minimum(v, 1e37) * np.where(rng.random(shape) < 0.5, -1, 1)
-    return synth.to_bf16_bits(v.astype(np.float32))
 
 
 # ---------------------------------------------------------------- the five configurations
@@ -333,3 +325,38 @@ def test_ste_backward_is_identity():
     torch.cuda.synchronize()
     assert torch.equal(x.grad.view(torch.int16), g.view(torch.int16))
     assert_same(host(y.detach()), oracle.fake_quant(synth.c1_weight()), "ste forward")
+
+
+def test_block_scale_divide_by_six_straddles():
+    """Blocks where an IEEE divide by 6 and a reciprocal multiply give different E4M3 bytes."""
+    cases = scale_straddle_cases()
+    assert len(cases) >= 32
+    for a, bmax in cases:
+        check_all_ops(straddle_block(bmax), amax_in=a, what="straddle")
+
+
+def test_more_than_2pow31_elements():
+    """64-bit indexing: 67000 x 32768 bf16 (2.2e9 elements, 4.4 GB), sampled rows vs the oracle."""
+    rows, cols = 67000, 32768
+    rng = np.random.default_rng(77)
+    tile = synth.normal_bf16(77, (64, cols), 0.02)
+    x = np.empty((rows, cols), np.uint16)
+    for r0 in range(0, rows, 64):                      # the tile, with a per-chunk exponent shift
+        n = min(64, rows - r0)
+        shift = np.uint16(int(rng.integers(0, 8)) << 7)
+        x[r0:r0 + n] = np.where((tile[:n] & 0x7FFF) != 0, tile[:n] + shift, tile[:n])
+    say("2^31+ elements: %dx%d" % (rows, cols))
+    xt = dev(x)
+    amax = scalar(0.0)
+    y = nv.nvfp4_fake_quant(xt, amax_out=amax)
+    packed, scales, gs = nv.nvfp4_quantize_pack(xt, amax_in=amax)
+    torch.cuda.synchronize()
+    a = oracle.amax(x)
+    assert fbits(amax.item()) == fbits(a)
+    sample = np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, 30, replace=False),
+                                       np.arange(65536 - 2, 65536 + 3)]))
+    assert_same(host(y[torch.from_numpy(sample).to(DEV)]), oracle.fake_quant(x[sample], a), "2^31+ fq rows")
+    p_ref, s_ref, g_ref = oracle.quantize(x[sample], a)
+    assert fbits(gs.item()) == fbits(g_ref)
+    assert_same(packed[torch.from_numpy(sample).to(DEV)].cpu().numpy(), p_ref, "2^31+ packed rows")
+    assert_same(scales[torch.from_numpy(sample).to(DEV)].cpu().numpy(), s_ref, "2^31+ scale rows")

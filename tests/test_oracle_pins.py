@@ -12,22 +12,13 @@ import torch
 
 import oracle
 import synth
+from cases import log_uniform_bf16, scale_straddle_cases, straddle_block, torch_fp8_decode, torch_fp8_encode
 from synth import bits_to_f32
 
 EPS32 = np.float32(1e-12)
 
 
 # ---------------------------------------------------------------- helpers
-
-def torch_fp8_decode(b):
-    b = np.ascontiguousarray(b, dtype=np.uint8)
-    return torch.from_numpy(b).view(torch.float8_e4m3fn).float().numpy()
-
-
-def torch_fp8_encode(v):
-    v = np.ascontiguousarray(v, dtype=np.float32)
-    return torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-
 
 def torch_bf16(f):
     f = np.ascontiguousarray(f, dtype=np.float32)
@@ -381,21 +372,12 @@ def rederive(xbits, amax_value, golden):
     return packed, s8.reshape(rows, cols // 16), gs, y
 
 
-def log_uniform_bf16(seed, shape, lo=-130, hi=120):
-    rng = np.random.default_rng(seed)
-    mag = np.exp2(rng.uniform(lo, hi, shape))
-    blockscale = np.exp2(rng.uniform(-20, 20, (shape[0], shape[1] // 16, 1)))
-    v = (mag.reshape(shape[0], -1, 16) * blockscale).reshape(shape)
-    v = np.minimum(v, 1e37) * np.where(rng.random(shape) < 0.5, -1, 1)
-    return synth.to_bf16_bits(v.astype(np.float32))
-
-
 CASES = {
     "c1": lambda: (synth.c1_weight(), None),
     "c2_rows": lambda: (synth.c2_weight()[:96], float(oracle.amax(synth.c2_weight()))),
     "c4_act_low_amax": lambda: (synth.c4_activation(0, tokens=64), 40.0),  # EMA-like: saturating blocks
     "c5_rows": lambda: (synth.c5_weight(rows=48), None),
-    "log_uniform": lambda: (log_uniform_bf16(1, (64, 512)), None),
+    "log_uniform": lambda: (log_uniform_bf16(1, (64, 512), -130, 120), None),
     "log_uniform_small_amax": lambda: (log_uniform_bf16(2, (32, 256), -140, -100), None),
 }
 
@@ -436,45 +418,11 @@ def test_ragged_columns_are_zero_padded():
     assert np.array_equal(oracle.dequantize(p1, s1, g1, 40), oracle.dequantize(p2, s2, g2, 48)[:, :40])
 
 
-def scale_straddle_cases(n=48):
-    """(amax, block max) pairs where fl(bamax / 6) * gs and fl(bamax * fl(1/6)) * gs round
-    to different E4M3 bytes: they tell an IEEE divide by 6 from a reciprocal multiply."""
-    rng = np.random.default_rng(5)
-    x = (np.arange(1, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
-    r, r2 = x / np.float32(6), x * (np.float32(1) / np.float32(6))
-    keep = (r != r2) & (x > 1e-8) & (x < 1e8)
-    x, r, r2 = x[keep], r[keep], r2[keep]
-    vals = torch_fp8_decode(np.arange(127, dtype=np.uint8)).astype(np.float64)
-    mids = ((vals[:-1] + vals[1:]) / 2)[8:120]
-    cases = []
-    with np.errstate(over="ignore", invalid="ignore"):
-        for i in rng.permutation(len(x)):
-            gs0 = np.float32(rng.choice(mids) / np.float64(r[i]))
-            for k in range(-3, 4):
-                gs = np.uint32(int(gs0.view(np.uint32)) + k).view(np.float32)
-                e = torch_fp8_encode(np.float32([r[i] * gs, r2[i] * gs]))
-                if e[0] == e[1]:
-                    continue
-                a0 = np.float32(2688.0 / np.float64(gs)).view(np.uint32).astype(np.int64)
-                for j in range(-8, 9):
-                    a = np.uint32(int(a0) + j).view(np.float32)
-                    if np.float32(2688.0) / a == gs and 1e-11 < a < 1e30:   # above the 1e-12 clamp
-                        cases.append((float(a), float(x[i])))
-                        break
-                break
-            if len(cases) == n:
-                return cases
-    return cases
-
-
 def test_block_scale_divides_by_six(golden):
     cases = scale_straddle_cases()
     assert len(cases) >= 32
     for a, bmax in cases:
-        row = np.zeros((1, 16), np.float32)
-        row[0, 0] = bmax
-        row[0, 1:] = np.float32(bmax) * np.float32(0.3)
-        x = synth.to_bf16_bits(row)
+        x = straddle_block(bmax)
         packed, scales, gs = oracle.quantize(x, a)
         p2, s2, gs2, _ = rederive(x, a, golden)
         assert gs == gs2 and scales[0, 0] == s2[0, 0] and np.array_equal(packed, p2)
