@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "NVFP4Error", "OBS_STATIC_MINMAX", "OBS_EMA", "lib", "library_path",
     "nvfp4_amax", "nvfp4_fake_quant", "nvfp4_quantize_pack", "nvfp4_dequant_unpack",
-    "nvfp4_observer_update", "nvfp4_strerror", "FakeQuantSTE",
+    "nvfp4_observer_update", "nvfp4_strerror", "FakeQuantSTE", "blocks_per_row",
 ]
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
@@ -124,21 +124,28 @@ def nvfp4_fake_quant(x: torch.Tensor, y: torch.Tensor | None = None,
     return y
 
 
+def blocks_per_row(cols: int) -> int:
+    """16-element blocks per row; a ragged row is zero-padded to a whole block."""
+    return -(-cols // 16)
+
+
 def nvfp4_quantize_pack(x: torch.Tensor, amax_in: torch.Tensor | None = None,
                         amax_out: torch.Tensor | None = None, packed: torch.Tensor | None = None,
                         scales: torch.Tensor | None = None,
                         global_scale: torch.Tensor | None = None):
-    """bf16 [R, C] -> (packed uint8 [R, C/2], E4M3 scale bytes uint8 [R, C/16], fp32 gs [1])."""
+    """bf16 [R, C] -> (packed uint8 [R, 8*nbr], E4M3 scale bytes uint8 [R, nbr], fp32 gs [1]),
+    nbr = ceil(C / 16)."""
     rows, cols = _matrix(x, "x")
     dev = x.device
+    nbr = blocks_per_row(cols)
     if packed is None:
-        packed = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        packed = torch.empty((rows, 8 * nbr), dtype=torch.uint8, device=dev)
     if scales is None:
-        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, nbr), dtype=torch.uint8, device=dev)
     global_scale = _scalar(dev, global_scale)
     if amax_in is None and amax_out is None:
         amax_out = _scalar(dev)
-    for t, shape in ((packed, (rows, cols // 2)), (scales, (rows, cols // 16))):
+    for t, shape in ((packed, (rows, 8 * nbr)), (scales, (rows, nbr))):
         if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
             raise ValueError("packed/scales must be contiguous uint8 CUDA tensors of shape %s" % (shape,))
     _check(lib.nvfp4_quantize_pack(_ptr(x), rows, cols, _ptr(amax_in), _ptr(amax_out), _ptr(packed),
@@ -148,13 +155,19 @@ def nvfp4_quantize_pack(x: torch.Tensor, amax_in: torch.Tensor | None = None,
 
 
 def nvfp4_dequant_unpack(packed: torch.Tensor, scales: torch.Tensor, global_scale: torch.Tensor,
-                         y: torch.Tensor | None = None) -> torch.Tensor:
-    """(packed [R, C/2], scales [R, C/16], gs) -> bf16 [R, C]."""
+                         y: torch.Tensor | None = None, cols: int | None = None) -> torch.Tensor:
+    """(packed [R, 8*nbr], scales [R, nbr], gs) -> bf16 [R, cols]; cols defaults to 16*nbr."""
     if packed.dtype != torch.uint8 or packed.dim() != 2 or not packed.is_cuda or not packed.is_contiguous():
         raise ValueError("packed must be a contiguous 2-D uint8 CUDA tensor")
-    rows, cols = packed.shape[0], packed.shape[1] * 2
-    if tuple(scales.shape) != (rows, cols // 16) or scales.dtype != torch.uint8 or not scales.is_contiguous():
-        raise ValueError("scales must be contiguous uint8 [%d, %d]" % (rows, cols // 16))
+    if packed.shape[1] % 8:
+        raise ValueError("packed rows hold 8 bytes per 16-element block")
+    rows, nbr = packed.shape[0], packed.shape[1] // 8
+    if cols is None:
+        cols = 16 * nbr
+    if blocks_per_row(cols) != nbr:
+        raise ValueError("cols=%d does not match %d packed blocks per row" % (cols, nbr))
+    if tuple(scales.shape) != (rows, nbr) or scales.dtype != torch.uint8 or not scales.is_contiguous():
+        raise ValueError("scales must be contiguous uint8 [%d, %d]" % (rows, nbr))
     _scalar(packed.device, global_scale)
     if y is None:
         y = torch.empty((rows, cols), dtype=torch.bfloat16, device=packed.device)

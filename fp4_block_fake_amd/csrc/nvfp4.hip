@@ -637,6 +637,120 @@ __global__ __launch_bounds__(kThreads) void k_dequant_unpack(const uint2* __rest
     }
 }
 
+// ---------------------------------------------------------------- ragged rows
+//
+// A row whose length is not a multiple of 16 is zero-padded to the next
+// multiple (VideoX-Fun page, quantize_weight_to_float4): its last block holds
+// fewer than 16 elements and zeros, which never change a block max.  Packed
+// codes and scales keep the padded layout ([rows, 8 * nbr] and [rows, nbr] for
+// nbr = ceil(cols / 16)), so block f is still byte 8f and scale f; only the
+// bf16 side is addressed per element.  One lane owns one block, as above.
+struct RaggedShape {
+    int64_t cols;       // elements per row
+    int64_t nbr;        // blocks per row
+    int64_t nblocks;    // rows * nbr
+};
+
+// First element and element count of block f.
+__device__ __forceinline__ int64_t ragged_block(const RaggedShape& g, int64_t f, int& n)
+{
+    const int64_t r = f / g.nbr;
+    const int64_t c0 = (f - r * g.nbr) * 16;
+    const int64_t left = g.cols - c0;
+    n = left < 16 ? (int)left : 16;
+    return r * g.cols + c0;
+}
+
+__device__ __forceinline__ void load_ragged(const uint16_t* __restrict__ x, int64_t e0, int n,
+                                            uint32_t (&w)[8])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = 2 * i < n ? x[e0 + 2 * i] : 0u;
+        const uint32_t hi = 2 * i + 1 < n ? x[e0 + 2 * i + 1] : 0u;
+        w[i] = lo | (hi << 16);
+    }
+}
+
+__device__ __forceinline__ void store_ragged(uint16_t* y, int64_t e0, int n, uint32_t c0, uint32_t c1,
+                                             float sd)
+{
+    const uint32_t o[8] = {decode_pair<0>(c0, sd), decode_pair<1>(c0, sd), decode_pair<2>(c0, sd),
+                           decode_pair<3>(c0, sd), decode_pair<0>(c1, sd), decode_pair<1>(c1, sd),
+                           decode_pair<2>(c1, sd), decode_pair<3>(c1, sd)};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (2 * i < n)
+            y[e0 + 2 * i] = (uint16_t)(o[i] & 0xFFFFu);
+        if (2 * i + 1 < n)
+            y[e0 + 2 * i + 1] = (uint16_t)(o[i] >> 16);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_fake_quant_ragged(const uint16_t* __restrict__ x,
+                                                                uint16_t* y, RaggedShape g,
+                                                                const float* __restrict__ amax)
+{
+    __shared__ uint4 table[128 * kEntryWords / 4];
+    uint32_t* tab = reinterpret_cast<uint32_t*>(table);
+    const float gs = global_scale_of(*amax);
+    if (threadIdx.x < 128)
+        build_entry(threadIdx.x, gs, tab + threadIdx.x * kEntryWords);
+    __syncthreads();
+    for (int64_t f = (int64_t)blockIdx.x * kThreads + threadIdx.x; f < g.nblocks;
+         f += (int64_t)gridDim.x * kThreads) {
+        int n;
+        const int64_t e0 = ragged_block(g, f, n);
+        uint32_t w[8];
+        load_ragged(x, e0, n, w);
+        const uint32_t* e = tab + block_scale_byte(w, gs) * kEntryWords;
+        uint32_t c0, c1;
+        block_codes(w, e, c0, c1);
+        store_ragged(y, e0, n, c0, c1, __uint_as_float(e[1]));
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_quantize_pack_ragged(const uint16_t* __restrict__ x,
+                                                                   uint2* __restrict__ packed,
+                                                                   uint8_t* __restrict__ scales,
+                                                                   float* __restrict__ gs_out,
+                                                                   RaggedShape g,
+                                                                   const float* __restrict__ amax)
+{
+    __shared__ uint4 table[128 * kEntryWords / 4];
+    uint32_t* tab = reinterpret_cast<uint32_t*>(table);
+    const float gs = global_scale_of(*amax);
+    if (threadIdx.x < 128)
+        build_entry(threadIdx.x, gs, tab + threadIdx.x * kEntryWords);
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        *gs_out = gs;
+    __syncthreads();
+    for (int64_t f = (int64_t)blockIdx.x * kThreads + threadIdx.x; f < g.nblocks;
+         f += (int64_t)gridDim.x * kThreads) {
+        int n;
+        const int64_t e0 = ragged_block(g, f, n);
+        uint32_t w[8];
+        load_ragged(x, e0, n, w);
+        pack_block<false>(w, tab, gs, packed, scales, f);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_dequant_unpack_ragged(const uint2* __restrict__ packed,
+                                                                    const uint8_t* __restrict__ scales,
+                                                                    const float* __restrict__ gs_in,
+                                                                    uint16_t* __restrict__ y,
+                                                                    RaggedShape g)
+{
+    const float gs = *gs_in;
+    for (int64_t f = (int64_t)blockIdx.x * kThreads + threadIdx.x; f < g.nblocks;
+         f += (int64_t)gridDim.x * kThreads) {
+        int n;
+        const int64_t e0 = ragged_block(g, f, n);
+        const uint2 p = packed[f];
+        store_ragged(y, e0, n, p.x, p.y, e4m3_decode(scales[f] & 0x7Fu) / gs);
+    }
+}
+
 __global__ void k_observer(float* state, const float* cur, int mode, float decay)
 {
     const float s = *state, c = *cur;
@@ -664,15 +778,28 @@ bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb)
     return na && nb && x < y + nb && y < x + na;
 }
 
-nvfp4_status check_matrix(int64_t rows, int64_t cols, int64_t* numel)
+struct Matrix {
+    int64_t numel;      // rows * cols
+    int64_t nbr;        // blocks per row, ceil(cols / 16)
+    int64_t nblocks;    // rows * nbr
+    bool ragged;        // cols % 16 != 0
+};
+
+nvfp4_status check_matrix(int64_t rows, int64_t cols, Matrix* m)
 {
-    if (rows < 0 || cols < 16 || cols % 16 != 0)
+    if (rows < 0 || cols < 1)
         return NVFP4_ERR_SHAPE;
-    if (rows > 0 && cols > (INT64_MAX / 4) / rows)
+    const int64_t nbr = (cols + 15) / 16;
+    if (rows > 0 && nbr > (INT64_MAX / 64) / rows)      // padded bytes stay far from overflow
         return NVFP4_ERR_SHAPE;
-    *numel = rows * cols;
+    m->numel = rows * cols;
+    m->nbr = nbr;
+    m->nblocks = rows * nbr;
+    m->ragged = cols % 16 != 0;
     return NVFP4_OK;
 }
+
+constexpr int kRaggedWgPerCu = 32;
 
 unsigned persistent_grid(int64_t items, int64_t items_per_wg, int wg_per_cu)
 {
@@ -730,7 +857,7 @@ const char* nvfp4_strerror(int status)
     switch (status) {
     case NVFP4_OK: return "ok";
     case NVFP4_ERR_NULL: return "a required pointer is NULL";
-    case NVFP4_ERR_SHAPE: return "bad shape (need rows >= 0, cols >= 16, cols % 16 == 0)";
+    case NVFP4_ERR_SHAPE: return "bad shape (need rows >= 0 and cols >= 1)";
     case NVFP4_ERR_ALIGN: return "misaligned pointer";
     case NVFP4_ERR_OVERLAP: return "an output overlaps an input or another output";
     case NVFP4_ERR_ARG: return "bad argument (mode, decay or group count)";
@@ -787,10 +914,11 @@ nvfp4_status nvfp4_amax(const void* const* xs, const int64_t* numels, int n, flo
 nvfp4_status nvfp4_fake_quant(const void* x, void* y, int64_t rows, int64_t cols,
                               const float* amax_in, float* amax_out, void* stream)
 {
-    int64_t n = 0;
-    nvfp4_status st = check_matrix(rows, cols, &n);
+    Matrix m;
+    nvfp4_status st = check_matrix(rows, cols, &m);
     if (st != NVFP4_OK)
         return st;
+    const int64_t n = m.numel;
     if ((n > 0 && (!x || !y)) || (!amax_in && !amax_out))
         return NVFP4_ERR_NULL;
     if (!aligned(x, 16) || !aligned(y, 16) || (amax_in && !aligned(amax_in, 4)) ||
@@ -805,7 +933,6 @@ nvfp4_status nvfp4_fake_quant(const void* x, void* y, int64_t rows, int64_t cols
         return NVFP4_ERR_OVERLAP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    const int64_t nblocks = n / 16;
     const float* a = amax_in;
     if (!a) {
         st = enqueue_amax_one(x, n, amax_out, s);
@@ -815,8 +942,14 @@ nvfp4_status nvfp4_fake_quant(const void* x, void* y, int64_t rows, int64_t cols
     }
     if (n == 0)
         return NVFP4_OK;
-    k_fake_quant<<<persistent_grid(nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
-        static_cast<const uint4*>(x), static_cast<uint4*>(y), nblocks, a);
+    if (m.ragged) {
+        const RaggedShape g{cols, m.nbr, m.nblocks};
+        k_fake_quant_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
+            static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), g, a);
+        return launched();
+    }
+    k_fake_quant<<<persistent_grid(m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
+        static_cast<const uint4*>(x), static_cast<uint4*>(y), m.nblocks, a);
     return launched();
 }
 
@@ -825,16 +958,17 @@ nvfp4_status nvfp4_quantize_pack(const void* x, int64_t rows, int64_t cols,
                                  uint8_t* packed, uint8_t* scales, float* global_scale,
                                  void* stream)
 {
-    int64_t n = 0;
-    nvfp4_status st = check_matrix(rows, cols, &n);
+    Matrix m;
+    nvfp4_status st = check_matrix(rows, cols, &m);
     if (st != NVFP4_OK)
         return st;
+    const int64_t n = m.numel;
     if ((n > 0 && (!x || !packed || !scales)) || !global_scale || (!amax_in && !amax_out))
         return NVFP4_ERR_NULL;
     if (!aligned(x, 16) || !aligned(packed, 8) || !aligned(global_scale, 4) ||
         (amax_in && !aligned(amax_in, 4)) || (!amax_in && !aligned(amax_out, 4)))
         return NVFP4_ERR_ALIGN;
-    const uint64_t xb = 2 * (uint64_t)n, pb = (uint64_t)n / 2, sb = (uint64_t)n / 16;
+    const uint64_t xb = 2 * (uint64_t)n, pb = 8 * (uint64_t)m.nblocks, sb = (uint64_t)m.nblocks;
     const void* outs[4] = {packed, scales, global_scale, amax_in ? nullptr : amax_out};
     const uint64_t lens[4] = {pb, sb, 4, amax_in ? 0u : 4u};
     for (int i = 0; i < 4; ++i) {
@@ -846,7 +980,6 @@ nvfp4_status nvfp4_quantize_pack(const void* x, int64_t rows, int64_t cols,
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    const int64_t nblocks = n / 16;
     const float* a = amax_in;
     if (!a) {
         st = enqueue_amax_one(x, n, amax_out, s);
@@ -854,9 +987,15 @@ nvfp4_status nvfp4_quantize_pack(const void* x, int64_t rows, int64_t cols,
             return st;
         a = amax_out;
     }
-    k_quantize_pack<<<persistent_grid(nblocks, (int64_t)kThreads * kUnroll, NVFP4_QP_WG_PER_CU), kThreads, 0, s>>>(
+    if (m.ragged) {
+        const RaggedShape g{cols, m.nbr, m.nblocks};
+        k_quantize_pack_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
+            static_cast<const uint16_t*>(x), reinterpret_cast<uint2*>(packed), scales, global_scale, g, a);
+        return launched();
+    }
+    k_quantize_pack<<<persistent_grid(m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_QP_WG_PER_CU), kThreads, 0, s>>>(
         static_cast<const uint4*>(x), reinterpret_cast<uint2*>(packed), scales, global_scale,
-        nblocks, a);
+        m.nblocks, a);
     return launched();
 }
 
@@ -864,25 +1003,30 @@ nvfp4_status nvfp4_dequant_unpack(const uint8_t* packed, const uint8_t* scales,
                                   const float* global_scale, int64_t rows, int64_t cols,
                                   void* y, void* stream)
 {
-    int64_t n = 0;
-    nvfp4_status st = check_matrix(rows, cols, &n);
+    Matrix m;
+    nvfp4_status st = check_matrix(rows, cols, &m);
     if (st != NVFP4_OK)
         return st;
-    if (n == 0)
+    if (m.numel == 0)
         return NVFP4_OK;
     if (!packed || !scales || !global_scale || !y)
         return NVFP4_ERR_NULL;
     if (!aligned(packed, 8) || !aligned(y, 16) || !aligned(global_scale, 4))
         return NVFP4_ERR_ALIGN;
-    const uint64_t yb = 2 * (uint64_t)n;
-    if (overlap(y, yb, packed, (uint64_t)n / 2) || overlap(y, yb, scales, (uint64_t)n / 16) ||
+    const uint64_t yb = 2 * (uint64_t)m.numel;
+    if (overlap(y, yb, packed, 8 * (uint64_t)m.nblocks) || overlap(y, yb, scales, (uint64_t)m.nblocks) ||
         overlap(y, yb, global_scale, 4))
         return NVFP4_ERR_OVERLAP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    const int64_t nblocks = n / 16;
-    k_dequant_unpack<<<persistent_grid(nblocks, (int64_t)kThreads * kDqUnroll, NVFP4_DQ_WG_PER_CU), kThreads, 0, s>>>(
-        reinterpret_cast<const uint2*>(packed), scales, global_scale, static_cast<uint4*>(y), nblocks);
+    if (m.ragged) {
+        const RaggedShape g{cols, m.nbr, m.nblocks};
+        k_dequant_unpack_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
+            reinterpret_cast<const uint2*>(packed), scales, global_scale, static_cast<uint16_t*>(y), g);
+        return launched();
+    }
+    k_dequant_unpack<<<persistent_grid(m.nblocks, (int64_t)kThreads * kDqUnroll, NVFP4_DQ_WG_PER_CU), kThreads, 0, s>>>(
+        reinterpret_cast<const uint2*>(packed), scales, global_scale, static_cast<uint4*>(y), m.nblocks);
     return launched();
 }
 

@@ -36,8 +36,12 @@
  *     launch returns NVFP4_ERR_HIP.  Asynchronous device faults surface at the
  *     caller's next synchronisation.
  *   - Inputs must be finite; NaN and Inf inputs give unspecified bytes.
- *   - Shapes: rows >= 0, cols >= 16 and cols % 16 == 0 (blocks never straddle
- *     rows).  rows == 0 is a valid empty tensor.
+ *   - Shapes: rows >= 0 and cols >= 1; rows == 0 is a valid empty tensor.
+ *     Blocks are 16 consecutive columns of one row and never straddle rows.  A
+ *     row whose length is not a multiple of 16 is zero-padded to
+ *     nbr = ceil(cols / 16) blocks (VideoX-Fun page, quantize_weight_to_float4):
+ *     the pad never changes a block max, the packed codes and scales keep the
+ *     padded layout, and bf16 outputs have exactly cols columns.
  */
 #ifndef NVFP4_H
 #define NVFP4_H
@@ -51,7 +55,7 @@ extern "C" {
 typedef enum nvfp4_status {
     NVFP4_OK = 0,
     NVFP4_ERR_NULL = 1,     /* a required pointer is NULL                          */
-    NVFP4_ERR_SHAPE = 2,    /* rows < 0, cols < 16, cols % 16 != 0, size overflow  */
+    NVFP4_ERR_SHAPE = 2,    /* rows < 0, cols < 1, or a size that overflows        */
     NVFP4_ERR_ALIGN = 3,    /* a pointer is not aligned as the call requires       */
     NVFP4_ERR_OVERLAP = 4,  /* an output overlaps an input or another output       */
     NVFP4_ERR_ARG = 5,      /* a bad mode, decay, or group count                   */
@@ -110,10 +114,10 @@ nvfp4_status nvfp4_fake_quant(const void* x, void* y, int64_t rows, int64_t cols
  *
  *   x             device bf16 [rows, cols], 16-byte aligned
  *   amax_in/out   as for nvfp4_fake_quant
- *   packed        device uint8 [rows, cols/2], 8-byte aligned; byte i of a row
- *                 holds the code of column 2i in its low nibble and of column
- *                 2i+1 in its high nibble
- *   scales        device uint8 [rows, cols/16], E4M3 (float8_e4m3fn) bytes,
+ *   packed        device uint8 [rows, 8 * nbr], 8-byte aligned; byte i of a row
+ *                 holds the code of (padded) column 2i in its low nibble and of
+ *                 column 2i+1 in its high nibble; padding columns get code 0
+ *   scales        device uint8 [rows, nbr], E4M3 (float8_e4m3fn) bytes,
  *                 row-major, one per block
  *   global_scale  device fp32: gs (not the amax), 4-byte aligned
  * Outputs must not overlap x, amax_in or each other.

@@ -53,8 +53,8 @@ def fq(x, y, rows, cols, amax_in, amax_out):
 
 
 def test_fake_quant_validation():
-    assert fq(A, A + (1 << 30), 4, 8, None, A + (2 << 30)) == ERR_SHAPE          # cols < 16
-    assert fq(A, A + (1 << 30), 4, 24, None, A + (2 << 30)) == ERR_SHAPE         # cols % 16
+    assert fq(A, A + (1 << 30), 4, 0, None, A + (2 << 30)) == ERR_SHAPE          # cols < 1
+    assert fq(A, A + (1 << 30), 4, -16, None, A + (2 << 30)) == ERR_SHAPE
     assert fq(A, A + (1 << 30), -1, 16, None, A + (2 << 30)) == ERR_SHAPE
     assert fq(A, A + (1 << 30), 1 << 40, 1 << 40, None, A + (2 << 30)) == ERR_SHAPE  # overflow
     assert fq(None, A, 4, 16, None, A + (2 << 30)) == ERR_NULL
@@ -71,7 +71,9 @@ def test_fake_quant_validation():
 def test_quantize_pack_validation():
     q = nv.lib.nvfp4_quantize_pack
     x, p, s, g, a = A, A + (1 << 30), A + (2 << 30), A + (3 << 30), A + (4 << 30)
-    assert q(P(x), 4, 20, None, P(a), P(p), P(s), P(g), None) == ERR_SHAPE
+    assert q(P(x), 4, 0, None, P(a), P(p), P(s), P(g), None) == ERR_SHAPE
+    # a ragged row (cols 20) pads to 2 blocks: 16 packed bytes per row, so 64 overlap 48 past p
+    assert q(P(x), 4, 20, None, P(a), P(p), P(p + 48), P(g), None) == ERR_OVERLAP
     assert q(P(x), 4, 16, None, None, P(p), P(s), P(g), None) == ERR_NULL
     assert q(P(x), 4, 16, None, P(a), None, P(s), P(g), None) == ERR_NULL
     assert q(P(x), 4, 16, None, P(a), P(p), P(s), None, None) == ERR_NULL
@@ -86,7 +88,8 @@ def test_quantize_pack_validation():
 def test_dequant_unpack_validation():
     d = nv.lib.nvfp4_dequant_unpack
     p, s, g, y = A, A + (1 << 30), A + (2 << 30), A + (3 << 30)
-    assert d(P(p), P(s), P(g), 4, 17, P(y), None) == ERR_SHAPE
+    assert d(P(p), P(s), P(g), 4, 0, P(y), None) == ERR_SHAPE
+    assert d(P(p), P(s), P(g), 4, 17, P(p + 64 - 8), None) == ERR_ALIGN
     assert d(None, P(s), P(g), 4, 16, P(y), None) == ERR_NULL
     assert d(P(p), P(s), P(g), 4, 16, None, None) == ERR_NULL
     assert d(P(p + 1), P(s), P(g), 4, 16, P(y), None) == ERR_ALIGN

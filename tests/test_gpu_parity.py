@@ -67,7 +67,7 @@ def check_all_ops(x, amax_in=None, what=""):
     y = nv.nvfp4_fake_quant(xt, amax_in=a_in, amax_out=a_out)
     a_out2 = scalar(-7.0)
     packed, scales, gs = nv.nvfp4_quantize_pack(xt, amax_in=a_in, amax_out=a_out2)
-    yd = nv.nvfp4_dequant_unpack(packed, scales, gs)
+    yd = nv.nvfp4_dequant_unpack(packed, scales, gs, cols=x.shape[1])
     torch.cuda.synchronize()
     p_ref, s_ref, g_ref = oracle.quantize(x, a)
     y_ref = oracle.fake_quant(x, a)
@@ -174,6 +174,20 @@ def test_c5_large_weight_full_path():
 
 
 # ---------------------------------------------------------------- edge tensors
+
+@pytest.mark.parametrize("shape", [(1, 1), (3, 7), (5, 15), (4, 17), (33, 40), (9, 1000), (2, 4097),
+                                   (130, 24), (1000, 33)])
+def test_ragged_columns_zero_padded(shape):
+    """Rows not a multiple of 16: zero-padded blocks, padded code/scale layout, cols outputs."""
+    rng = np.random.default_rng(shape[0] * 131 + shape[1])
+    x = synth.to_bf16_bits((rng.standard_normal(shape) * np.exp(rng.uniform(-3, 3, shape))).astype(np.float32))
+    check_all_ops(x, what="ragged cols")
+    check_all_ops(x, amax_in=float(np.float32(0.75)), what="ragged cols, cached amax")
+    xt = dev(x)
+    nv.nvfp4_fake_quant(xt, y=xt, amax_out=scalar(0.0))          # in place
+    torch.cuda.synchronize()
+    assert_same(host(xt), oracle.fake_quant(x), "ragged in place")
+
 
 @pytest.mark.parametrize("shape", [(1, 16), (7, 48), (3, 16000), (1037, 144), (515, 16)])
 def test_ragged_grid_tails(shape):
