@@ -99,6 +99,73 @@ def cpu_baseline(x, rows):
     }
 
 
+def secondary(nv, synth, np, torch, dev, reps=20):
+    """Per-call throughput on the other workloads (not part of the headline step)."""
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+
+    def timed(fn, nbytes):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        return {"us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                "pct_of_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # c3: shared amax of fused QKV siblings in one launch, then a fake-quant of each
+    sibs = [to_dev(a) for a in synth.c3_siblings()]
+    ys = [torch.empty_like(t) for t in sibs]
+    shared = torch.empty(1, dtype=torch.float32, device=dev)
+    n3 = sum(t.numel() for t in sibs)
+
+    def c3():
+        nv.nvfp4_amax(sibs, amax=shared)
+        for t, y in zip(sibs, ys):
+            nv.nvfp4_fake_quant(t, y=y, amax_in=shared)
+    out["c3_qkv_shared_amax_fake_quant"] = timed(c3, 6.0 * n3)
+    del sibs, ys
+
+    # c4 activation step: amax, both observers, a fake-quant with each observer's amax
+    x = to_dev(synth.c4_activation(0))
+    y1, y2 = torch.empty_like(x), torch.empty_like(x)
+    cur = torch.empty(1, dtype=torch.float32, device=dev)
+    st_s = torch.full((1,), -1.0, dtype=torch.float32, device=dev)
+    st_e = torch.full((1,), -1.0, dtype=torch.float32, device=dev)
+
+    def c4act():
+        nv.nvfp4_amax(x, amax=cur)
+        nv.nvfp4_observer_update(st_s, cur, nv.OBS_STATIC_MINMAX)
+        nv.nvfp4_observer_update(st_e, cur, nv.OBS_EMA, 0.01)
+        nv.nvfp4_fake_quant(x, y=y1, amax_in=st_s)
+        nv.nvfp4_fake_quant(x, y=y2, amax_in=st_e)
+    out["c4_activation_step_8192x4096"] = timed(c4act, 10.0 * x.numel())
+    out["c4_activation_cached_fake_quant"] = timed(lambda: nv.nvfp4_fake_quant(x, y=y1, amax_in=st_s),
+                                                   4.0 * x.numel())
+    del x, y1, y2
+
+    w = to_dev(synth.c4_weight())
+    yw = torch.empty_like(w)
+    aw = torch.empty(1, dtype=torch.float32, device=dev)
+    out["c4_weight_fused_amax_fake_quant_14336x4096"] = timed(
+        lambda: nv.nvfp4_fake_quant(w, y=yw, amax_out=aw), 6.0 * w.numel())
+    pk = torch.empty((w.shape[0], w.shape[1] // 2), dtype=torch.uint8, device=dev)
+    sc = torch.empty((w.shape[0], w.shape[1] // 16), dtype=torch.uint8, device=dev)
+    gsw = torch.empty(1, dtype=torch.float32, device=dev)
+    out["c4_weight_fused_amax_quantize_pack_14336x4096"] = timed(
+        lambda: nv.nvfp4_quantize_pack(w, amax_out=aw, packed=pk, scales=sc, global_scale=gsw),
+        4.5625 * w.numel())
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +174,7 @@ def main():
     ap.add_argument("--rows", type=int, default=28672)
     ap.add_argument("--cols", type=int, default=8192)
     ap.add_argument("--cpu-rows", type=int, default=8192, help="rows of the oracle's CPU sample (0: skip)")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the c3/c4 per-call lines")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -255,6 +323,9 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_secondary:
+        log("secondary workloads")
+        result["secondary"] = secondary(nv, synth, np, torch, dev)
     if args.cpu_rows > 0:
         log("cpu baseline: oracle on %d rows" % args.cpu_rows)
         result["cpu_baseline"] = cpu_baseline(x_host, min(args.cpu_rows, rows))

@@ -64,7 +64,7 @@ namespace {
 #define NVFP4_AMAX_UNROLL 8       // 16-byte vectors per lane per amax chunk
 #endif
 #ifndef NVFP4_AMAX_WG_PER_CU
-#define NVFP4_AMAX_WG_PER_CU 4    // persistent workgroups per CU
+#define NVFP4_AMAX_WG_PER_CU 2    // persistent workgroups per CU (each ends in one atomic)
 #endif
 #ifndef NVFP4_FQ_WG_PER_CU
 #define NVFP4_FQ_WG_PER_CU 64
@@ -503,8 +503,15 @@ __global__ __launch_bounds__(kThreads) void k_amax(AmaxGroup g, float* out)
     }
     __shared__ uint32_t wave_max[kThreads / 64];
     const uint32_t r = workgroup_max(mx, wave_max);
-    if (threadIdx.x == 0)
-        atomicMax(reinterpret_cast<int*>(out), (int)(r << 16));
+    if (threadIdx.x == 0) {
+        // Same-address atomics serialise at the coherence point; the maximum only
+        // grows, so a workgroup that already sees a value at least as large as its
+        // own has nothing to add (a stale read costs one redundant atomic at most).
+        int* dst = reinterpret_cast<int*>(out);
+        const int mine = (int)(r << 16);
+        if (mine > __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            atomicMax(dst, mine);
+    }
 }
 
 // The kUnroll blocks of one iteration of a quantizing pass, loaded into v.

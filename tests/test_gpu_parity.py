@@ -315,6 +315,32 @@ def test_amax_groups_tails_and_accumulate():
         assert fbits(one.item()) == fbits(oracle.amax(a))
 
 
+def test_amax_buffer_reused_after_a_larger_result():
+    """A workgroup skips its atomic when the buffer already holds at least its own
+    maximum; a result left by an earlier call must never count as such a value."""
+    rng = np.random.default_rng(19)
+    big = synth.to_bf16_bits(rng.standard_normal((2048, 4096)).astype(np.float32) * 8)
+    small = synth.to_bf16_bits(rng.standard_normal((2048, 4096)).astype(np.float32) * 0.01)
+    tb, ts = dev(big), dev(small)
+    buf = scalar(0.0)
+    say("amax buffer reuse, 2048x4096")
+    for _ in range(3):
+        nv.nvfp4_amax(tb, amax=buf)
+        nv.nvfp4_amax(ts, amax=buf)
+        torch.cuda.synchronize()
+        assert fbits(buf.item()) == fbits(oracle.amax(small))
+        nv.nvfp4_amax(tb, amax=buf)
+        y = nv.nvfp4_fake_quant(ts, amax_out=buf)
+        torch.cuda.synchronize()
+        assert fbits(buf.item()) == fbits(oracle.amax(small))
+        assert_same(host(y), oracle.fake_quant(small, oracle.amax(small)), "fake-quant after reuse")
+        nv.nvfp4_amax(tb, amax=buf)
+        _, _, gs = nv.nvfp4_quantize_pack(ts, amax_out=buf)
+        torch.cuda.synchronize()
+        assert fbits(buf.item()) == fbits(oracle.amax(small))
+        assert fbits(gs.item()) == fbits(oracle.global_scale(oracle.amax(small)))
+
+
 @pytest.mark.parametrize("decay", [0.01, 0.3, 1.0])
 def test_observer_sequences(decay):
     cur = np.float32([3.5, 2.0, 7.25, 1e-3, 40.0, 39.0, 0.0, 55.5, 12.0, 13.0])
