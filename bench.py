@@ -132,6 +132,8 @@ def secondary(nv, synth, np, torch, dev, reps=20):
         for t, y in zip(sibs, ys):
             nv.nvfp4_fake_quant(t, y=y, amax_in=shared)
     out["c3_qkv_shared_amax_fake_quant"] = timed(c3, 6.0 * n3)
+    out["c3_qkv_group_fake_quant_one_launch"] = timed(
+        lambda: nv.nvfp4_fake_quant_group(sibs, ys=ys, amax_out=shared), 6.0 * n3)
     del sibs, ys
 
     # c4 activation step: amax, both observers, a fake-quant with each observer's amax
@@ -148,6 +150,14 @@ def secondary(nv, synth, np, torch, dev, reps=20):
         nv.nvfp4_fake_quant(x, y=y1, amax_in=st_s)
         nv.nvfp4_fake_quant(x, y=y2, amax_in=st_e)
     out["c4_activation_step_8192x4096"] = timed(c4act, 10.0 * x.numel())
+
+    def c4act_dual():
+        nv.nvfp4_amax(x, amax=cur)
+        nv.nvfp4_observer_update(st_s, cur, nv.OBS_STATIC_MINMAX)
+        nv.nvfp4_observer_update(st_e, cur, nv.OBS_EMA, 0.01)
+        nv.nvfp4_fake_quant_dual(x, st_s, st_e, y0=y1, y1=y2)
+    # same outputs from one read of x: 8 bytes per element of traffic instead of 10
+    out["c4_activation_step_dual_fake_quant"] = timed(c4act_dual, 8.0 * x.numel())
     out["c4_activation_cached_fake_quant"] = timed(lambda: nv.nvfp4_fake_quant(x, y=y1, amax_in=st_s),
                                                    4.0 * x.numel())
     del x, y1, y2

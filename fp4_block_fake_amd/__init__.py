@@ -15,8 +15,9 @@ import torch
 
 __all__ = [
     "NVFP4Error", "OBS_STATIC_MINMAX", "OBS_EMA", "lib", "library_path",
-    "nvfp4_amax", "nvfp4_fake_quant", "nvfp4_quantize_pack", "nvfp4_dequant_unpack",
-    "nvfp4_observer_update", "nvfp4_strerror", "FakeQuantSTE", "blocks_per_row",
+    "nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
+    "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_observer_update", "nvfp4_strerror",
+    "FakeQuantSTE", "blocks_per_row",
 ]
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
@@ -24,8 +25,8 @@ library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp
 OBS_STATIC_MINMAX = 0
 OBS_EMA = 1
 
-_EXPORTS = ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_quantize_pack", "nvfp4_dequant_unpack",
-            "nvfp4_observer_update", "nvfp4_strerror")
+_EXPORTS = ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
+            "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_observer_update", "nvfp4_strerror")
 
 
 class NVFP4Error(RuntimeError):
@@ -42,6 +43,8 @@ def _load() -> ctypes.CDLL:
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     so.nvfp4_amax.argtypes = [P, P, I, P, I, P]
     so.nvfp4_fake_quant.argtypes = [P, P, I64, I64, P, P, P]
+    so.nvfp4_fake_quant_group.argtypes = [P, P, P, P, I, P, P, P]
+    so.nvfp4_fake_quant_dual.argtypes = [P, I64, I64, P, P, P, P, P]
     so.nvfp4_quantize_pack.argtypes = [P, I64, I64, P, P, P, P, P, P]
     so.nvfp4_dequant_unpack.argtypes = [P, P, P, I64, I64, P, P]
     so.nvfp4_observer_update.argtypes = [P, P, I, ctypes.c_float, P]
@@ -109,8 +112,8 @@ def nvfp4_amax(tensors, amax: torch.Tensor | None = None, accumulate: bool = Fal
 def nvfp4_fake_quant(x: torch.Tensor, y: torch.Tensor | None = None,
                      amax_in: torch.Tensor | None = None,
                      amax_out: torch.Tensor | None = None) -> torch.Tensor:
-    """bf16 [R, C] -> fake-quantized bf16 [R, C].  Without amax_in the amax is computed
-    first (into amax_out, allocated when not given and then reachable as y.amax)."""
+    """bf16 [R, C] -> fake-quantized bf16 [R, C].  Without amax_in the amax of x is
+    computed first, into amax_out (a scratch scalar when not given)."""
     rows, cols = _matrix(x, "x")
     if y is None:
         y = torch.empty_like(x)
@@ -122,6 +125,51 @@ def nvfp4_fake_quant(x: torch.Tensor, y: torch.Tensor | None = None,
     _check(lib.nvfp4_fake_quant(_ptr(x), _ptr(y), rows, cols, _ptr(amax_in), _ptr(amax_out),
                                 _stream(x.device)), "nvfp4_fake_quant")
     return y
+
+
+def nvfp4_fake_quant_group(xs, ys=None, amax_in: torch.Tensor | None = None,
+                           amax_out: torch.Tensor | None = None):
+    """Fake-quantize fused siblings with one shared amax -> list of bf16 outputs.
+    Without amax_in the amax over all of xs is computed first, into amax_out."""
+    xs = list(xs)
+    if not xs:
+        raise ValueError("nvfp4_fake_quant_group needs at least one tensor")
+    shapes = [_matrix(x, "xs[%d]" % i) for i, x in enumerate(xs)]
+    dev = xs[0].device
+    ys = [torch.empty_like(x) for x in xs] if ys is None else list(ys)
+    if len(ys) != len(xs):
+        raise ValueError("ys must have one output per input")
+    for i, (x, y) in enumerate(zip(xs, ys)):
+        if _matrix(y, "ys[%d]" % i) != x.shape or x.device != dev or y.device != dev:
+            raise ValueError("ys[%d] must match xs[%d] in shape and device" % (i, i))
+    if amax_in is not None:
+        _scalar(dev, amax_in)
+    elif amax_out is None:
+        amax_out = _scalar(dev)
+    n = len(xs)
+    xp = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+    yp = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+    rs = (ctypes.c_int64 * n)(*[r for r, _ in shapes])
+    cs = (ctypes.c_int64 * n)(*[c for _, c in shapes])
+    _check(lib.nvfp4_fake_quant_group(xp, yp, rs, cs, n, _ptr(amax_in), _ptr(amax_out), _stream(dev)),
+           "nvfp4_fake_quant_group")
+    return ys
+
+
+def nvfp4_fake_quant_dual(x: torch.Tensor, amax0: torch.Tensor, amax1: torch.Tensor,
+                          y0: torch.Tensor | None = None, y1: torch.Tensor | None = None):
+    """One read of x fake-quantized under two amaxes (two observers) -> (y0, y1)."""
+    rows, cols = _matrix(x, "x")
+    _scalar(x.device, amax0)
+    _scalar(x.device, amax1)
+    y0 = torch.empty_like(x) if y0 is None else y0
+    y1 = torch.empty_like(x) if y1 is None else y1
+    for name, y in (("y0", y0), ("y1", y1)):
+        if _matrix(y, name) != x.shape:
+            raise ValueError("%s must have the shape of x" % name)
+    _check(lib.nvfp4_fake_quant_dual(_ptr(x), rows, cols, _ptr(amax0), _ptr(y0), _ptr(amax1), _ptr(y1),
+                                     _stream(x.device)), "nvfp4_fake_quant_dual")
+    return y0, y1
 
 
 def blocks_per_row(cols: int) -> int:

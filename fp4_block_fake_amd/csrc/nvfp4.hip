@@ -533,16 +533,15 @@ __device__ __forceinline__ void load_blocks(const uint4* __restrict__ x, int64_t
 // iteration's loads are issued before the workgroup builds its scale-byte
 // table, so the table build hides under their latency; with kPipeline the
 // next iteration's loads are in flight while the current blocks are processed.
-template <bool NtLd, typename Body>
-__device__ __forceinline__ void quantize_pass(const uint4* __restrict__ x, int64_t nblocks, float gs,
-                                              uint32_t* tab, Body body)
+template <bool NtLd, typename Build, typename Body>
+__device__ __forceinline__ void quantize_pass(const uint4* __restrict__ x, int64_t nblocks, Build build,
+                                              Body body)
 {
     const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
     int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
     uint4 v[kUnroll][2];
     load_blocks<NtLd>(x, base, nblocks, v);
-    if (threadIdx.x < 128)
-        build_entry(threadIdx.x, gs, tab + threadIdx.x * kEntryWords);
+    build();
     __syncthreads();
     for (; base < nblocks; base += stride) {
         uint4 next[kUnroll][2];
@@ -569,6 +568,13 @@ __device__ __forceinline__ void quantize_pass(const uint4* __restrict__ x, int64
     }
 }
 
+// Threads 0..127 tabulate the 128 scale bytes under gs (the other threads idle).
+__device__ __forceinline__ void build_table(float gs, uint32_t* tab)
+{
+    if (threadIdx.x < 128)
+        build_entry(threadIdx.x, gs, tab + threadIdx.x * kEntryWords);
+}
+
 __global__ __launch_bounds__(kThreads) void k_fake_quant(const uint4* __restrict__ x, uint4* y,
                                                          int64_t nblocks,
                                                          const float* __restrict__ amax)
@@ -576,9 +582,91 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant(const uint4* __restrict
     __shared__ uint4 table[128 * kEntryWords / 4];
     uint32_t* tab = reinterpret_cast<uint32_t*>(table);
     const float gs = global_scale_of(*amax);
-    quantize_pass<NVFP4_FQ_NT_LD != 0>(x, nblocks, gs, tab, [&](const uint32_t (&w)[8], int64_t b) {
+    quantize_pass<NVFP4_FQ_NT_LD != 0>(x, nblocks, [&] { build_table(gs, tab); },
+                                       [&](const uint32_t (&w)[8], int64_t b) {
         fake_quant_block<NVFP4_FQ_NT_ST != 0>(w, tab, gs, y, b);
     });
+}
+
+// One read of x, fake-quantized under two amaxes into y0 and y1: an activation
+// seen by two observers (verl QATLinear page, section 5) costs 2 + 2 * 2 bytes
+// per element instead of 2 * (2 + 2).  Each half of the workgroup tabulates
+// one amax.  A lane reads its whole block before writing either output, so
+// y0 == x or y1 == x (in place) is safe.
+static_assert(kThreads == 256, "the dual table build gives each amax 128 threads");
+__global__ __launch_bounds__(kThreads) void k_fake_quant_dual(const uint4* __restrict__ x, uint4* y0,
+                                                              uint4* y1, int64_t nblocks,
+                                                              const float* __restrict__ amax0,
+                                                              const float* __restrict__ amax1)
+{
+    __shared__ uint4 table[2 * 128 * kEntryWords / 4];
+    uint32_t* tab = reinterpret_cast<uint32_t*>(table);
+    const float gs0 = global_scale_of(*amax0);
+    const float gs1 = global_scale_of(*amax1);
+    quantize_pass<NVFP4_FQ_NT_LD != 0>(x, nblocks, [&] {
+        const uint32_t half = threadIdx.x >> 7, s = threadIdx.x & 127u;
+        build_entry(s, half ? gs1 : gs0, tab + (half * 128u + s) * kEntryWords);
+    }, [&](const uint32_t (&w)[8], int64_t b) {
+        fake_quant_block<NVFP4_FQ_NT_ST != 0>(w, tab, gs0, y0, b);
+        fake_quant_block<NVFP4_FQ_NT_ST != 0>(w, tab + 128 * kEntryWords, gs1, y1, b);
+    });
+}
+
+// Tensors that share one amax (fused siblings, verl QATLinear page, section 4),
+// fake-quantized in one launch.  Their blocks are visited in chunks of
+// kThreads * kUnroll blocks, one chunk per workgroup iteration as in
+// quantize_pass; a chunk never spans two tensors, so the tensor of a chunk is
+// the same for the whole workgroup and its pointers stay scalar.
+struct FqGroup {
+    const uint4* x[NVFP4_AMAX_GROUP_MAX];
+    uint4* y[NVFP4_AMAX_GROUP_MAX];
+    int64_t nblocks[NVFP4_AMAX_GROUP_MAX];
+    int64_t chunk_end[NVFP4_AMAX_GROUP_MAX];    // running sum of ceil(nblocks / chunk)
+    int32_t count;
+};
+
+__global__ __launch_bounds__(kThreads) void k_fake_quant_group(FqGroup g, const float* __restrict__ amax)
+{
+    constexpr int64_t kChunk = (int64_t)kThreads * kUnroll;
+    __shared__ uint4 table[128 * kEntryWords / 4];
+    uint32_t* tab = reinterpret_cast<uint32_t*>(table);
+    const float gs = global_scale_of(*amax);
+    const int64_t total = g.chunk_end[g.count - 1];
+    // chunks only grow along the loop, so the tensor cursor only moves forward
+    int t = 0;
+    int64_t begin = 0;
+    auto seek = [&](int64_t c) {
+        while (c >= g.chunk_end[t]) {
+            begin = g.chunk_end[t];
+            ++t;
+        }
+    };
+    int64_t c = blockIdx.x;
+    uint4 v[kUnroll][2];
+    if (c < total) {
+        seek(c);
+        load_blocks<NVFP4_FQ_NT_LD != 0>(g.x[t], (c - begin) * kChunk + threadIdx.x, g.nblocks[t], v);
+    }
+    build_table(gs, tab);
+    __syncthreads();
+    for (; c < total; c += gridDim.x) {
+        const int64_t base = (c - begin) * kChunk + threadIdx.x, n = g.nblocks[t];
+        uint4* y = g.y[t];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t b = walk(base + (int64_t)u * kThreads, n);
+            if (b >= 0) {
+                uint32_t w[8];
+                unpack8(v[u][0], v[u][1], w);
+                fake_quant_block<NVFP4_FQ_NT_ST != 0>(w, tab, gs, y, b);
+            }
+        }
+        if (c + gridDim.x < total) {
+            seek(c + gridDim.x);
+            load_blocks<NVFP4_FQ_NT_LD != 0>(g.x[t], (c + gridDim.x - begin) * kChunk + threadIdx.x,
+                                             g.nblocks[t], v);
+        }
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void k_quantize_pack(const uint4* __restrict__ x,
@@ -593,7 +681,8 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack(const uint4* __restr
     const float gs = global_scale_of(*amax);
     if (blockIdx.x == 0 && threadIdx.x == 0)
         *gs_out = gs;
-    quantize_pass<NVFP4_QP_NT_LD != 0>(x, nblocks, gs, tab, [&](const uint32_t (&w)[8], int64_t b) {
+    quantize_pass<NVFP4_QP_NT_LD != 0>(x, nblocks, [&] { build_table(gs, tab); },
+                                       [&](const uint32_t (&w)[8], int64_t b) {
         pack_block<NVFP4_QP_NT_ST != 0>(w, tab, gs, packed, scales, b);
     });
 }
@@ -844,14 +933,88 @@ nvfp4_status enqueue_amax(const void* const* xs, const int64_t* numels, int n, f
     return launched();
 }
 
+// Collects non-empty tensors and enqueues one amax launch per
+// NVFP4_AMAX_GROUP_MAX of them.
+struct AmaxBatch {
+    const void* x[NVFP4_AMAX_GROUP_MAX];
+    int64_t n[NVFP4_AMAX_GROUP_MAX];
+    int k = 0;
+
+    nvfp4_status add(const void* p, int64_t numel, float* amax, hipStream_t s)
+    {
+        if (numel == 0)
+            return NVFP4_OK;
+        x[k] = p;
+        n[k] = numel;
+        return ++k == NVFP4_AMAX_GROUP_MAX ? flush(amax, s) : NVFP4_OK;
+    }
+    nvfp4_status flush(float* amax, hipStream_t s)
+    {
+        const int c = k;
+        k = 0;
+        return c ? enqueue_amax(x, n, c, amax, s) : NVFP4_OK;
+    }
+};
+
+// *amax := 0, so that the atomic maxima of the launches that follow start clean.
+nvfp4_status enqueue_reset(float* amax, hipStream_t s)
+{
+    k_set_scalar<<<1, 1, 0, s>>>(amax, 0.0f);
+    return launched();
+}
+
 nvfp4_status enqueue_amax_one(const void* x, int64_t numel, float* amax, hipStream_t stream)
 {
-    k_set_scalar<<<1, 1, 0, stream>>>(amax, 0.0f);
-    nvfp4_status st = launched();
+    nvfp4_status st = enqueue_reset(amax, stream);
     if (st != NVFP4_OK || numel == 0)
         return st;
     return enqueue_amax(&x, &numel, 1, amax, stream);
 }
+
+// One fake-quant launch of a single tensor with a device amax.
+nvfp4_status enqueue_fake_quant(const void* x, void* y, int64_t cols, const Matrix& m, const float* a,
+                                hipStream_t s)
+{
+    if (m.numel == 0)
+        return NVFP4_OK;
+    if (m.ragged) {
+        const RaggedShape g{cols, m.nbr, m.nblocks};
+        k_fake_quant_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
+            static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), g, a);
+        return launched();
+    }
+    k_fake_quant<<<persistent_grid(m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
+        static_cast<const uint4*>(x), static_cast<uint4*>(y), m.nblocks, a);
+    return launched();
+}
+
+// Collects tensors whose rows are whole blocks and enqueues one group launch
+// per NVFP4_AMAX_GROUP_MAX of them.
+struct FakeQuantBatch {
+    FqGroup g{};
+    int64_t chunks = 0;
+
+    nvfp4_status add(const void* x, void* y, int64_t nblocks, const float* a, hipStream_t s)
+    {
+        constexpr int64_t kChunk = (int64_t)kThreads * kUnroll;
+        const int k = g.count;
+        g.x[k] = static_cast<const uint4*>(x);
+        g.y[k] = static_cast<uint4*>(y);
+        g.nblocks[k] = nblocks;
+        chunks += (nblocks + kChunk - 1) / kChunk;
+        g.chunk_end[k] = chunks;
+        return ++g.count == NVFP4_AMAX_GROUP_MAX ? flush(a, s) : NVFP4_OK;
+    }
+    nvfp4_status flush(const float* a, hipStream_t s)
+    {
+        if (g.count == 0)
+            return NVFP4_OK;
+        k_fake_quant_group<<<persistent_grid(chunks, 1, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(g, a);
+        g = FqGroup{};
+        chunks = 0;
+        return launched();
+    }
+};
 
 }  // namespace
 
@@ -894,28 +1057,15 @@ nvfp4_status nvfp4_amax(const void* const* xs, const int64_t* numels, int n, flo
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (!accumulate) {
-        k_set_scalar<<<1, 1, 0, s>>>(amax, 0.0f);
-        if (launched() != NVFP4_OK)
-            return NVFP4_ERR_HIP;
-    }
-    for (int first = 0; first < n; first += NVFP4_AMAX_GROUP_MAX) {
-        const void* gx[NVFP4_AMAX_GROUP_MAX];
-        int64_t gn[NVFP4_AMAX_GROUP_MAX];
-        int k = 0;
-        for (int i = first; i < n && i < first + NVFP4_AMAX_GROUP_MAX; ++i)
-            if (numels[i] > 0) {
-                gx[k] = xs[i];
-                gn[k] = numels[i];
-                ++k;
-            }
-        if (k == 0)
-            continue;
-        nvfp4_status st = enqueue_amax(gx, gn, k, amax, s);
+    if (!accumulate && enqueue_reset(amax, s) != NVFP4_OK)
+        return NVFP4_ERR_HIP;
+    AmaxBatch batch;
+    for (int i = 0; i < n; ++i) {
+        const nvfp4_status st = batch.add(xs[i], numels[i], amax, s);
         if (st != NVFP4_OK)
             return st;
     }
-    return NVFP4_OK;
+    return batch.flush(amax, s);
 }
 
 nvfp4_status nvfp4_fake_quant(const void* x, void* y, int64_t rows, int64_t cols,
@@ -947,16 +1097,110 @@ nvfp4_status nvfp4_fake_quant(const void* x, void* y, int64_t rows, int64_t cols
             return st;
         a = amax_out;
     }
-    if (n == 0)
+    return enqueue_fake_quant(x, y, cols, m, a, s);
+}
+
+nvfp4_status nvfp4_fake_quant_group(const void* const* xs, void* const* ys, const int64_t* rows,
+                                    const int64_t* cols, int n, const float* amax_in,
+                                    float* amax_out, void* stream)
+{
+    if (!xs || !ys || !rows || !cols)
+        return NVFP4_ERR_NULL;
+    if (n < 1)
+        return NVFP4_ERR_ARG;
+    for (int i = 0; i < n; ++i) {
+        Matrix m;
+        const nvfp4_status st = check_matrix(rows[i], cols[i], &m);
+        if (st != NVFP4_OK)
+            return st;
+        if (m.numel > 0 && (!xs[i] || !ys[i]))
+            return NVFP4_ERR_NULL;
+    }
+    if (!amax_in && !amax_out)
+        return NVFP4_ERR_NULL;
+    if ((amax_in && !aligned(amax_in, 4)) || (!amax_in && !aligned(amax_out, 4)))
+        return NVFP4_ERR_ALIGN;
+    for (int i = 0; i < n; ++i)
+        if (!aligned(xs[i], 16) || !aligned(ys[i], 16))
+            return NVFP4_ERR_ALIGN;
+    for (int i = 0; i < n; ++i) {
+        const uint64_t bi = 2 * (uint64_t)(rows[i] * cols[i]);
+        for (int j = 0; j < n; ++j) {
+            const uint64_t bj = 2 * (uint64_t)(rows[j] * cols[j]);
+            if (!(i == j && xs[i] == ys[i]) && overlap(ys[i], bi, xs[j], bj))
+                return NVFP4_ERR_OVERLAP;
+            if (j > i && overlap(ys[i], bi, ys[j], bj))
+                return NVFP4_ERR_OVERLAP;
+        }
+        if (!amax_in && (overlap(amax_out, 4, xs[i], bi) || overlap(amax_out, 4, ys[i], bi)))
+            return NVFP4_ERR_OVERLAP;
+        if (amax_in && overlap(amax_in, 4, ys[i], bi))
+            return NVFP4_ERR_OVERLAP;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    nvfp4_status st;
+    const float* a = amax_in;
+    if (!a) {
+        if (enqueue_reset(amax_out, s) != NVFP4_OK)
+            return NVFP4_ERR_HIP;
+        AmaxBatch amax;
+        for (int i = 0; i < n; ++i)
+            if ((st = amax.add(xs[i], rows[i] * cols[i], amax_out, s)) != NVFP4_OK)
+                return st;
+        if ((st = amax.flush(amax_out, s)) != NVFP4_OK)
+            return st;
+        a = amax_out;
+    }
+    FakeQuantBatch batch;
+    for (int i = 0; i < n; ++i) {
+        Matrix m;
+        check_matrix(rows[i], cols[i], &m);
+        if (m.numel == 0)
+            continue;
+        st = m.ragged ? enqueue_fake_quant(xs[i], ys[i], cols[i], m, a, s)
+                      : batch.add(xs[i], ys[i], m.nblocks, a, s);
+        if (st != NVFP4_OK)
+            return st;
+    }
+    return batch.flush(a, s);
+}
+
+nvfp4_status nvfp4_fake_quant_dual(const void* x, int64_t rows, int64_t cols, const float* amax0,
+                                   void* y0, const float* amax1, void* y1, void* stream)
+{
+    Matrix m;
+    nvfp4_status st = check_matrix(rows, cols, &m);
+    if (st != NVFP4_OK)
+        return st;
+    if ((m.numel > 0 && (!x || !y0 || !y1)) || !amax0 || !amax1)
+        return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(y0, 16) || !aligned(y1, 16) || !aligned(amax0, 4) ||
+        !aligned(amax1, 4))
+        return NVFP4_ERR_ALIGN;
+    const uint64_t bytes = 2 * (uint64_t)m.numel;
+    if (overlap(y0, bytes, y1, bytes) || (y0 != x && overlap(y0, bytes, x, bytes)) ||
+        (y1 != x && overlap(y1, bytes, x, bytes)))
+        return NVFP4_ERR_OVERLAP;
+    for (const float* a : {amax0, amax1})
+        if (overlap(a, 4, y0, bytes) || overlap(a, 4, y1, bytes))
+            return NVFP4_ERR_OVERLAP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (m.numel == 0)
         return NVFP4_OK;
     if (m.ragged) {
-        const RaggedShape g{cols, m.nbr, m.nblocks};
-        k_fake_quant_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
-            static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), g, a);
-        return launched();
+        // two passes; an output written in place goes last, after x has been read
+        if (y0 == x) {
+            st = enqueue_fake_quant(x, y1, cols, m, amax1, s);
+            return st != NVFP4_OK ? st : enqueue_fake_quant(x, y0, cols, m, amax0, s);
+        }
+        st = enqueue_fake_quant(x, y0, cols, m, amax0, s);
+        return st != NVFP4_OK ? st : enqueue_fake_quant(x, y1, cols, m, amax1, s);
     }
-    k_fake_quant<<<persistent_grid(m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
-        static_cast<const uint4*>(x), static_cast<uint4*>(y), m.nblocks, a);
+    k_fake_quant_dual<<<persistent_grid(m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
+        static_cast<const uint4*>(x), static_cast<uint4*>(y0), static_cast<uint4*>(y1), m.nblocks,
+        amax0, amax1);
     return launched();
 }
 

@@ -108,6 +108,48 @@ nvfp4_status nvfp4_fake_quant(const void* x, void* y, int64_t rows, int64_t cols
                               const float* amax_in, float* amax_out, void* stream);
 
 /*
+ * nvfp4_fake_quant_group -- fake-quantize n tensors that share one amax, the
+ * fused siblings of one layer (verl QATLinear page, section 4: q, k and v, or
+ * gate and up, are fake-quantized with the maximum over all of them).  Each
+ * output equals nvfp4_fake_quant of its tensor with that shared amax; tensors
+ * whose rows are whole blocks are fake-quantized together, one launch per
+ * NVFP4_AMAX_GROUP_MAX of them (ragged tensors get a launch each).
+ *
+ *   xs, ys       HOST arrays of n device pointers: bf16 [rows[i], cols[i]],
+ *                16-byte aligned; NULL allowed for an empty tensor.  ys[i] ==
+ *                xs[i] (exact in-place) is allowed; any other overlap between
+ *                an output and an input or another output is an error.
+ *   rows, cols   HOST arrays of n shapes, each as for nvfp4_fake_quant
+ *   n            >= 1
+ *   amax_in      NULL: the amax of the whole group is computed first (one
+ *                grouped pass, as nvfp4_amax) into amax_out (required then).
+ *                Non-NULL: device fp32 amax used for every tensor.
+ *   amax_out     as for nvfp4_fake_quant
+ * Errors: NULL, SHAPE, ALIGN, OVERLAP, ARG (n < 1), HIP.
+ */
+nvfp4_status nvfp4_fake_quant_group(const void* const* xs, void* const* ys, const int64_t* rows,
+                                    const int64_t* cols, int n, const float* amax_in,
+                                    float* amax_out, void* stream);
+
+/*
+ * nvfp4_fake_quant_dual -- one bf16 [rows, cols] tensor fake-quantized under
+ * two amaxes, reading x once: the activation of a layer fake-quantized with
+ * the states of two observers (verl QATLinear page, section 5; for instance
+ * static running max and EMA side by side).  y0 equals nvfp4_fake_quant(x,
+ * amax_in = amax0) and y1 the same with amax1.  The stream traffic is 6 bytes
+ * per element instead of 8 for two calls.
+ *
+ *   x            device bf16 [rows, cols], 16-byte aligned
+ *   amax0, amax1 device fp32 amaxes (required), 4-byte aligned
+ *   y0, y1       device bf16 [rows, cols], 16-byte aligned; either one (not
+ *                both) may be x itself; y0 and y1 must not overlap each other,
+ *                the amaxes, or x otherwise
+ * Errors: NULL, SHAPE, ALIGN, OVERLAP, HIP.
+ */
+nvfp4_status nvfp4_fake_quant_dual(const void* x, int64_t rows, int64_t cols, const float* amax0,
+                                   void* y0, const float* amax1, void* y1, void* stream);
+
+/*
  * nvfp4_quantize_pack -- bf16 [rows, cols] -> packed NVFP4 (VideoX-Fun page,
  * quantize_weight_to_float4, returning nibbles, E4M3 block scales and the
  * fp32 per-tensor factor).

@@ -29,10 +29,10 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(nvfp4_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_five_calls():
+def test_header_declares_every_call():
     names = declared_functions()
-    for n in ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_quantize_pack", "nvfp4_dequant_unpack",
-              "nvfp4_observer_update", "nvfp4_strerror"):
+    for n in ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
+              "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_observer_update", "nvfp4_strerror"):
         assert n in names
 
 
@@ -66,6 +66,54 @@ def test_fake_quant_validation():
     assert fq(A, A + 16, 4, 16, None, A + (2 << 30)) == ERR_OVERLAP             # partial overlap
     assert fq(A, A + (1 << 30), 4, 16, None, A + 64) == ERR_OVERLAP             # amax inside x
     assert fq(A, A + (1 << 30), 4, 16, A + (1 << 30) + 4, None) == ERR_OVERLAP  # amax_in inside y
+
+
+def test_fake_quant_group_validation():
+    g = nv.lib.nvfp4_fake_quant_group
+    G = 1 << 30
+
+    def call(xs, ys, shapes, amax_in=None, amax_out=A + 9 * G, n=None):
+        n = len(xs) if n is None else n
+        k = max(len(xs), 1)
+        xp = (ctypes.c_void_p * k)(*xs)
+        yp = (ctypes.c_void_p * k)(*ys)
+        rs = (ctypes.c_int64 * k)(*[r for r, _ in shapes])
+        cs = (ctypes.c_int64 * k)(*[c for _, c in shapes])
+        return g(xp, yp, rs, cs, n, P(amax_in), P(amax_out), None)
+
+    x0, x1, y0, y1 = A, A + G, A + 2 * G, A + 3 * G
+    sh = [(4, 16), (8, 32)]
+    assert g(None, None, None, None, 1, None, P(A), None) == ERR_NULL
+    assert call([x0], [y0], [(4, 16)], n=0) == ERR_ARG
+    assert call([x0, x1], [y0, y1], [(4, 16), (4, 0)]) == ERR_SHAPE
+    assert call([x0, None], [y0, y1], sh) == ERR_NULL
+    assert call([x0, x1], [y0, y1], sh, amax_in=None, amax_out=None) == ERR_NULL
+    assert call([x0, x1 + 8], [y0, y1], sh) == ERR_ALIGN
+    assert call([x0, x1], [y0, y1 + 4], sh) == ERR_ALIGN
+    assert call([x0, x1], [y0, y1], sh, amax_out=A + 9 * G + 2) == ERR_ALIGN
+    assert call([x0, x1], [x1, y1], sh) == ERR_OVERLAP             # y0 is another member's input
+    assert call([x0, x1], [y0, y0 + 64], sh) == ERR_OVERLAP        # two outputs overlap
+    assert call([x0, x1], [x0 + 16, y1], sh) == ERR_OVERLAP        # partial overlap with its input
+    assert call([x0, x1], [y0, y1], sh, amax_out=x1 + 4) == ERR_OVERLAP
+    assert call([x0, x1], [y0, y1], sh, amax_in=y1 + 8) == ERR_OVERLAP
+
+
+def test_fake_quant_dual_validation():
+    d = nv.lib.nvfp4_fake_quant_dual
+    G = 1 << 30
+    x, y0, y1, a0, a1 = A, A + G, A + 2 * G, A + 3 * G, A + 3 * G + 4
+    assert d(P(x), 4, 0, P(a0), P(y0), P(a1), P(y1), None) == ERR_SHAPE
+    assert d(P(x), -1, 16, P(a0), P(y0), P(a1), P(y1), None) == ERR_SHAPE
+    assert d(None, 4, 16, P(a0), P(y0), P(a1), P(y1), None) == ERR_NULL
+    assert d(P(x), 4, 16, None, P(y0), P(a1), P(y1), None) == ERR_NULL
+    assert d(P(x), 4, 16, P(a0), P(y0), None, P(y1), None) == ERR_NULL
+    assert d(P(x), 4, 16, P(a0), P(y0), P(a1), None, None) == ERR_NULL
+    assert d(P(x + 8), 4, 16, P(a0), P(y0), P(a1), P(y1), None) == ERR_ALIGN
+    assert d(P(x), 4, 16, P(a0 + 1), P(y0), P(a1), P(y1), None) == ERR_ALIGN
+    assert d(P(x), 4, 16, P(a0), P(y0), P(a1), P(y0), None) == ERR_OVERLAP     # y0 == y1
+    assert d(P(x), 4, 16, P(a0), P(x), P(a1), P(x), None) == ERR_OVERLAP       # both in place
+    assert d(P(x), 4, 16, P(a0), P(x + 32), P(a1), P(y1), None) == ERR_OVERLAP  # partial
+    assert d(P(x), 4, 16, P(y1 + 4), P(y0), P(a1), P(y1), None) == ERR_OVERLAP  # amax in an output
 
 
 def test_quantize_pack_validation():

@@ -23,38 +23,12 @@ if not torch.cuda.is_available():
 
 import fp4_block_fake_amd as nv  # noqa: E402
 
-DEV = torch.device("cuda:0")
 EPS32 = np.float32(1e-12)
 
 
 # ---------------------------------------------------------------- helpers
 
-def say(msg):
-    print("[gpu-parity] " + msg, flush=True)
-
-
-def dev(a):
-    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
-
-
-def host(t):
-    return t.view(torch.int16).cpu().numpy().view(np.uint16)
-
-
-def fbits(v):
-    return int(np.float32(v).view(np.uint32))
-
-
-def scalar(v):
-    return torch.tensor([v], dtype=torch.float32, device=DEV)
-
-
-def assert_same(got, want, what):
-    got, want = np.asarray(got), np.asarray(want)
-    assert got.shape == want.shape, "%s: shape %s vs %s" % (what, got.shape, want.shape)
-    bad = np.flatnonzero(got.reshape(-1) != want.reshape(-1))
-    assert bad.size == 0, "%s: %d mismatches, first at %d: got %r want %r" % (
-        what, bad.size, bad[0], got.reshape(-1)[bad[0]], want.reshape(-1)[bad[0]])
+from gpu_util import DEV, assert_same, dev, fbits, host, sample_rows, say, scalar  # noqa: E402
 
 
 def check_all_ops(x, amax_in=None, what=""):
@@ -80,11 +54,6 @@ def check_all_ops(x, amax_in=None, what=""):
     assert_same(host(y), y_ref, what + " fake-quant")
     assert_same(host(yd), y_ref, what + " dequant-unpack")
     return y
-
-
-def sample_rows(rows, seed, k=62):
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, k, replace=False)]))
 
 
 # ---------------------------------------------------------------- the five configurations
