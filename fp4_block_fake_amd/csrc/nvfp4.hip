@@ -55,10 +55,10 @@ namespace {
 // MI355X (c5 weight, 470 MB); the macros let a build be re-tuned without
 // editing the kernels.
 #ifndef NVFP4_UNROLL
-#define NVFP4_UNROLL 4            // blocks per lane per iteration: fake-quant, pack
+#define NVFP4_UNROLL 4            // half blocks per lane per iteration: fake-quant, pack
 #endif
 #ifndef NVFP4_DQ_UNROLL
-#define NVFP4_DQ_UNROLL 8         // blocks per lane per iteration: unpack
+#define NVFP4_DQ_UNROLL 8         // half blocks per lane per iteration: unpack
 #endif
 #ifndef NVFP4_AMAX_UNROLL
 #define NVFP4_AMAX_UNROLL 8       // 16-byte vectors per lane per amax chunk
@@ -73,28 +73,25 @@ namespace {
 #define NVFP4_QP_WG_PER_CU 64
 #endif
 #ifndef NVFP4_DQ_WG_PER_CU
-#define NVFP4_DQ_WG_PER_CU 16
+#define NVFP4_DQ_WG_PER_CU 32
 #endif
 // 1: the quantizing passes walk the tensor from its end, so they start on the
-// data the amax pass read last.  This pays only when the amax pass leaves x in
-// the Infinity Cache, i.e. with NVFP4_AMAX_NT 0; streaming amax loads win more.
+// data the amax pass read last (measured no better than forward on MI355X).
 #ifndef NVFP4_REVERSE
 #define NVFP4_REVERSE 0
 #endif
-// 1: the quantizing passes keep the next iteration's loads in flight while
-// processing the current one (more registers, fewer waves)
-#ifndef NVFP4_PIPELINE
-#define NVFP4_PIPELINE 0
-#endif
-// non-temporal (streaming) hints on loads (LD) and stores (ST)
+// Non-temporal (streaming) hints on loads (LD) and stores (ST).  The amax pass
+// reads with allocating loads: what it reads last stays in the Infinity Cache
+// (256 MB), where the quantizing pass over the same tensor finds it.  The
+// quantizing passes stream x in and their outputs out.
 #ifndef NVFP4_AMAX_NT
-#define NVFP4_AMAX_NT 1
+#define NVFP4_AMAX_NT 0
 #endif
 #ifndef NVFP4_FQ_NT_LD
-#define NVFP4_FQ_NT_LD 0
+#define NVFP4_FQ_NT_LD 1
 #endif
 #ifndef NVFP4_FQ_NT_ST
-#define NVFP4_FQ_NT_ST 0
+#define NVFP4_FQ_NT_ST 1
 #endif
 #ifndef NVFP4_QP_NT_LD
 #define NVFP4_QP_NT_LD 1
@@ -103,7 +100,7 @@ namespace {
 #define NVFP4_QP_NT_ST 1
 #endif
 #ifndef NVFP4_DQ_NT_ST
-#define NVFP4_DQ_NT_ST 0
+#define NVFP4_DQ_NT_ST 1
 #endif
 
 constexpr int kThreads = 256;                    // 4 waves of 64
@@ -111,7 +108,6 @@ constexpr int kUnroll = NVFP4_UNROLL;
 constexpr int kDqUnroll = NVFP4_DQ_UNROLL;
 constexpr int kAmaxUnroll = NVFP4_AMAX_UNROLL;
 constexpr bool kReverse = NVFP4_REVERSE != 0;
-constexpr bool kPipeline = NVFP4_PIPELINE != 0;
 
 constexpr float kEps = 1e-12f;    // clamp of the amax and of the block scale
 constexpr float kGsNumerator = 2688.0f;  // E4M3 max 448 times E2M1 max 6
@@ -154,6 +150,14 @@ __device__ __forceinline__ void store16(uint4* p, uint4 v)
 {
     if (NT)
         __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+    else
+        *p = v;
+}
+template <bool NT>
+__device__ __forceinline__ void store4(uint32_t* p, uint32_t v)
+{
+    if (NT)
+        __builtin_nontemporal_store(v, p);
     else
         *p = v;
 }
@@ -354,14 +358,9 @@ __device__ __forceinline__ void decode_store(uint32_t c0, uint32_t c1, float sd,
                                                decode_pair<2>(c1, sd), decode_pair<3>(c1, sd)));
 }
 
-// Block scale byte of a block from its eight dwords.
-__device__ __forceinline__ uint32_t block_scale_byte(const uint32_t (&w)[8], float gs)
+// E4M3 scale byte of a block whose largest magnitude has the bf16 bits bm.
+__device__ __forceinline__ uint32_t scale_byte_of(uint32_t bm, float gs)
 {
-    uint32_t mx = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        mx = pk_max(mx, w[i] & 0x7FFF7FFFu);
-    const uint32_t bm = max(mx & 0xFFFFu, mx >> 16);
     // bamax / 6 without a divide: a bf16 value has 8 significant bits, so its
     // quotient by 3 never lies within 2^-52 (relative) of a binary32 rounding
     // mid-point, and rounding the binary64 product with 1/6 once more to
@@ -372,6 +371,67 @@ __device__ __forceinline__ uint32_t block_scale_byte(const uint32_t (&w)[8], flo
     // which the min turns into the saturated 0x7E
     const uint32_t s = __builtin_amdgcn_cvt_pk_fp8_f32(sixth * gs, 0.0f, 0, false) & 0xFFu;
     return s < 0x7Eu ? s : 0x7Eu;
+}
+
+// Scale byte of a block from its eight dwords (one lane holds the whole block).
+__device__ __forceinline__ uint32_t block_scale_byte(const uint32_t (&w)[8], float gs)
+{
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        mx = pk_max(mx, w[i] & 0x7FFF7FFFu);
+    return scale_byte_of(max(mx & 0xFFFFu, mx >> 16), gs);
+}
+
+// ---------------------------------------------------------------- half blocks
+//
+// The streaming kernels give each lane half a block: lanes 2k and 2k+1 hold the
+// two 8-element halves of one block, so every load and store is contiguous
+// across the wave (16 bytes per lane of bf16, 4 bytes per lane of codes).  On
+// MI355X this layout, with streaming (non-temporal) loads and stores, moves a
+// read-and-write stream ~15% faster than one lane per block accessing 32
+// bytes at a 32-byte lane stride.  The two lanes of a block are always both
+// active or both inactive: element counts of whole-block tensors are even in
+// halves, and every guard compares an even-aligned pair the same way.
+
+// Largest magnitude (bf16 bits) of the block whose half this lane holds: its
+// own four dwords, then the partner lane's maximum by a DPP quad permute
+// [1, 0, 3, 2] (lane 2k <-> 2k+1).
+__device__ __forceinline__ uint32_t pair_max(const uint32_t (&w)[4])
+{
+    const uint32_t mx = pk_max(pk_max(w[0] & 0x7FFF7FFFu, w[1] & 0x7FFF7FFFu),
+                               pk_max(w[2] & 0x7FFF7FFFu, w[3] & 0x7FFF7FFFu));
+    const uint32_t m = max(mx & 0xFFFFu, mx >> 16);
+    return max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0xB1, 0xF, 0xF, false));
+}
+
+// The eight codes of a half block (one dword of nibbles) under table entry e.
+__device__ __forceinline__ uint32_t half_codes(const uint32_t (&w)[4], const uint32_t* e)
+{
+    const uint32_t head = e[0];
+    if (!(head & kNotFast))
+        return codes_fast(w, __uint_as_float(head));
+    uint32_t t[6];
+    const uint4 a = *reinterpret_cast<const uint4*>(e + 2);
+    const uint2 b = *reinterpret_cast<const uint2*>(e + 6);
+    t[0] = a.x; t[1] = a.y; t[2] = a.z; t[3] = a.w; t[4] = b.x; t[5] = b.y;
+    return codes_threshold(w, t - 2);
+}
+
+// Eight codes -> eight bf16 outputs (16 bytes).
+__device__ __forceinline__ uint4 decode_half(uint32_t c, float sd)
+{
+    return make_uint4(decode_pair<0>(c, sd), decode_pair<1>(c, sd), decode_pair<2>(c, sd),
+                      decode_pair<3>(c, sd));
+}
+
+// Fake-quant of a half block whose block maximum is bm, into y[j].
+template <bool NtStore>
+__device__ __forceinline__ void fake_quant_half(const uint32_t (&w)[4], uint32_t bm, const uint32_t* tab,
+                                                float gs, uint4* y, int64_t j)
+{
+    const uint32_t* e = tab + scale_byte_of(bm, gs) * kEntryWords;
+    store16<NtStore>(y + j, decode_half(half_codes(w, e), __uint_as_float(e[1])));
 }
 
 // The 16 codes of a block (two dwords of nibbles) and its table entry.
@@ -391,23 +451,6 @@ __device__ __forceinline__ void block_codes(const uint32_t (&w)[8], const uint32
         c0 = codes_threshold(w, t - 2);
         c1 = codes_threshold(w + 4, t - 2);
     }
-}
-
-__device__ __forceinline__ void unpack8(const uint4& a, const uint4& b, uint32_t (&w)[8])
-{
-    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-}
-
-// Fake-quant one block (its eight input dwords) into y[2b], y[2b+1].
-template <bool NtStore>
-__device__ __forceinline__ void fake_quant_block(const uint32_t (&w)[8], const uint32_t* tab, float gs,
-                                                 uint4* y, int64_t b)
-{
-    const uint32_t* e = tab + block_scale_byte(w, gs) * kEntryWords;
-    uint32_t c0, c1;
-    block_codes(w, e, c0, c1);
-    decode_store<NtStore>(c0, c1, __uint_as_float(e[1]), y, b);
 }
 
 // Quantize-pack one block: eight code bytes into packed[b], its scale byte into scales[b].
@@ -514,57 +557,42 @@ __global__ __launch_bounds__(kThreads) void k_amax(AmaxGroup g, float* out)
     }
 }
 
-// The kUnroll blocks of one iteration of a quantizing pass, loaded into v.
+// The kUnroll half blocks of one iteration of a quantizing pass (zeros past the end).
 template <bool NtLd>
-__device__ __forceinline__ void load_blocks(const uint4* __restrict__ x, int64_t base, int64_t nblocks,
-                                            uint4 (&v)[kUnroll][2])
+__device__ __forceinline__ void load_halves(const uint4* __restrict__ x, int64_t base, int64_t nhalves,
+                                            uint4 (&v)[kUnroll])
 {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        const int64_t b = walk(base + (int64_t)u * kThreads, nblocks);
-        if (b >= 0) {
-            v[u][0] = load16<NtLd>(x + 2 * b);
-            v[u][1] = load16<NtLd>(x + 2 * b + 1);
-        }
+        const int64_t j = walk(base + (int64_t)u * kThreads, nhalves);
+        v[u] = j >= 0 ? load16<NtLd>(x + j) : make_uint4(0u, 0u, 0u, 0u);
     }
 }
 
-// A quantizing pass over all blocks with a grid stride.  The first
-// iteration's loads are issued before the workgroup builds its scale-byte
-// table, so the table build hides under their latency; with kPipeline the
-// next iteration's loads are in flight while the current blocks are processed.
+// A quantizing pass over all half blocks with a grid stride; body(w, j) gets
+// the four dwords of half j.  The first iteration's loads are issued before
+// the workgroup builds its scale-byte table, so the table build hides under
+// their latency.
 template <bool NtLd, typename Build, typename Body>
-__device__ __forceinline__ void quantize_pass(const uint4* __restrict__ x, int64_t nblocks, Build build,
+__device__ __forceinline__ void quantize_pass(const uint4* __restrict__ x, int64_t nhalves, Build build,
                                               Body body)
 {
     const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
     int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
-    uint4 v[kUnroll][2];
-    load_blocks<NtLd>(x, base, nblocks, v);
+    uint4 v[kUnroll];
+    load_halves<NtLd>(x, base, nhalves, v);
     build();
     __syncthreads();
-    for (; base < nblocks; base += stride) {
-        uint4 next[kUnroll][2];
-        if (kPipeline)
-            load_blocks<NtLd>(x, base + stride, nblocks, next);
+    for (; base < nhalves; base += stride) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t b = walk(base + (int64_t)u * kThreads, nblocks);
-            if (b >= 0) {
-                uint32_t w[8];
-                unpack8(v[u][0], v[u][1], w);
-                body(w, b);
+            const int64_t j = walk(base + (int64_t)u * kThreads, nhalves);
+            if (j >= 0) {
+                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                body(w, j);
             }
         }
-        if (kPipeline) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                v[u][0] = next[u][0];
-                v[u][1] = next[u][1];
-            }
-        } else {
-            load_blocks<NtLd>(x, base + stride, nblocks, v);
-        }
+        load_halves<NtLd>(x, base + stride, nhalves, v);
     }
 }
 
@@ -576,26 +604,26 @@ __device__ __forceinline__ void build_table(float gs, uint32_t* tab)
 }
 
 __global__ __launch_bounds__(kThreads) void k_fake_quant(const uint4* __restrict__ x, uint4* y,
-                                                         int64_t nblocks,
+                                                         int64_t nhalves,
                                                          const float* __restrict__ amax)
 {
     __shared__ uint4 table[128 * kEntryWords / 4];
     uint32_t* tab = reinterpret_cast<uint32_t*>(table);
     const float gs = global_scale_of(*amax);
-    quantize_pass<NVFP4_FQ_NT_LD != 0>(x, nblocks, [&] { build_table(gs, tab); },
-                                       [&](const uint32_t (&w)[8], int64_t b) {
-        fake_quant_block<NVFP4_FQ_NT_ST != 0>(w, tab, gs, y, b);
+    quantize_pass<NVFP4_FQ_NT_LD != 0>(x, nhalves, [&] { build_table(gs, tab); },
+                                       [&](const uint32_t (&w)[4], int64_t j) {
+        fake_quant_half<NVFP4_FQ_NT_ST != 0>(w, pair_max(w), tab, gs, y, j);
     });
 }
 
 // One read of x, fake-quantized under two amaxes into y0 and y1: an activation
 // seen by two observers (verl QATLinear page, section 5) costs 2 + 2 * 2 bytes
 // per element instead of 2 * (2 + 2).  Each half of the workgroup tabulates
-// one amax.  A lane reads its whole block before writing either output, so
+// one amax.  A lane reads its half block before writing either output, so
 // y0 == x or y1 == x (in place) is safe.
 static_assert(kThreads == 256, "the dual table build gives each amax 128 threads");
 __global__ __launch_bounds__(kThreads) void k_fake_quant_dual(const uint4* __restrict__ x, uint4* y0,
-                                                              uint4* y1, int64_t nblocks,
+                                                              uint4* y1, int64_t nhalves,
                                                               const float* __restrict__ amax0,
                                                               const float* __restrict__ amax1)
 {
@@ -603,25 +631,26 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant_dual(const uint4* __res
     uint32_t* tab = reinterpret_cast<uint32_t*>(table);
     const float gs0 = global_scale_of(*amax0);
     const float gs1 = global_scale_of(*amax1);
-    quantize_pass<NVFP4_FQ_NT_LD != 0>(x, nblocks, [&] {
+    quantize_pass<NVFP4_FQ_NT_LD != 0>(x, nhalves, [&] {
         const uint32_t half = threadIdx.x >> 7, s = threadIdx.x & 127u;
         build_entry(s, half ? gs1 : gs0, tab + (half * 128u + s) * kEntryWords);
-    }, [&](const uint32_t (&w)[8], int64_t b) {
-        fake_quant_block<NVFP4_FQ_NT_ST != 0>(w, tab, gs0, y0, b);
-        fake_quant_block<NVFP4_FQ_NT_ST != 0>(w, tab + 128 * kEntryWords, gs1, y1, b);
+    }, [&](const uint32_t (&w)[4], int64_t j) {
+        const uint32_t bm = pair_max(w);
+        fake_quant_half<NVFP4_FQ_NT_ST != 0>(w, bm, tab, gs0, y0, j);
+        fake_quant_half<NVFP4_FQ_NT_ST != 0>(w, bm, tab + 128 * kEntryWords, gs1, y1, j);
     });
 }
 
 // Tensors that share one amax (fused siblings, verl QATLinear page, section 4),
-// fake-quantized in one launch.  Their blocks are visited in chunks of
-// kThreads * kUnroll blocks, one chunk per workgroup iteration as in
-// quantize_pass; a chunk never spans two tensors, so the tensor of a chunk is
-// the same for the whole workgroup and its pointers stay scalar.
+// fake-quantized in one launch.  Their half blocks are visited in chunks of
+// kThreads * kUnroll, one chunk per workgroup iteration as in quantize_pass; a
+// chunk never spans two tensors, so the tensor of a chunk is the same for the
+// whole workgroup and its pointers stay scalar.
 struct FqGroup {
     const uint4* x[NVFP4_AMAX_GROUP_MAX];
     uint4* y[NVFP4_AMAX_GROUP_MAX];
-    int64_t nblocks[NVFP4_AMAX_GROUP_MAX];
-    int64_t chunk_end[NVFP4_AMAX_GROUP_MAX];    // running sum of ceil(nblocks / chunk)
+    int64_t nhalves[NVFP4_AMAX_GROUP_MAX];
+    int64_t chunk_end[NVFP4_AMAX_GROUP_MAX];    // running sum of ceil(nhalves / chunk)
     int32_t count;
 };
 
@@ -642,38 +671,39 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant_group(FqGroup g, const 
         }
     };
     int64_t c = blockIdx.x;
-    uint4 v[kUnroll][2];
+    uint4 v[kUnroll];
     if (c < total) {
         seek(c);
-        load_blocks<NVFP4_FQ_NT_LD != 0>(g.x[t], (c - begin) * kChunk + threadIdx.x, g.nblocks[t], v);
+        load_halves<NVFP4_FQ_NT_LD != 0>(g.x[t], (c - begin) * kChunk + threadIdx.x, g.nhalves[t], v);
     }
     build_table(gs, tab);
     __syncthreads();
     for (; c < total; c += gridDim.x) {
-        const int64_t base = (c - begin) * kChunk + threadIdx.x, n = g.nblocks[t];
+        const int64_t base = (c - begin) * kChunk + threadIdx.x, n = g.nhalves[t];
         uint4* y = g.y[t];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t b = walk(base + (int64_t)u * kThreads, n);
-            if (b >= 0) {
-                uint32_t w[8];
-                unpack8(v[u][0], v[u][1], w);
-                fake_quant_block<NVFP4_FQ_NT_ST != 0>(w, tab, gs, y, b);
+            const int64_t j = walk(base + (int64_t)u * kThreads, n);
+            if (j >= 0) {
+                const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                fake_quant_half<NVFP4_FQ_NT_ST != 0>(w, pair_max(w), tab, gs, y, j);
             }
         }
         if (c + gridDim.x < total) {
             seek(c + gridDim.x);
-            load_blocks<NVFP4_FQ_NT_LD != 0>(g.x[t], (c + gridDim.x - begin) * kChunk + threadIdx.x,
-                                             g.nblocks[t], v);
+            load_halves<NVFP4_FQ_NT_LD != 0>(g.x[t], (c + gridDim.x - begin) * kChunk + threadIdx.x,
+                                             g.nhalves[t], v);
         }
     }
 }
 
+// Quantize-pack: lane j stores the eight codes of half j (one dword of the
+// packed codes); the even lane of a block also stores its scale byte.
 __global__ __launch_bounds__(kThreads) void k_quantize_pack(const uint4* __restrict__ x,
-                                                            uint2* __restrict__ packed,
+                                                            uint32_t* __restrict__ packed,
                                                             uint8_t* __restrict__ scales,
                                                             float* __restrict__ gs_out,
-                                                            int64_t nblocks,
+                                                            int64_t nhalves,
                                                             const float* __restrict__ amax)
 {
     __shared__ uint4 table[128 * kEntryWords / 4];
@@ -681,16 +711,24 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack(const uint4* __restr
     const float gs = global_scale_of(*amax);
     if (blockIdx.x == 0 && threadIdx.x == 0)
         *gs_out = gs;
-    quantize_pass<NVFP4_QP_NT_LD != 0>(x, nblocks, [&] { build_table(gs, tab); },
-                                       [&](const uint32_t (&w)[8], int64_t b) {
-        pack_block<NVFP4_QP_NT_ST != 0>(w, tab, gs, packed, scales, b);
+    quantize_pass<NVFP4_QP_NT_LD != 0>(x, nhalves, [&] { build_table(gs, tab); },
+                                       [&](const uint32_t (&w)[4], int64_t j) {
+        const uint32_t sb = scale_byte_of(pair_max(w), gs);
+        store4<NVFP4_QP_NT_ST != 0>(packed + j, half_codes(w, tab + sb * kEntryWords));
+        if (!(j & 1))
+            scales[j >> 1] = (uint8_t)sb;
     });
 }
 
-__global__ __launch_bounds__(kThreads) void k_dequant_unpack(const uint2* __restrict__ packed,
+// Two lanes per block: lane j decodes the eight codes of dword j of the packed
+// codes (half j % 2 of block j / 2) with that block's scale byte and writes its
+// eight bf16 outputs, 16 bytes at j.  Every stream is then contiguous across a
+// wave (4-byte code loads, 16-byte stores), which writes the output ~20% faster
+// on MI355X than one lane per block storing 32 bytes at a 32-byte lane stride.
+__global__ __launch_bounds__(kThreads) void k_dequant_unpack(const uint32_t* __restrict__ packed,
                                                              const uint8_t* __restrict__ scales,
                                                              const float* __restrict__ gs_in,
-                                                             uint4* __restrict__ y, int64_t nblocks)
+                                                             uint4* __restrict__ y, int64_t nhalves)
 {
     __shared__ float sd_of[128];                   // decode(S) / gs for every scale byte
     const float gs = *gs_in;
@@ -702,28 +740,29 @@ __global__ __launch_bounds__(kThreads) void k_dequant_unpack(const uint2* __rest
     // while the current ones are decoded and stored
     const int64_t stride = (int64_t)gridDim.x * kThreads * kDqUnroll;
     int64_t base = (int64_t)blockIdx.x * kThreads * kDqUnroll + threadIdx.x;
-    uint2 p[kDqUnroll];
-    uint32_t s[kDqUnroll];
+    uint32_t p[kDqUnroll], s[kDqUnroll];
 #pragma unroll
     for (int u = 0; u < kDqUnroll; ++u) {
-        const int64_t b = base + (int64_t)u * kThreads;
-        p[u] = b < nblocks ? packed[b] : make_uint2(0u, 0u);
-        s[u] = b < nblocks ? scales[b] : 0u;
+        const int64_t j = base + (int64_t)u * kThreads;
+        p[u] = j < nhalves ? packed[j] : 0u;
+        s[u] = j < nhalves ? scales[j >> 1] : 0u;
     }
-    for (; base < nblocks; base += stride) {
-        uint2 pn[kDqUnroll];
-        uint32_t sn[kDqUnroll];
+    for (; base < nhalves; base += stride) {
+        uint32_t pn[kDqUnroll], sn[kDqUnroll];
 #pragma unroll
         for (int u = 0; u < kDqUnroll; ++u) {
-            const int64_t b = base + stride + (int64_t)u * kThreads;
-            pn[u] = b < nblocks ? packed[b] : make_uint2(0u, 0u);
-            sn[u] = b < nblocks ? scales[b] : 0u;
+            const int64_t j = base + stride + (int64_t)u * kThreads;
+            pn[u] = j < nhalves ? packed[j] : 0u;
+            sn[u] = j < nhalves ? scales[j >> 1] : 0u;
         }
 #pragma unroll
         for (int u = 0; u < kDqUnroll; ++u) {
-            const int64_t b = base + (int64_t)u * kThreads;
-            if (b < nblocks)
-                decode_store<NVFP4_DQ_NT_ST != 0>(p[u].x, p[u].y, sd_of[s[u] & 0x7Fu], y, b);
+            const int64_t j = base + (int64_t)u * kThreads;
+            if (j < nhalves) {
+                const float sd = sd_of[s[u] & 0x7Fu];
+                store16<NVFP4_DQ_NT_ST != 0>(y + j, make_uint4(decode_pair<0>(p[u], sd), decode_pair<1>(p[u], sd),
+                                                               decode_pair<2>(p[u], sd), decode_pair<3>(p[u], sd)));
+            }
         }
 #pragma unroll
         for (int u = 0; u < kDqUnroll; ++u) {
@@ -983,8 +1022,8 @@ nvfp4_status enqueue_fake_quant(const void* x, void* y, int64_t cols, const Matr
             static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), g, a);
         return launched();
     }
-    k_fake_quant<<<persistent_grid(m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
-        static_cast<const uint4*>(x), static_cast<uint4*>(y), m.nblocks, a);
+    k_fake_quant<<<persistent_grid(2 * m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
+        static_cast<const uint4*>(x), static_cast<uint4*>(y), 2 * m.nblocks, a);
     return launched();
 }
 
@@ -1000,8 +1039,8 @@ struct FakeQuantBatch {
         const int k = g.count;
         g.x[k] = static_cast<const uint4*>(x);
         g.y[k] = static_cast<uint4*>(y);
-        g.nblocks[k] = nblocks;
-        chunks += (nblocks + kChunk - 1) / kChunk;
+        g.nhalves[k] = 2 * nblocks;
+        chunks += (2 * nblocks + kChunk - 1) / kChunk;
         g.chunk_end[k] = chunks;
         return ++g.count == NVFP4_AMAX_GROUP_MAX ? flush(a, s) : NVFP4_OK;
     }
@@ -1198,8 +1237,8 @@ nvfp4_status nvfp4_fake_quant_dual(const void* x, int64_t rows, int64_t cols, co
         st = enqueue_fake_quant(x, y0, cols, m, amax0, s);
         return st != NVFP4_OK ? st : enqueue_fake_quant(x, y1, cols, m, amax1, s);
     }
-    k_fake_quant_dual<<<persistent_grid(m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
-        static_cast<const uint4*>(x), static_cast<uint4*>(y0), static_cast<uint4*>(y1), m.nblocks,
+    k_fake_quant_dual<<<persistent_grid(2 * m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
+        static_cast<const uint4*>(x), static_cast<uint4*>(y0), static_cast<uint4*>(y1), 2 * m.nblocks,
         amax0, amax1);
     return launched();
 }
@@ -1244,9 +1283,9 @@ nvfp4_status nvfp4_quantize_pack(const void* x, int64_t rows, int64_t cols,
             static_cast<const uint16_t*>(x), reinterpret_cast<uint2*>(packed), scales, global_scale, g, a);
         return launched();
     }
-    k_quantize_pack<<<persistent_grid(m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_QP_WG_PER_CU), kThreads, 0, s>>>(
-        static_cast<const uint4*>(x), reinterpret_cast<uint2*>(packed), scales, global_scale,
-        m.nblocks, a);
+    k_quantize_pack<<<persistent_grid(2 * m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_QP_WG_PER_CU), kThreads, 0, s>>>(
+        static_cast<const uint4*>(x), reinterpret_cast<uint32_t*>(packed), scales, global_scale,
+        2 * m.nblocks, a);
     return launched();
 }
 
@@ -1276,8 +1315,8 @@ nvfp4_status nvfp4_dequant_unpack(const uint8_t* packed, const uint8_t* scales,
             reinterpret_cast<const uint2*>(packed), scales, global_scale, static_cast<uint16_t*>(y), g);
         return launched();
     }
-    k_dequant_unpack<<<persistent_grid(m.nblocks, (int64_t)kThreads * kDqUnroll, NVFP4_DQ_WG_PER_CU), kThreads, 0, s>>>(
-        reinterpret_cast<const uint2*>(packed), scales, global_scale, static_cast<uint4*>(y), m.nblocks);
+    k_dequant_unpack<<<persistent_grid(2 * m.nblocks, (int64_t)kThreads * kDqUnroll, NVFP4_DQ_WG_PER_CU), kThreads, 0, s>>>(
+        reinterpret_cast<const uint32_t*>(packed), scales, global_scale, static_cast<uint4*>(y), 2 * m.nblocks);
     return launched();
 }
 
