@@ -183,3 +183,35 @@ def fake_quant(x: np.ndarray, amax_value: float | None = None) -> np.ndarray:
     if rc != 0:
         raise MemoryError("oracle fake_quant: allocation failed")
     return y
+
+
+# ---- the consumer: a linear layer over a packed weight ---------------------------
+
+def bf16_array_to_f64(h: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64 values (a bf16 is the upper half of a binary32)."""
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def linear(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, gs, k: int,
+           bias: np.ndarray | None = None) -> np.ndarray:
+    """y = x . dq(W)^T + b in float64: the VideoX-Fun page's per-forward reconstruction,
+    which dequantizes the packed weight to its bf16 form (dequantize above) and runs the
+    layer's linear on it.  x: bf16 bits [M, k]; packed, scales: as quantize() returns
+    them for W [N, k]; bias: bf16 bits [N] or None.  The product is a float64 library
+    matmul; a device result (binary32 sums, bf16 output) is compared with it under the
+    error bound that linear_magnitude() scales."""
+    w = bf16_array_to_f64(dequantize(packed, scales, gs, k))
+    y = bf16_array_to_f64(x) @ w.T
+    if bias is not None:
+        y = y + bf16_array_to_f64(bias)[None, :]
+    return y
+
+
+def linear_magnitude(x: np.ndarray, packed: np.ndarray, scales: np.ndarray, gs, k: int,
+                     bias: np.ndarray | None = None) -> np.ndarray:
+    """sum_k |x[m, k] w[n, k]| + |b[n]|, the scale of a rounding-error bound for y."""
+    w = np.abs(bf16_array_to_f64(dequantize(packed, scales, gs, k)))
+    s = np.abs(bf16_array_to_f64(x)) @ w.T
+    if bias is not None:
+        s = s + np.abs(bf16_array_to_f64(bias))[None, :]
+    return s

@@ -428,3 +428,56 @@ def test_block_scale_divides_by_six(golden):
         assert gs == gs2 and scales[0, 0] == s2[0, 0] and np.array_equal(packed, p2)
         wrong = torch_fp8_encode(np.float32([np.float32(bmax) * (np.float32(1) / np.float32(6)) * gs]))
         assert wrong[0] != scales[0, 0]
+
+
+# ---------------------------------------------------------------- linear over a packed weight
+
+def _packed_weight(n, k, seed):
+    rng = np.random.default_rng(seed)
+    w = synth.to_bf16_bits((rng.standard_normal((n, k)) * 0.05).astype(np.float32))
+    return oracle.quantize(w)
+
+
+def test_linear_one_hot_rows_read_back_the_weight_columns():
+    """x = identity: row i of y is column i of dq(W) plus the bias (no transpose, no offset)."""
+    n, k = 48, 64
+    packed, scales, gs = _packed_weight(n, k, 3)
+    bias = synth.to_bf16_bits(np.linspace(-1, 1, n).astype(np.float32))
+    eye = np.where(np.eye(k, dtype=bool), np.uint16(0x3F80), np.uint16(0))
+    w = oracle.bf16_array_to_f64(oracle.dequantize(packed, scales, gs, k))
+    y = oracle.linear(eye, packed, scales, gs, k, bias)
+    assert y.shape == (k, n)
+    assert np.array_equal(y, w.T + oracle.bf16_array_to_f64(bias)[None, :])
+    assert np.array_equal(oracle.linear(eye, packed, scales, gs, k), w.T)
+
+
+def test_linear_matches_brute_force_loops():
+    m, n, k = 3, 5, 32
+    packed, scales, gs = _packed_weight(n, k, 4)
+    rng = np.random.default_rng(5)
+    x = synth.to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    bias = synth.to_bf16_bits(rng.standard_normal(n).astype(np.float32))
+    wbits = oracle.dequantize(packed, scales, gs, k)
+    got = oracle.linear(x, packed, scales, gs, k, bias)
+    mag = oracle.linear_magnitude(x, packed, scales, gs, k, bias)
+    for i in range(m):
+        for j in range(n):
+            acc = oracle.bf16_to_f32(int(bias[j]))
+            s = abs(acc)
+            for t in range(k):
+                p = oracle.bf16_to_f32(int(x[i, t])) * oracle.bf16_to_f32(int(wbits[j, t]))
+                acc += p
+                s += abs(p)
+            assert abs(got[i, j] - acc) <= 1e-13 * s
+            assert abs(mag[i, j] - s) <= 1e-13 * s
+
+
+def test_linear_is_linear_in_x():
+    n, k = 16, 96
+    packed, scales, gs = _packed_weight(n, k, 6)
+    rng = np.random.default_rng(7)
+    x = synth.to_bf16_bits(rng.standard_normal((4, k)).astype(np.float32))
+    twice = (x.astype(np.uint32) + (1 << 7)).astype(np.uint16)      # exponent + 1: exactly 2x
+    assert np.array_equal(oracle.bf16_array_to_f64(twice), 2 * oracle.bf16_array_to_f64(x))
+    assert np.array_equal(oracle.linear(twice, packed, scales, gs, k),
+                          2 * oracle.linear(x, packed, scales, gs, k))
