@@ -173,6 +173,24 @@ def secondary(nv, synth, np, torch, dev, reps=20):
     out["c4_weight_fused_amax_quantize_pack_14336x4096"] = timed(
         lambda: nv.nvfp4_quantize_pack(w, amax_out=aw, packed=pk, scales=sc, global_scale=gsw),
         4.5625 * w.numel())
+    del w, yw, pk, sc
+
+    # the c5 weight used as a linear layer (packed once), against unpack + torch's bf16 GEMM
+    # and torch's bf16 GEMM on an already unpacked weight (the two on torch are context only)
+    wc = to_dev(synth.c5_weight())
+    n, k = wc.shape
+    packed, scales, gsc = nv.nvfp4_quantize_pack(wc)
+    wdq = nv.nvfp4_dequant_unpack(packed, scales, gsc)
+    del wc
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    for m in (1, 16, 64):
+        xm = torch.randn(m, k, generator=gen).to(torch.bfloat16).to(dev)
+        ym = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+        line = timed(lambda: nv.nvfp4_linear(xm, packed, scales, gsc, y=ym), n * k * 0.5625 + 2.0 * m * (k + n))
+        line["unpack_plus_torch_gemm_us"] = timed(
+            lambda: torch.nn.functional.linear(xm, nv.nvfp4_dequant_unpack(packed, scales, gsc, y=wdq)), 1.0)["us"]
+        line["torch_bf16_gemm_us"] = timed(lambda: torch.nn.functional.linear(xm, wdq), 1.0)["us"]
+        out["c5_weight_linear_%dx8192_by_28672x8192" % m] = line
     return out
 
 

@@ -16,8 +16,8 @@ import torch
 __all__ = [
     "NVFP4Error", "OBS_STATIC_MINMAX", "OBS_EMA", "lib", "library_path",
     "nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
-    "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_observer_update", "nvfp4_strerror",
-    "FakeQuantSTE", "blocks_per_row",
+    "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
+    "nvfp4_strerror", "FakeQuantSTE", "blocks_per_row",
 ]
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
@@ -26,7 +26,8 @@ OBS_STATIC_MINMAX = 0
 OBS_EMA = 1
 
 _EXPORTS = ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
-            "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_observer_update", "nvfp4_strerror")
+            "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
+            "nvfp4_strerror")
 
 
 class NVFP4Error(RuntimeError):
@@ -47,6 +48,7 @@ def _load() -> ctypes.CDLL:
     so.nvfp4_fake_quant_dual.argtypes = [P, I64, I64, P, P, P, P, P]
     so.nvfp4_quantize_pack.argtypes = [P, I64, I64, P, P, P, P, P, P]
     so.nvfp4_dequant_unpack.argtypes = [P, P, P, I64, I64, P, P]
+    so.nvfp4_linear.argtypes = [P, I64, I64, P, P, P, I64, P, P, P]
     so.nvfp4_observer_update.argtypes = [P, P, I, ctypes.c_float, P]
     so.nvfp4_strerror.argtypes = [I]
     so.nvfp4_strerror.restype = ctypes.c_char_p
@@ -222,6 +224,32 @@ def nvfp4_dequant_unpack(packed: torch.Tensor, scales: torch.Tensor, global_scal
     _matrix(y, "y")
     _check(lib.nvfp4_dequant_unpack(_ptr(packed), _ptr(scales), _ptr(global_scale), rows, cols,
                                     _ptr(y), _stream(packed.device)), "nvfp4_dequant_unpack")
+    return y
+
+
+def nvfp4_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                 global_scale: torch.Tensor, bias: torch.Tensor | None = None,
+                 y: torch.Tensor | None = None) -> torch.Tensor:
+    """x bf16 [M, K] times the packed weight [N, K] (transposed), plus bias -> bf16 [M, N].
+    packed / scales / global_scale as nvfp4_quantize_pack returns them; K % 32 == 0."""
+    m, k = _matrix(x, "x")
+    if packed.dtype != torch.uint8 or packed.dim() != 2 or not packed.is_cuda or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous 2-D uint8 CUDA tensor")
+    n = packed.shape[0]
+    if packed.shape[1] * 2 != k:
+        raise ValueError("packed holds %d codes per row, x has %d columns" % (packed.shape[1] * 2, k))
+    if tuple(scales.shape) != (n, k // 16) or scales.dtype != torch.uint8 or not scales.is_contiguous():
+        raise ValueError("scales must be contiguous uint8 [%d, %d]" % (n, k // 16))
+    _scalar(x.device, global_scale)
+    if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (n,) or
+                             not bias.is_contiguous() or not bias.is_cuda):
+        raise ValueError("bias must be a contiguous bfloat16 CUDA tensor of %d elements" % n)
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    if _matrix(y, "y") != (m, n):
+        raise ValueError("y must be [%d, %d]" % (m, n))
+    _check(lib.nvfp4_linear(_ptr(x), m, k, _ptr(packed), _ptr(scales), _ptr(global_scale), n, _ptr(bias),
+                            _ptr(y), _stream(x.device)), "nvfp4_linear")
     return y
 
 

@@ -72,6 +72,18 @@ namespace {
 #ifndef NVFP4_QP_WG_PER_CU
 #define NVFP4_QP_WG_PER_CU 64
 #endif
+#ifndef NVFP4_LIN_DEPTH
+#define NVFP4_LIN_DEPTH 2         // K steps of weight loads in flight per linear wave (even)
+#endif
+#ifndef NVFP4_LIN_KS
+#define NVFP4_LIN_KS 0            // K step of the linear kernel (128, 256); 0: by shape
+#endif
+#ifndef NVFP4_LIN_W
+#define NVFP4_LIN_W 4             // waves per linear workgroup (4 or 8)
+#endif
+#ifndef NVFP4_LIN_NT
+#define NVFP4_LIN_NT 0            // 16-row weight tiles per linear workgroup (1..8); 0: by shape
+#endif
 #ifndef NVFP4_DQ_WG_PER_CU
 #define NVFP4_DQ_WG_PER_CU 32
 #endif
@@ -886,6 +898,217 @@ __global__ __launch_bounds__(kThreads) void k_dequant_unpack_ragged(const uint2*
     }
 }
 
+// ---------------------------------------------------------------- linear over a packed weight
+//
+// y[m, n] = bf16( sum_k x[m, k] * w[n, k] + b[n] ), w = the bf16 weight that
+// dequant-unpack would write (VideoX-Fun page, the per-forward reconstruction:
+// the packed weight is dequantized to bf16 and the layer's linear runs on it).
+// Here the dequantization happens in registers, straight into the B operand of
+// bf16 MFMAs, so the bf16 weight never exists in memory: the weight costs 0.5625
+// bytes per element of HBM traffic instead of 2 (read) + 2 (write) + 2 (read).
+//
+// v_mfma_f32_16x16x32_bf16 operand layout (checked on MI355X): lane l holds
+// A[l % 16][8 (l / 16) .. + 8], B[8 (l / 16) .. + 8][l % 16], and accumulator
+// element i of lane l is D[4 (l / 16) + i][l % 16].  The sum over k may visit k
+// in any order, so in a KS-wide step lane group g = l / 16 takes the KS / 4
+// contiguous k from KS g / 4 for all KS / 32 MFMAs of the step (MFMA q uses the
+// q-th 8 of them), for A and B alike: per weight row, KS / 128 16-byte loads of
+// codes and one load of their KS / 64 scale bytes; per x row, KS / 32 16-byte
+// loads.
+//
+// A workgroup computes a tile of 16 MT rows of x by 16 NT rows of w; its W
+// waves split K (steps interleaved) and their partial sums meet in LDS, added in
+// wave order, so results do not depend on timing.  Rows past the end of x or w
+// read row 0 instead: accumulator element D[m][n] depends only on row m of x
+// and row n of w, and those rows are never stored, so every load stays
+// unconditional (no branch splits the load pipeline).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLinDepth = NVFP4_LIN_DEPTH;
+
+// Eight codes (one dword) -> the B operand: their bf16 values decode * sd, as
+// dequant-unpack writes them.
+__device__ __forceinline__ bf16x8 decode_operand(uint32_t c, float sd)
+{
+    return __builtin_bit_cast(bf16x8, decode_half(c, sd));
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int i)
+{
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+template <int MT, int NT, int W, int KS>
+__global__ __launch_bounds__(64 * W) void k_linear(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                     const uint32_t* __restrict__ packed,
+                                                     const uint8_t* __restrict__ scales,
+                                                     const float* __restrict__ gs_in, int64_t N,
+                                                     const uint16_t* __restrict__ bias,
+                                                     uint16_t* __restrict__ y)
+{
+    static_assert(KS == 128 || KS == 256, "step width");
+    constexpr int kQ = KS / 32;            // MFMAs per weight tile and step
+    constexpr int kCv = KS / 128;          // 16-byte code loads per row and step
+    __shared__ float sd_of[128];
+    __shared__ f32x4 partial[W - 1][MT * NT][64];
+    const float gs = *gs_in;
+    if (threadIdx.x < 128)
+        sd_of[threadIdx.x] = e4m3_decode(threadIdx.x) / gs;
+    __syncthreads();
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * NT, m0 = (int64_t)blockIdx.y * 16 * MT;
+    const int64_t cw = K / 8, sw = K / 16;           // code dwords and scale bytes per weight row
+    const bool scale_dword = KS == 256 && (sw & 3) == 0 && ((uintptr_t)scales & 3) == 0;
+
+    const uint32_t* wrow[NT];
+    const uint8_t* srow[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int64_t n = n0 + 16 * t + r;
+        wrow[t] = packed + (n < N ? n : 0) * cw;
+        srow[t] = scales + (n < N ? n : 0) * sw;
+    }
+    const uint16_t* xrow[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int64_t m = m0 + 16 * i + r;
+        xrow[i] = x + (m < M ? m : 0) * K;
+    }
+
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // The weight operands of a step (codes and scale bytes, the HBM stream) are
+    // loaded kLinDepth steps ahead; x (from L2) one step ahead.
+    struct WOp {
+        uint4 c[NT][kCv];
+        uint32_t sc[NT];                   // KS / 64 scale bytes, lowest first
+    };
+    struct XOp {
+        uint4 a[MT][kQ];
+    };
+    auto load_w = [&](int64_t st, WOp& o) {
+        const int64_t k0 = st * KS + (KS / 4) * g;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int v = 0; v < kCv; ++v)
+                o.c[t][v] = *reinterpret_cast<const uint4*>(wrow[t] + k0 / 8 + 4 * v);
+            const uint8_t* sp = srow[t] + k0 / 16;
+            if (KS == 128)
+                o.sc[t] = *reinterpret_cast<const uint16_t*>(sp);
+            else if (scale_dword)
+                o.sc[t] = *reinterpret_cast<const uint32_t*>(sp);
+            else
+                o.sc[t] = (uint32_t)*reinterpret_cast<const uint16_t*>(sp) |
+                          ((uint32_t)*reinterpret_cast<const uint16_t*>(sp + 2) << 16);
+        }
+    };
+    auto load_x = [&](int64_t st, XOp& o) {
+        const int64_t k0 = st * KS + (KS / 4) * g;
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int q = 0; q < kQ; ++q)
+                o.a[i][q] = *reinterpret_cast<const uint4*>(xrow[i] + k0 + 8 * q);
+    };
+    auto mma_step = [&](const WOp& o, const XOp& xo) {
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const float sd = sd_of[(o.sc[t] >> (8 * (q / 2))) & 0x7Fu];
+                const bf16x8 b = decode_operand(dword_of(o.c[t][q / 4], q % 4), sd);
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xo.a[i][q]), b,
+                                                                        acc[i][t], 0, 0, 0);
+            }
+        }
+    };
+    // A wave's j-th step uses ring[j % D] and xbuf[j % 2]; D is even, so both
+    // indices are compile-time constants in the unrolled body.
+    static_assert(kLinDepth % 2 == 0, "the x double buffer alternates with the ring");
+    const int64_t steps = K / KS;
+    WOp ring[kLinDepth];
+    XOp xbuf[2];
+#pragma unroll
+    for (int d = 0; d < kLinDepth; ++d)
+        if (wave + d * W < steps)
+            load_w(wave + d * W, ring[d]);
+    if (wave < steps)
+        load_x(wave, xbuf[0]);
+    for (int64_t st = wave; st < steps; st += kLinDepth * W) {
+#pragma unroll
+        for (int d = 0; d < kLinDepth; ++d) {
+            const int64_t at = st + d * W;
+            if (at < steps) {
+                if (at + W < steps)
+                    load_x(at + W, xbuf[(d + 1) % 2]);
+                mma_step(ring[d], xbuf[d % 2]);
+                if (at + kLinDepth * W < steps)
+                    load_w(at + kLinDepth * W, ring[d]);
+            }
+        }
+    }
+    // K % KS: 32-wide steps shared out over the waves, in the plain layout
+    // (lane group g takes k in [8 g, 8 g + 8) of the step)
+    for (int64_t kt = steps * KS + 32 * wave; kt < K; kt += 32 * W) {
+        const int64_t k0 = kt + 8 * g;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const bf16x8 b = decode_operand(wrow[t][k0 / 8], sd_of[srow[t][k0 / 16] & 0x7Fu]);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const uint4 a = *reinterpret_cast<const uint4*>(xrow[i] + k0);
+                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, acc[i][t],
+                                                                    0, 0, 0);
+            }
+        }
+    }
+
+    // waves 1..W-1 hand their partial sums to wave 0, which adds them in order
+    if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                partial[wave - 1][i * NT + t][lane] = acc[i][t];
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            f32x4 v = acc[i][t];
+#pragma unroll
+            for (int w = 0; w < W - 1; ++w)
+                v += partial[w][i * NT + t][lane];
+            const int64_t n = n0 + 16 * t + r;
+            if (n >= N)
+                continue;
+            const float b = bias ? bf16_value(bias[n]) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t m = m0 + 16 * i + 4 * g + e;
+                if (m < M) {
+                    const f32x2 o = {v[e] + b, 0.0f};
+                    y[m * N + n] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(o, bf16x2)) & 0xFFFFu);
+                }
+            }
+        }
+    }
+}
+
 __global__ void k_observer(float* state, const float* cur, int mode, float decay)
 {
     const float s = *state, c = *cur;
@@ -1054,6 +1277,70 @@ struct FakeQuantBatch {
         return launched();
     }
 };
+
+// One launch of the linear kernel with MT x NT MFMA tiles per workgroup, W
+// waves, KS-wide K steps.
+template <int MT, int NT, int W, int KS>
+nvfp4_status enqueue_linear(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                            const uint8_t* scales, const float* gs, int64_t n, const void* bias, void* y,
+                            hipStream_t s)
+{
+    const dim3 grid((unsigned)((n + 16 * NT - 1) / (16 * NT)), (unsigned)((m + 16 * MT - 1) / (16 * MT)));
+    k_linear<MT, NT, W, KS><<<grid, 64 * W, 0, s>>>(static_cast<const uint16_t*>(x), m, k,
+                                                   reinterpret_cast<const uint32_t*>(packed), scales, gs, n,
+                                                   static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y));
+    return launched();
+}
+
+// K step: 256 wide (fewer, wider loads) for one 16-row tile of x and at most
+// four weight tiles, else 128 wide (fewer registers).  Four waves split K;
+// more waves measured no faster on MI355X (8) or spill registers (16).
+template <int MT, int NT>
+nvfp4_status enqueue_linear_w(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                              const uint8_t* scales, const float* gs, int64_t n, const void* bias, void* y,
+                              hipStream_t s)
+{
+    constexpr int kKS = NVFP4_LIN_KS ? NVFP4_LIN_KS : (MT == 1 && NT <= 4 ? 256 : 128);
+    if constexpr (NVFP4_LIN_W == 8)
+        return enqueue_linear<MT, NT, 8, kKS>(x, m, k, packed, scales, gs, n, bias, y, s);
+    return enqueue_linear<MT, NT, 4, kKS>(x, m, k, packed, scales, gs, n, bias, y, s);
+}
+
+// Weight tiles per workgroup.  A weight of N rows is N / 16 tiles; when that is
+// 256 c for c <= 8 (N a multiple of 4096, as the widths of transformer layers
+// usually are), c tiles per workgroup give every CU of the 256 exactly one
+// workgroup, which measured best for 16 to 64 rows of x (and within 3% for one
+// row).  Otherwise: 4, 2 or 1 tiles, the largest that still makes 256
+// workgroups.
+template <int MT>
+nvfp4_status enqueue_linear_mt(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                               const uint8_t* scales, const float* gs, int64_t n, const void* bias, void* y,
+                               hipStream_t s)
+{
+#define NVFP4_LIN_ARGS x, m, k, packed, scales, gs, n, bias, y, s
+    if (NVFP4_LIN_NT > 0)
+        return enqueue_linear_w<MT, NVFP4_LIN_NT == 0 ? 1 : NVFP4_LIN_NT>(NVFP4_LIN_ARGS);
+    const int64_t gy = (m + 16 * MT - 1) / (16 * MT);
+    if (gy == 1 && n % 4096 == 0) {
+        switch (n / 4096) {
+        case 1: return enqueue_linear_w<MT, 1>(NVFP4_LIN_ARGS);
+        case 2: return enqueue_linear_w<MT, 2>(NVFP4_LIN_ARGS);
+        case 3: return enqueue_linear_w<MT, 3>(NVFP4_LIN_ARGS);
+        case 4: return enqueue_linear_w<MT, 4>(NVFP4_LIN_ARGS);
+        case 5: return enqueue_linear_w<MT, 5>(NVFP4_LIN_ARGS);
+        case 6: return enqueue_linear_w<MT, 6>(NVFP4_LIN_ARGS);
+        case 7: return enqueue_linear_w<MT, 7>(NVFP4_LIN_ARGS);
+        case 8: return enqueue_linear_w<MT, 8>(NVFP4_LIN_ARGS);
+        default: break;
+        }
+    }
+    if (((n + 63) / 64) * gy >= 256)
+        return enqueue_linear_w<MT, 4>(NVFP4_LIN_ARGS);
+    if (((n + 31) / 32) * gy >= 256)
+        return enqueue_linear_w<MT, 2>(NVFP4_LIN_ARGS);
+    return enqueue_linear_w<MT, 1>(NVFP4_LIN_ARGS);
+#undef NVFP4_LIN_ARGS
+}
 
 }  // namespace
 
@@ -1335,6 +1622,36 @@ nvfp4_status nvfp4_observer_update(float* state, const float* cur, int mode, flo
     (void)hipGetLastError();
     k_observer<<<1, 1, 0, s>>>(state, cur, mode, decay);
     return launched();
+}
+
+nvfp4_status nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                          const uint8_t* scales, const float* global_scale, int64_t n, const void* bias,
+                          void* y, void* stream)
+{
+    if (m < 0 || n < 0 || k < 32 || k % 32 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (k > ((int64_t)1 << 40) || m > ((int64_t)1 << 40) / k || n > ((int64_t)1 << 40) / k ||
+        (m > 0 && n > ((int64_t)1 << 50) / m) || (m + 63) / 64 > 65535)
+        return NVFP4_ERR_SHAPE;
+    if (!packed || !scales || !global_scale || (m > 0 && (!x || !y)))
+        return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(global_scale, 4) ||
+        !aligned(bias, 2) || !aligned(y, 2))
+        return NVFP4_ERR_ALIGN;
+    const uint64_t yb = 2 * (uint64_t)(m * n);
+    if (overlap(y, yb, x, 2 * (uint64_t)(m * k)) || overlap(y, yb, packed, (uint64_t)(n * k / 2)) ||
+        overlap(y, yb, scales, (uint64_t)(n * k / 16)) || overlap(y, yb, global_scale, 4) ||
+        overlap(y, yb, bias, bias ? 2 * (uint64_t)n : 0))
+        return NVFP4_ERR_OVERLAP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (m == 0 || n == 0)
+        return NVFP4_OK;
+    if (m <= 16)
+        return enqueue_linear_mt<1>(x, m, k, packed, scales, global_scale, n, bias, y, s);
+    if (m <= 32)
+        return enqueue_linear_mt<2>(x, m, k, packed, scales, global_scale, n, bias, y, s);
+    return enqueue_linear_mt<4>(x, m, k, packed, scales, global_scale, n, bias, y, s);
 }
 
 }  // extern "C"

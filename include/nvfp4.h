@@ -182,6 +182,30 @@ nvfp4_status nvfp4_dequant_unpack(const uint8_t* packed, const uint8_t* scales,
                                   void* y, void* stream);
 
 /*
+ * nvfp4_linear -- y = x . w^T + b for a weight w stored as packed NVFP4: the
+ * layer's linear run on the dequantized weight (VideoX-Fun page, the
+ * per-forward reconstruction, where the packed weight is dequantized to bf16
+ * before the module's own forward).  w is exactly the bf16 tensor that
+ * nvfp4_dequant_unpack writes, but it is decoded in registers and never stored.
+ * Products and sums are binary32 (the weight and x are bf16, so every product is
+ * exact); the order of the sums is fixed by the kernel and does not change from
+ * run to run; y is rounded to bf16 (nearest even) once, after the bias is added.
+ *
+ *   x             device bf16 [m, k], 16-byte aligned
+ *   packed        device uint8 [n, k / 2], the codes of w as nvfp4_quantize_pack
+ *                 writes them, 16-byte aligned
+ *   scales        device uint8 [n, k / 16], E4M3 block scales, 2-byte aligned
+ *   global_scale  device fp32 gs of w
+ *   bias          device bf16 [n], 2-byte aligned, or NULL for none
+ *   y             device bf16 [m, n], 2-byte aligned; must not overlap an input
+ *   m >= 0, n >= 0; k >= 32 and k % 32 == 0 (other widths: unpack, then a GEMM)
+ * Errors: SHAPE, NULL, ALIGN, OVERLAP, HIP.
+ */
+nvfp4_status nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                          const uint8_t* scales, const float* global_scale, int64_t n, const void* bias,
+                          void* y, void* stream);
+
+/*
  * nvfp4_observer_update -- one activation-observer step on device scalars
  * (verl QATLinear page, section 5):
  *   NVFP4_OBS_STATIC_MINMAX:  *state := max(*state, *cur)

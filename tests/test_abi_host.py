@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_every_call():
     names = declared_functions()
     for n in ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
-              "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_observer_update", "nvfp4_strerror"):
+              "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
+              "nvfp4_strerror"):
         assert n in names
 
 
@@ -144,6 +145,30 @@ def test_dequant_unpack_validation():
     assert d(P(p), P(s), P(g), 4, 16, P(y + 8), None) == ERR_ALIGN
     assert d(P(p), P(s), P(g), 4, 16, P(p), None) == ERR_OVERLAP
     assert d(P(p), P(s), P(g), 4, 16, P(g - 16), None) == ERR_OVERLAP
+
+
+def test_linear_validation():
+    li = nv.lib.nvfp4_linear
+    G = 1 << 30
+    x, p, sc, g, b, y = A, A + G, A + 2 * G, A + 3 * G, A + 3 * G + 256, A + 4 * G
+    assert li(P(x), 4, 48, P(p), P(sc), P(g), 8, None, P(y), None) == ERR_SHAPE      # k % 32
+    assert li(P(x), 4, 16, P(p), P(sc), P(g), 8, None, P(y), None) == ERR_SHAPE      # k < 32
+    assert li(P(x), -1, 64, P(p), P(sc), P(g), 8, None, P(y), None) == ERR_SHAPE
+    assert li(P(x), 4, 64, P(p), P(sc), P(g), -8, None, P(y), None) == ERR_SHAPE
+    assert li(P(x), 64 * 65536, 64, P(p), P(sc), P(g), 8, None, P(y), None) == ERR_SHAPE  # grid rows
+    assert li(None, 4, 64, P(p), P(sc), P(g), 8, None, P(y), None) == ERR_NULL
+    assert li(P(x), 4, 64, None, P(sc), P(g), 8, None, P(y), None) == ERR_NULL
+    assert li(P(x), 4, 64, P(p), None, P(g), 8, None, P(y), None) == ERR_NULL
+    assert li(P(x), 4, 64, P(p), P(sc), None, 8, None, P(y), None) == ERR_NULL
+    assert li(P(x), 4, 64, P(p), P(sc), P(g), 8, None, None, None) == ERR_NULL
+    assert li(P(x + 8), 4, 64, P(p), P(sc), P(g), 8, None, P(y), None) == ERR_ALIGN
+    assert li(P(x), 4, 64, P(p + 8), P(sc), P(g), 8, None, P(y), None) == ERR_ALIGN
+    assert li(P(x), 4, 64, P(p), P(sc + 1), P(g), 8, None, P(y), None) == ERR_ALIGN
+    assert li(P(x), 4, 64, P(p), P(sc), P(g), 8, P(b + 1), P(y), None) == ERR_ALIGN
+    assert li(P(x), 4, 64, P(p), P(sc), P(g), 8, None, P(y + 1), None) == ERR_ALIGN
+    assert li(P(x), 4, 64, P(p), P(sc), P(g), 8, None, P(x + 64), None) == ERR_OVERLAP
+    assert li(P(x), 4, 64, P(p), P(sc), P(g), 8, None, P(p + 32), None) == ERR_OVERLAP
+    assert li(P(x), 4, 64, P(p), P(sc), P(g), 8, P(b), P(b - 2), None) == ERR_OVERLAP
 
 
 def test_amax_validation():

@@ -1,0 +1,118 @@
+"""GPU parity of nvfp4_linear, the linear layer over a packed NVFP4 weight (VideoX-Fun
+page, the per-forward reconstruction: dequantize the packed weight to bf16, then the
+layer's linear).
+
+Expected values come from the oracle: its dequantize() gives the bf16 weight and a
+float64 matmul gives y.  The device sums binary32 products of bf16 values (exact) in an
+order of its own and rounds y to bf16 once, so
+
+    |y_dev - y| <= 2^-9 |y| (final rounding) + (1 + 2^-9) * gamma * S,
+    gamma = (k + 4) * 2^-24 * 1.01,  S = sum_k |x w| + |b|,
+
+(k products and at most 4 more additions, the standard bound for any summation order).
+The test uses 2^-8 |y| + 2 (k + 8) 2^-24 S + 2^-133, which is looser than that bound, and
+also holds in the bf16 subnormal range.  One case is exact: one-hot rows of x with no bias
+give y = w^T exactly (as values: -0 weights come out +0), which checks every decoded
+weight element through the product.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU visible", allow_module_level=True)
+
+import fp4_block_fake_amd as nv  # noqa: E402
+from gpu_util import DEV, assert_same, dev, host, say  # noqa: E402
+
+
+def weight(n, k, seed, sigma=0.02):
+    rng = np.random.default_rng(seed)
+    w = synth.to_bf16_bits((rng.standard_normal((n, k)) * sigma).astype(np.float32))
+    return oracle.quantize(w)
+
+
+def to_dev_packed(packed, scales, gs):
+    return (torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV),
+            torch.tensor([gs], dtype=torch.float32, device=DEV))
+
+
+def check_bound(y_dev_bits, x, packed, scales, gs, k, bias, what):
+    y = oracle.linear(x, packed, scales, gs, k, bias)
+    s = oracle.linear_magnitude(x, packed, scales, gs, k, bias)
+    got = oracle.bf16_array_to_f64(y_dev_bits)
+    tol = 2.0 ** -8 * np.abs(y) + 2 * (k + 8) * 2.0 ** -24 * s + 2.0 ** -133
+    err = np.abs(got - y)
+    bad = np.flatnonzero(err > tol)
+    assert bad.size == 0, "%s: %d outside the bound, first %s: got %r want %r (tol %r)" % (
+        what, bad.size, np.unravel_index(bad[0], y.shape), got.flat[bad[0]], y.flat[bad[0]], tol.flat[bad[0]])
+    return float((err / np.maximum(tol, 1e-300)).max())
+
+
+@pytest.mark.parametrize("n,k", [(40, 256), (100, 96), (16, 32), (33, 160)])
+def test_one_hot_rows_give_the_weight_exactly(n, k):
+    packed, scales, gs = weight(n, k, n + k)
+    eye = np.where(np.eye(k, dtype=bool), np.uint16(0x3F80), np.uint16(0))
+    say("linear one-hot n=%d k=%d" % (n, k))
+    y = nv.nvfp4_linear(dev(eye), *to_dev_packed(packed, scales, gs))
+    torch.cuda.synchronize()
+    # values, not bit patterns: a code-8 weight is -0, and a sum that starts at +0 gives +0
+    got = oracle.bf16_array_to_f64(host(y))
+    want = oracle.bf16_array_to_f64(oracle.dequantize(packed, scales, gs, k).T)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, "one-hot rows: %d mismatches, first at %d: got %r want %r" % (
+        bad.size, bad[0], got.flat[bad[0]], want.flat[bad[0]])
+    assert (got != 0).sum() > got.size // 2
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 64, 128), (16, 48, 256), (17, 40, 4096), (64, 96, 352),
+                                   (100, 130, 512), (3, 2048, 8192), (200, 64, 160), (65, 1, 32)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_linear_within_the_rounding_bound(m, n, k, with_bias):
+    packed, scales, gs = weight(n, k, 7 * m + n + k)
+    rng = np.random.default_rng(m + 3 * n + 5 * k)
+    x = synth.to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    bias = synth.to_bf16_bits(rng.standard_normal(n).astype(np.float32)) if with_bias else None
+    say("linear m=%d n=%d k=%d bias=%s" % (m, n, k, with_bias))
+    yt = nv.nvfp4_linear(dev(x), *to_dev_packed(packed, scales, gs),
+                         bias=None if bias is None else dev(bias))
+    torch.cuda.synchronize()
+    check_bound(host(yt), x, packed, scales, gs, k, bias, "m=%d n=%d k=%d" % (m, n, k))
+    # deterministic: a second call gives the same bits
+    y2 = nv.nvfp4_linear(dev(x), *to_dev_packed(packed, scales, gs),
+                         bias=None if bias is None else dev(bias))
+    torch.cuda.synchronize()
+    assert torch.equal(yt.view(torch.int16), y2.view(torch.int16))
+
+
+def test_c5_weight_as_a_layer():
+    """The c5 weight (28672 x 8192) quantized on the device, then used as a linear layer
+    on 16 tokens; sampled output columns are checked against the oracle."""
+    w = synth.c5_weight()
+    say("linear on the c5 weight")
+    packed, scales, gs = nv.nvfp4_quantize_pack(dev(w))
+    rng = np.random.default_rng(55)
+    x = synth.to_bf16_bits(rng.standard_normal((16, w.shape[1])).astype(np.float32))
+    y = nv.nvfp4_linear(dev(x), packed, scales, gs)
+    torch.cuda.synchronize()
+    cols = np.unique(np.concatenate([[0, w.shape[0] - 1], rng.choice(w.shape[0], 62, replace=False)]))
+    p_rows, s_rows = packed.cpu().numpy()[cols], scales.cpu().numpy()[cols]
+    g = float(gs.item())
+    p_ref, s_ref, g_ref = oracle.quantize(w[cols], oracle.amax(w))
+    assert_same(p_rows, p_ref, "c5 packed rows")
+    assert_same(s_rows, s_ref, "c5 scale rows")
+    check_bound(host(y)[:, cols], x, p_rows, s_rows, g, w.shape[1], None, "c5 sampled columns")
+
+
+def test_empty_and_rejected_shapes():
+    packed, scales, gs = to_dev_packed(*weight(8, 64, 1))
+    y = nv.nvfp4_linear(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV), packed, scales, gs)
+    assert y.shape == (0, 8)
+    with pytest.raises(nv.NVFP4Error):
+        p2, s2, g2 = to_dev_packed(*weight(8, 48, 2))
+        nv.nvfp4_linear(torch.zeros((4, 48), dtype=torch.bfloat16, device=DEV), p2, s2, g2)
