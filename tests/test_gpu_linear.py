@@ -90,6 +90,22 @@ def test_linear_within_the_rounding_bound(m, n, k, with_bias):
     assert torch.equal(yt.view(torch.int16), y2.view(torch.int16))
 
 
+# Launch shapes the tile choice reaches: 256-wide steps whose scale bytes are not 4-byte
+# aligned (k % 64 == 32, up to 16 rows of x), one workgroup per CU for widths n = 4096 c
+# (c tiles of 16 weight rows per workgroup, c = 1, 3, 5, 8), and several 16-row tiles of x.
+@pytest.mark.parametrize("m,n,k", [(5, 40, 288), (16, 130, 800), (4, 12288, 256), (2, 20480, 128),
+                                   (64, 32768, 64), (33, 4096, 96), (48, 8192, 160)])
+def test_linear_launch_shapes(m, n, k):
+    packed, scales, gs = weight(n, k, 11 * m + n + k)
+    rng = np.random.default_rng(m * 5 + n + k)
+    x = synth.to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    bias = synth.to_bf16_bits(rng.standard_normal(n).astype(np.float32))
+    say("linear launch shape m=%d n=%d k=%d" % (m, n, k))
+    yt = nv.nvfp4_linear(dev(x), *to_dev_packed(packed, scales, gs), bias=dev(bias))
+    torch.cuda.synchronize()
+    check_bound(host(yt), x, packed, scales, gs, k, bias, "m=%d n=%d k=%d" % (m, n, k))
+
+
 def test_c5_weight_as_a_layer():
     """The c5 weight (28672 x 8192) quantized on the device, then used as a linear layer
     on 16 tokens; sampled output columns are checked against the oracle."""
