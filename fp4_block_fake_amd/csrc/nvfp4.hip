@@ -75,11 +75,14 @@ namespace {
 #ifndef NVFP4_LIN_DEPTH
 #define NVFP4_LIN_DEPTH 2         // K steps of weight loads in flight per linear wave (even)
 #endif
+#ifndef NVFP4_LIN_SCALES_LDS
+#define NVFP4_LIN_SCALES_LDS 1    // stage the linear workgroup's scale rows in LDS when they fit
+#endif
 #ifndef NVFP4_LIN_KS
 #define NVFP4_LIN_KS 0            // K step of the linear kernel (128, 256); 0: by shape
 #endif
 #ifndef NVFP4_LIN_W
-#define NVFP4_LIN_W 4             // waves per linear workgroup (4 or 8)
+#define NVFP4_LIN_W 0             // waves per linear workgroup (4 or 8); 0: by shape
 #endif
 #ifndef NVFP4_LIN_NT
 #define NVFP4_LIN_NT 0            // 16-row weight tiles per linear workgroup (1..8); 0: by shape
@@ -926,6 +929,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLinDepth = NVFP4_LIN_DEPTH;
+constexpr size_t kLinLdsBudget = 64 * 1024 - 128 * sizeof(float);   // beside the sd table
 
 // Eight codes (one dword) -> the B operand: their bf16 values decode * sd, as
 // dequant-unpack writes them.
@@ -939,7 +943,11 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& v, int i)
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-template <int MT, int NT, int W, int KS>
+// Dynamic LDS of the linear kernel: with SL, the scale rows of the workgroup's
+// weight tiles during the K loop; then the partial sums of waves 1..W-1.
+extern __shared__ __align__(16) uint8_t lin_lds[];
+
+template <int MT, int NT, int W, int KS, bool SL>
 __global__ __launch_bounds__(64 * W) void k_linear(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                      const uint32_t* __restrict__ packed,
                                                      const uint8_t* __restrict__ scales,
@@ -951,26 +959,67 @@ __global__ __launch_bounds__(64 * W) void k_linear(const uint16_t* __restrict__ 
     constexpr int kQ = KS / 32;            // MFMAs per weight tile and step
     constexpr int kCv = KS / 128;          // 16-byte code loads per row and step
     __shared__ float sd_of[128];
-    __shared__ f32x4 partial[W - 1][MT * NT][64];
+    f32x4 (*partial)[MT * NT][64] = reinterpret_cast<f32x4 (*)[MT * NT][64]>(lin_lds);
     const float gs = *gs_in;
     if (threadIdx.x < 128)
         sd_of[threadIdx.x] = e4m3_decode(threadIdx.x) / gs;
-    __syncthreads();
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * NT, m0 = (int64_t)blockIdx.y * 16 * MT;
     const int64_t cw = K / 8, sw = K / 16;           // code dwords and scale bytes per weight row
-    const bool scale_dword = KS == 256 && (sw & 3) == 0 && ((uintptr_t)scales & 3) == 0;
+    const bool scale_dword = KS == 256 && (sw & 3) == 0 && (SL || ((uintptr_t)scales & 3) == 0);
+    if (SL) {
+        // The workgroup's scale rows are contiguous: one coalesced copy into LDS
+        // (16-byte pieces when aligned, 2-byte otherwise; every row is an even
+        // number of bytes).
+        const int64_t rows = N - n0 < 16 * NT ? N - n0 : 16 * NT;
+        const uint8_t* src = scales + n0 * sw;
+        const int64_t bytes = rows * sw;
+        if (((uintptr_t)src & 15) == 0) {
+            for (int64_t i = threadIdx.x; i < bytes / 16; i += 64 * W)
+                reinterpret_cast<uint4*>(lin_lds)[i] = reinterpret_cast<const uint4*>(src)[i];
+            for (int64_t i = bytes / 16 * 16 + 2 * threadIdx.x; i < bytes; i += 2 * 64 * W)
+                *reinterpret_cast<uint16_t*>(lin_lds + i) = *reinterpret_cast<const uint16_t*>(src + i);
+        } else {
+            for (int64_t i = 2 * threadIdx.x; i < bytes; i += 2 * 64 * W)
+                *reinterpret_cast<uint16_t*>(lin_lds + i) = *reinterpret_cast<const uint16_t*>(src + i);
+        }
+    }
+    __syncthreads();
 
     const uint32_t* wrow[NT];
-    const uint8_t* srow[NT];
+    const uint8_t* srow[NT];               // without SL: the scale row in HBM
+    uint32_t soff[NT];                     // with SL: the scale row's offset in LDS
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int64_t n = n0 + 16 * t + r;
         wrow[t] = packed + (n < N ? n : 0) * cw;
         srow[t] = scales + (n < N ? n : 0) * sw;
+        soff[t] = (uint32_t)((n < N ? 16 * t + r : 0) * sw);
     }
+    // scale bytes [k / 16, k / 16 + bytes) of weight tile t (bytes = 1, 2 or 4)
+    auto scale_bytes = [&](int t, int64_t k, int bytes) -> uint32_t {
+        if (SL) {
+            const uint8_t* sp = lin_lds + soff[t] + k / 16;
+            if (bytes == 1)
+                return *sp;
+            if (bytes == 2 || !scale_dword)
+                return bytes == 2 ? *reinterpret_cast<const uint16_t*>(sp)
+                                  : (uint32_t)*reinterpret_cast<const uint16_t*>(sp) |
+                                    ((uint32_t)*reinterpret_cast<const uint16_t*>(sp + 2) << 16);
+            return *reinterpret_cast<const uint32_t*>(sp);
+        }
+        const uint8_t* sp = srow[t] + k / 16;
+        if (bytes == 1)
+            return *sp;
+        if (bytes == 2)
+            return *reinterpret_cast<const uint16_t*>(sp);
+        if (scale_dword)
+            return *reinterpret_cast<const uint32_t*>(sp);
+        return (uint32_t)*reinterpret_cast<const uint16_t*>(sp) |
+               ((uint32_t)*reinterpret_cast<const uint16_t*>(sp + 2) << 16);
+    };
     const uint16_t* xrow[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
@@ -1001,14 +1050,7 @@ __global__ __launch_bounds__(64 * W) void k_linear(const uint16_t* __restrict__ 
 #pragma unroll
             for (int v = 0; v < kCv; ++v)
                 o.c[t][v] = *reinterpret_cast<const uint4*>(wrow[t] + k0 / 8 + 4 * v);
-            const uint8_t* sp = srow[t] + k0 / 16;
-            if (KS == 128)
-                o.sc[t] = *reinterpret_cast<const uint16_t*>(sp);
-            else if (scale_dword)
-                o.sc[t] = *reinterpret_cast<const uint32_t*>(sp);
-            else
-                o.sc[t] = (uint32_t)*reinterpret_cast<const uint16_t*>(sp) |
-                          ((uint32_t)*reinterpret_cast<const uint16_t*>(sp + 2) << 16);
+            o.sc[t] = scale_bytes(t, k0, KS / 64);
         }
     };
     auto load_x = [&](int64_t st, XOp& o) {
@@ -1064,7 +1106,7 @@ __global__ __launch_bounds__(64 * W) void k_linear(const uint16_t* __restrict__ 
         const int64_t k0 = kt + 8 * g;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const bf16x8 b = decode_operand(wrow[t][k0 / 8], sd_of[srow[t][k0 / 16] & 0x7Fu]);
+            const bf16x8 b = decode_operand(wrow[t][k0 / 8], sd_of[scale_bytes(t, k0, 1) & 0x7Fu]);
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
                 const uint4 a = *reinterpret_cast<const uint4*>(xrow[i] + k0);
@@ -1075,6 +1117,9 @@ __global__ __launch_bounds__(64 * W) void k_linear(const uint16_t* __restrict__ 
     }
 
     // waves 1..W-1 hand their partial sums to wave 0, which adds them in order
+    // (through the LDS the scales used, once every wave is past the K loop)
+    if (SL)
+        __syncthreads();
     if (wave > 0) {
 #pragma unroll
         for (int i = 0; i < MT; ++i)
@@ -1286,24 +1331,35 @@ nvfp4_status enqueue_linear(const void* x, int64_t m, int64_t k, const uint8_t* 
                             hipStream_t s)
 {
     const dim3 grid((unsigned)((n + 16 * NT - 1) / (16 * NT)), (unsigned)((m + 16 * MT - 1) / (16 * MT)));
-    k_linear<MT, NT, W, KS><<<grid, 64 * W, 0, s>>>(static_cast<const uint16_t*>(x), m, k,
-                                                   reinterpret_cast<const uint32_t*>(packed), scales, gs, n,
-                                                   static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y));
+    const size_t partial_bytes = (size_t)(W - 1) * MT * NT * 64 * sizeof(f32x4);
+    const size_t scale_bytes = (size_t)16 * NT * (k / 16);
+    // the scale rows go to LDS when they fit in the 64 KB a workgroup may always use
+    if (NVFP4_LIN_SCALES_LDS && scale_bytes <= kLinLdsBudget) {
+        const size_t lds = scale_bytes > partial_bytes ? scale_bytes : partial_bytes;
+        k_linear<MT, NT, W, KS, true><<<grid, 64 * W, lds, s>>>(
+            static_cast<const uint16_t*>(x), m, k, reinterpret_cast<const uint32_t*>(packed), scales, gs, n,
+            static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y));
+    } else {
+        k_linear<MT, NT, W, KS, false><<<grid, 64 * W, partial_bytes, s>>>(
+            static_cast<const uint16_t*>(x), m, k, reinterpret_cast<const uint32_t*>(packed), scales, gs, n,
+            static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y));
+    }
     return launched();
 }
 
 // K step: 256 wide (fewer, wider loads) for one 16-row tile of x and at most
-// four weight tiles, else 128 wide (fewer registers).  Four waves split K;
-// more waves measured no faster on MI355X (8) or spill registers (16).
+// four weight tiles, else 128 wide (fewer registers).  The waves split K: 8 for
+// one 16-row tile of x (more loads in flight per CU; 33 vs 38 us for one row of
+// x on the c5 weight), else 4 (the partial sums of 8 waves of several x tiles do
+// not fit in LDS, and 16 waves spill registers).
 template <int MT, int NT>
 nvfp4_status enqueue_linear_w(const void* x, int64_t m, int64_t k, const uint8_t* packed,
                               const uint8_t* scales, const float* gs, int64_t n, const void* bias, void* y,
                               hipStream_t s)
 {
     constexpr int kKS = NVFP4_LIN_KS ? NVFP4_LIN_KS : (MT == 1 && NT <= 4 ? 256 : 128);
-    if constexpr (NVFP4_LIN_W == 8)
-        return enqueue_linear<MT, NT, 8, kKS>(x, m, k, packed, scales, gs, n, bias, y, s);
-    return enqueue_linear<MT, NT, 4, kKS>(x, m, k, packed, scales, gs, n, bias, y, s);
+    constexpr int kW = NVFP4_LIN_W ? NVFP4_LIN_W : (MT == 1 ? 8 : 4);
+    return enqueue_linear<MT, NT, kW, kKS>(x, m, k, packed, scales, gs, n, bias, y, s);
 }
 
 // Weight tiles per workgroup.  A weight of N rows is N / 16 tiles; when that is
