@@ -1,0 +1,90 @@
+"""The library's calls under HIP graph capture.
+
+Every call only enqueues kernels on the caller's stream (no allocation, no memset, no
+host synchronisation), so a caller may capture a sequence of them in a graph and replay
+it.  Each replay here runs after eager work that overwrites every output and amax, and
+must reproduce the eager results bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU visible", allow_module_level=True)
+
+import fp4_block_fake_amd as nv  # noqa: E402
+from gpu_util import DEV, assert_same, dev, fbits, host, say, scalar  # noqa: E402
+
+
+def test_captured_sequence_replays_exactly():
+    rng = np.random.default_rng(61)
+    x = synth.to_bf16_bits((rng.standard_normal((512, 1024)) * 0.05).astype(np.float32))
+    sibs = [synth.to_bf16_bits((rng.standard_normal((r, 256)) * s).astype(np.float32))
+            for r, s in ((256, 0.02), (64, 0.03), (64, 0.01))]
+    xt, st = dev(x), [dev(s) for s in sibs]
+    y = torch.empty_like(xt)
+    ys = [torch.empty_like(t) for t in st]
+    packed = torch.empty((512, 512), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((512, 64), dtype=torch.uint8, device=DEV)
+    a_fq, a_qp, a_grp, gs = scalar(0.0), scalar(0.0), scalar(0.0), scalar(0.0)
+    yd = torch.empty_like(xt)
+    state = scalar(-1.0)
+    xl = dev(synth.to_bf16_bits(rng.standard_normal((8, 1024)).astype(np.float32)))
+    yl = torch.empty((8, 512), dtype=torch.bfloat16, device=DEV)
+
+    def sequence():
+        nv.nvfp4_fake_quant(xt, y=y, amax_out=a_fq)
+        nv.nvfp4_quantize_pack(xt, amax_out=a_qp, packed=packed, scales=scales, global_scale=gs)
+        nv.nvfp4_dequant_unpack(packed, scales, gs, y=yd)
+        nv.nvfp4_fake_quant_group(st, ys=ys, amax_out=a_grp)
+        nv.nvfp4_observer_update(state, a_fq, nv.OBS_EMA, 0.25)
+        nv.nvfp4_linear(xl, packed[:, :], scales, gs, y=yl)
+
+    # warm up on a side stream, then capture
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sequence()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sequence()
+    torch.cuda.synchronize()
+
+    a = oracle.amax(x)
+    y_ref = oracle.fake_quant(x, a)
+    p_ref, s_ref, g_ref = oracle.quantize(x, a)
+    a_group = oracle.amax_group(sibs)
+    for replay in range(4):
+        # eager work between replays overwrites everything the graph writes
+        for t in (y, yd, yl, *ys):
+            t.fill_(float(replay + 1))
+        packed.fill_(0xFF)
+        scales.fill_(0x7F)
+        for s in (a_fq, a_qp, a_grp, gs):
+            s.fill_(-5.0)
+        state.fill_(-1.0)
+        torch.cuda.synchronize()
+        say("graph replay %d" % replay)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert fbits(a_fq.item()) == fbits(a) and fbits(a_qp.item()) == fbits(a)
+        assert fbits(gs.item()) == fbits(g_ref)
+        assert fbits(state.item()) == fbits(oracle.observer(-1.0, a, oracle.OBS_EMA, 0.25))
+        assert_same(host(y), y_ref, "replayed fake-quant")
+        assert_same(packed.cpu().numpy(), p_ref, "replayed codes")
+        assert_same(scales.cpu().numpy(), s_ref, "replayed scales")
+        assert_same(host(yd), y_ref, "replayed unpack")
+        assert fbits(a_grp.item()) == fbits(a_group)
+        for i, (s, t) in enumerate(zip(sibs, ys)):
+            assert_same(host(t), oracle.fake_quant(s, a_group), "replayed sibling %d" % i)
+        y_lin = oracle.linear(host(xl), p_ref, s_ref, g_ref, 1024)
+        got = oracle.bf16_array_to_f64(host(yl))
+        mag = oracle.linear_magnitude(host(xl), p_ref, s_ref, g_ref, 1024)
+        assert np.all(np.abs(got - y_lin) <= 2.0 ** -8 * np.abs(y_lin) + 2 * 1032 * 2.0 ** -24 * mag + 2.0 ** -133)
