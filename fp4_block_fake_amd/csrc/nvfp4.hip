@@ -8,23 +8,26 @@
 //
 // Design
 // ------
-// * Every kernel streams HBM: 2-6 bytes per element, a few dozen integer ops.
-//   There is no contraction, so no MFMA; the limits are HBM bandwidth and the
-//   VALU issue rate (about 20 lane-ops per element at 8 TB/s for fake-quant).
-// * One lane owns one 16-element block (two 16-byte loads).  The block max is
-//   taken from the lane's own registers with packed 16-bit max on the
-//   magnitude fields; no cross-lane traffic is needed per block.
-// * The per-element IEEE divide x / sq is replaced by integer compares that
-//   give bit-identical codes (see "Decision thresholds" below).  Everything
-//   that depends only on the E4M3 scale byte S (the thresholds and the eight
-//   bf16 outputs of the block) is built once per workgroup for all 128 bytes
-//   into a 6 KB LDS table, so a block costs one scale computation and one LDS
-//   lookup.
-// * Workgroups are persistent (a few per CU) and walk the tensor with a grid
-//   stride, which amortises the table build over many blocks.
+// * The quantizing kernels stream HBM (2-6 bytes per element) with a few dozen
+//   lane ops per element; the limits are HBM bandwidth and the VALU issue rate.
+// * Lanes 2k and 2k+1 hold the two halves of a 16-element block, so every load
+//   and store is contiguous across a wave; the block max combines the lane's
+//   packed 16-bit max with its partner's through one DPP permute.
+// * Element codes: q' = fl(x * r), r = 1 / sq, through the gfx950 FP4
+//   converter wherever that is provably the same code as the correctly rounded
+//   quotient fl(x / sq) for every bf16 input (a per-scale-byte certificate);
+//   otherwise integer compares against exact decision thresholds ("Decision
+//   thresholds" below).  Everything that depends only on the E4M3 scale byte S
+//   (the multiplier, the decoded scale, the thresholds, the certificate) is
+//   tabulated once per workgroup for all 128 bytes in a 4 KB LDS table, so a
+//   block costs one scale computation and one LDS lookup.
+// * Workgroups walk the tensor with a grid stride, which amortises the table
+//   build over many blocks.
 // * The per-tensor amax is a separate streaming pass with one atomic max per
 //   workgroup; the quantizing kernels read it from device memory, so a fused
 //   call never returns to the host.
+// * The linear layer over a packed weight is the one dense contraction: there
+//   the weight is decoded in registers into bf16 MFMA operands.
 //
 // Decision thresholds
 // -------------------
@@ -420,8 +423,8 @@ __device__ __forceinline__ uint32_t pair_max(const uint32_t (&w)[4])
     return max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0xB1, 0xF, 0xF, false));
 }
 
-// The eight codes of a half block (one dword of nibbles) under table entry e.
-__device__ __forceinline__ uint32_t half_codes(const uint32_t (&w)[4], const uint32_t* e)
+// The eight codes of four bf16 pairs (one dword of nibbles) under table entry e.
+__device__ __forceinline__ uint32_t half_codes(const uint32_t* w, const uint32_t* e)
 {
     const uint32_t head = e[0];
     if (!(head & kNotFast))
@@ -453,19 +456,8 @@ __device__ __forceinline__ void fake_quant_half(const uint32_t (&w)[4], uint32_t
 __device__ __forceinline__ void block_codes(const uint32_t (&w)[8], const uint32_t* e, uint32_t& c0,
                                             uint32_t& c1)
 {
-    const uint32_t head = e[0];
-    if (!(head & kNotFast)) {
-        const float r = __uint_as_float(head);
-        c0 = codes_fast(w, r);
-        c1 = codes_fast(w + 4, r);
-    } else {
-        uint32_t t[6];
-        const uint4 a = *reinterpret_cast<const uint4*>(e + 2);
-        const uint2 b = *reinterpret_cast<const uint2*>(e + 6);
-        t[0] = a.x; t[1] = a.y; t[2] = a.z; t[3] = a.w; t[4] = b.x; t[5] = b.y;
-        c0 = codes_threshold(w, t - 2);
-        c1 = codes_threshold(w + 4, t - 2);
-    }
+    c0 = half_codes(w, e);
+    c1 = half_codes(w + 4, e);
 }
 
 // Quantize-pack one block: eight code bytes into packed[b], its scale byte into scales[b].
@@ -499,7 +491,8 @@ __device__ __forceinline__ uint32_t workgroup_max(uint32_t mx, uint32_t* wave_ma
 
 // ---------------------------------------------------------------- kernels
 
-// i-th block of a pass (or -1 past the end); the pass runs backwards when kReverse.
+// i-th unit (half block, or block for the ragged kernels) of a pass, or -1 past
+// the end; the pass runs backwards when kReverse.
 __device__ __forceinline__ int64_t walk(int64_t i, int64_t nblocks)
 {
     if (i >= nblocks)
@@ -574,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(AmaxGroup g, float* out)
 
 // The kUnroll half blocks of one iteration of a quantizing pass (zeros past the end).
 template <bool NtLd>
-__device__ __forceinline__ void load_halves(const uint4* __restrict__ x, int64_t base, int64_t nhalves,
+__device__ __forceinline__ void load_halves(const uint4* x, int64_t base, int64_t nhalves,
                                             uint4 (&v)[kUnroll])
 {
 #pragma unroll
@@ -589,7 +582,7 @@ __device__ __forceinline__ void load_halves(const uint4* __restrict__ x, int64_t
 // the workgroup builds its scale-byte table, so the table build hides under
 // their latency.
 template <bool NtLd, typename Build, typename Body>
-__device__ __forceinline__ void quantize_pass(const uint4* __restrict__ x, int64_t nhalves, Build build,
+__device__ __forceinline__ void quantize_pass(const uint4* x, int64_t nhalves, Build build,
                                               Body body)
 {
     const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
@@ -618,7 +611,7 @@ __device__ __forceinline__ void build_table(float gs, uint32_t* tab)
         build_entry(threadIdx.x, gs, tab + threadIdx.x * kEntryWords);
 }
 
-__global__ __launch_bounds__(kThreads) void k_fake_quant(const uint4* __restrict__ x, uint4* y,
+__global__ __launch_bounds__(kThreads) void k_fake_quant(const uint4* x, uint4* y,
                                                          int64_t nhalves,
                                                          const float* __restrict__ amax)
 {
@@ -637,7 +630,7 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant(const uint4* __restrict
 // one amax.  A lane reads its half block before writing either output, so
 // y0 == x or y1 == x (in place) is safe.
 static_assert(kThreads == 256, "the dual table build gives each amax 128 threads");
-__global__ __launch_bounds__(kThreads) void k_fake_quant_dual(const uint4* __restrict__ x, uint4* y0,
+__global__ __launch_bounds__(kThreads) void k_fake_quant_dual(const uint4* x, uint4* y0,
                                                               uint4* y1, int64_t nhalves,
                                                               const float* __restrict__ amax0,
                                                               const float* __restrict__ amax1)
@@ -794,7 +787,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant_unpack(const uint32_t* __r
 // fewer than 16 elements and zeros, which never change a block max.  Packed
 // codes and scales keep the padded layout ([rows, 8 * nbr] and [rows, nbr] for
 // nbr = ceil(cols / 16)), so block f is still byte 8f and scale f; only the
-// bf16 side is addressed per element.  One lane owns one block, as above.
+// bf16 side is addressed per element.  Rows may start at any element, so the
+// half-block layout's vector accesses do not apply: one lane owns one block.
 struct RaggedShape {
     int64_t cols;       // elements per row
     int64_t nbr;        // blocks per row
@@ -811,7 +805,7 @@ __device__ __forceinline__ int64_t ragged_block(const RaggedShape& g, int64_t f,
     return r * g.cols + c0;
 }
 
-__device__ __forceinline__ void load_ragged(const uint16_t* __restrict__ x, int64_t e0, int n,
+__device__ __forceinline__ void load_ragged(const uint16_t* x, int64_t e0, int n,
                                             uint32_t (&w)[8])
 {
 #pragma unroll
@@ -837,7 +831,7 @@ __device__ __forceinline__ void store_ragged(uint16_t* y, int64_t e0, int n, uin
     }
 }
 
-__global__ __launch_bounds__(kThreads) void k_fake_quant_ragged(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(kThreads) void k_fake_quant_ragged(const uint16_t* x,
                                                                 uint16_t* y, RaggedShape g,
                                                                 const float* __restrict__ amax)
 {
