@@ -64,10 +64,13 @@ namespace {
 #define NVFP4_DQ_UNROLL 8         // half blocks per lane per iteration: unpack
 #endif
 #ifndef NVFP4_AMAX_UNROLL
-#define NVFP4_AMAX_UNROLL 8       // 16-byte vectors per lane per amax chunk
+#define NVFP4_AMAX_UNROLL 4       // 16-byte vectors per lane per amax chunk
 #endif
 #ifndef NVFP4_AMAX_WG_PER_CU
 #define NVFP4_AMAX_WG_PER_CU 2    // persistent workgroups per CU (each ends in one atomic)
+#endif
+#ifndef NVFP4_AMAX_PREFETCH
+#define NVFP4_AMAX_PREFETCH 1     // 1: the amax loop loads chunk c + grid while folding chunk c
 #endif
 #ifndef NVFP4_FQ_WG_PER_CU
 #define NVFP4_FQ_WG_PER_CU 64
@@ -524,7 +527,8 @@ __global__ __launch_bounds__(kThreads) void k_amax(AmaxGroup g, float* out)
     int t = 0;
     int64_t begin = 0, end = g.chunk_end[0], n = g.nvec[0];
     const uint4* __restrict__ src = g.vec[0];
-    for (int64_t c = blockIdx.x; c < total; c += gridDim.x) {
+    // the vectors of chunk c (zeros past the end of its tensor)
+    auto load_chunk = [&](int64_t c, uint4 (&v)[kAmaxUnroll]) {
         while (c >= end) {
             ++t;
             begin = end;
@@ -533,18 +537,40 @@ __global__ __launch_bounds__(kThreads) void k_amax(AmaxGroup g, float* out)
             src = g.vec[t];
         }
         const int64_t first = (c - begin) * kChunk + threadIdx.x;
-        uint4 v[kAmaxUnroll];
 #pragma unroll
         for (int u = 0; u < kAmaxUnroll; ++u) {
             const int64_t i = first + (int64_t)u * kThreads;
             v[u] = i < n ? load16<NVFP4_AMAX_NT != 0>(src + i) : make_uint4(0u, 0u, 0u, 0u);
         }
+    };
+    auto fold = [&](const uint4 (&v)[kAmaxUnroll]) {
 #pragma unroll
         for (int u = 0; u < kAmaxUnroll; ++u) {
             mx = pk_max(mx, v[u].x & 0x7FFF7FFFu);
             mx = pk_max(mx, v[u].y & 0x7FFF7FFFu);
             mx = pk_max(mx, v[u].z & 0x7FFF7FFFu);
             mx = pk_max(mx, v[u].w & 0x7FFF7FFFu);
+        }
+    };
+    if (NVFP4_AMAX_PREFETCH) {
+        // the next chunk's loads are in flight while the current one is folded
+        uint4 cur[kAmaxUnroll], nxt[kAmaxUnroll];
+        int64_t c = blockIdx.x;
+        if (c < total)
+            load_chunk(c, cur);
+        for (; c < total; c += gridDim.x) {
+            if (c + gridDim.x < total)
+                load_chunk(c + gridDim.x, nxt);
+            fold(cur);
+#pragma unroll
+            for (int u = 0; u < kAmaxUnroll; ++u)
+                cur[u] = nxt[u];
+        }
+    } else {
+        for (int64_t c = blockIdx.x; c < total; c += gridDim.x) {
+            uint4 v[kAmaxUnroll];
+            load_chunk(c, v);
+            fold(v);
         }
     }
     if (blockIdx.x == 0) {
