@@ -11,13 +11,20 @@ timed region.  The step is issued as the library calls
     nvfp4_quantize_pack(x, amax_in=a2)            /
     nvfp4_dequant_unpack(...)        -> y2
 
-which enqueue exactly the kernels of the two fused calls, with HIP events
-recorded between them on the launch stream so every kernel is timed live.
+which enqueue exactly the kernels of the two fused calls.  Inside the timed
+region, HIP events on the launch stream bracket the fake-quant kernel (the
+dominant launch) in every step; a diagnostic pass afterwards records events
+between all calls for the per-op times.
 
 Prints one JSON line on stdout (logs go to stderr):
-  value      algorithmic GB/s of the whole step (13.125 bytes per element)
-  roofline   the dominant kernel's algorithmic GB/s against 8 TB/s HBM
+  value         algorithmic GB/s of the whole step (13.125 bytes per element)
+  roofline      the dominant kernel's algorithmic GB/s against 8 TB/s HBM
   cpu_baseline  the CPU oracle on a bounded sample of the same workload
+  ops           per-op times of the diagnostic pass
+  secondary     per-call-sequence times on the other workloads (fused siblings,
+                the activation step with its observers, the mid-size weight)
+                and the packed c5 weight used as a linear layer; --no-secondary
+                skips them
 """
 import argparse
 import hashlib
