@@ -320,6 +320,24 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 4.0 * n * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
+    # Cold steps: before each, outside its events, 1 GiB is read to evict the
+    # Infinity Cache (256 MB) and the L2s, so the step starts with none of its data
+    # cached (a read leaves clean lines, so no write-back overlaps the step).
+    flush = torch.ones((1 << 30) // 4, dtype=torch.int32, device=dev)
+    cold_ms = []
+    for k in range(max(5, args.steps // 10)):
+        flush.sum()
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        step()
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cold_ms.append(c0.elapsed_time(c1))
+    del flush
+    cold_ms.sort()
+    cold_med = cold_ms[len(cold_ms) // 2]
+
     value = STEP_BYTES_PER_ELEM * n / (ms_per_step * 1e-3) / 1e9
     result = {
         "metric": "NVFP4 fake-quant / quantize-pack GB/s and % of HBM peak on 1 MI355X",
@@ -345,6 +363,10 @@ def main():
         "elements_per_s": round(n / (ms_per_step * 1e-3), 1),
         "ops": op_report,
         "copy_gbs": round(copy_gbs, 1),
+        "cold_step": {"ms": round(cold_med, 4),
+                      "gbs": round(STEP_BYTES_PER_ELEM * n / (cold_med * 1e-3) / 1e9, 1),
+                      "runs": len(cold_ms),
+                      "note": "median step after reading 1 GiB (caches evicted); value is the warm rate"},
         "roofline": {
             "kernel": KERNEL_NAMES[dom],
             "bound": "hbm",
