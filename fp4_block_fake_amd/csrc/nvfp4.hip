@@ -102,11 +102,11 @@ namespace {
 #define NVFP4_REVERSE 0
 #endif
 // Non-temporal (streaming) hints on loads (LD) and stores (ST).  The amax pass
-// reads with allocating loads: what it reads last stays in the Infinity Cache
-// (256 MB), where the quantizing pass over the same tensor finds it.  The
-// quantizing passes stream x in and their outputs out.
-#ifndef NVFP4_AMAX_NT
-#define NVFP4_AMAX_NT 0
+// reads its last NVFP4_AMAX_ALLOC_BYTES with allocating loads: that part stays in
+// the Infinity Cache (256 MB), where the quantizing pass over the same tensor
+// finds it.  The quantizing passes stream x in and their outputs out.
+#ifndef NVFP4_AMAX_ALLOC_BYTES
+#define NVFP4_AMAX_ALLOC_BYTES (192LL << 20)  // bytes at the end of an amax pass read with allocating loads
 #endif
 #ifndef NVFP4_FQ_NT_LD
 #define NVFP4_FQ_NT_LD 1
@@ -512,6 +512,7 @@ struct AmaxGroup {
     const uint16_t* tail[NVFP4_AMAX_GROUP_MAX];    // last numel % 8 values
     int32_t ntail[NVFP4_AMAX_GROUP_MAX];
     int32_t count;
+    int64_t alloc_from;                            // chunks from here on load into the caches
 };
 
 // max |x| over a group of tensors; one signed-integer atomic max per workgroup on
@@ -540,7 +541,9 @@ __global__ __launch_bounds__(kThreads) void k_amax(AmaxGroup g, float* out)
 #pragma unroll
         for (int u = 0; u < kAmaxUnroll; ++u) {
             const int64_t i = first + (int64_t)u * kThreads;
-            v[u] = i < n ? load16<NVFP4_AMAX_NT != 0>(src + i) : make_uint4(0u, 0u, 0u, 0u);
+            v[u] = i >= n                ? make_uint4(0u, 0u, 0u, 0u)
+                   : c >= g.alloc_from ? load16<false>(src + i)
+                                       : load16<true>(src + i);
         }
     };
     auto fold = [&](const uint4 (&v)[kAmaxUnroll]) {
@@ -1256,6 +1259,11 @@ nvfp4_status enqueue_amax(const void* const* xs, const int64_t* numels, int n, f
         chunks += (g.nvec[i] + kChunk - 1) / kChunk;
         g.chunk_end[i] = chunks;
     }
+    // Only the last NVFP4_AMAX_ALLOC_BYTES of the group are read with allocating
+    // loads: that is what the Infinity Cache still holds when the quantizing pass
+    // over the same tensor gets there; the rest streams past the caches.
+    const int64_t alloc_chunks = (int64_t)NVFP4_AMAX_ALLOC_BYTES / (kChunk * 16);
+    g.alloc_from = chunks > alloc_chunks ? chunks - alloc_chunks : 0;
     k_amax<<<persistent_grid(chunks, 1, NVFP4_AMAX_WG_PER_CU), kThreads, 0, stream>>>(g, amax);
     return launched();
 }
