@@ -43,6 +43,49 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(so, name), name
 
 
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "nvfp4.h"
+
+int main(void)
+{
+    /* every call is reachable from C; the arguments below fail validation, which
+       returns before any HIP call */
+    const void* xs[1] = {0};
+    int64_t numels[1] = {16};
+    int bad = 0;
+    bad |= nvfp4_amax(xs, numels, 1, 0, 0, 0) != NVFP4_ERR_NULL;
+    bad |= nvfp4_fake_quant(0, 0, 4, 16, 0, 0, 0) != NVFP4_ERR_NULL;
+    bad |= nvfp4_fake_quant_group(0, 0, 0, 0, 1, 0, 0, 0) != NVFP4_ERR_NULL;
+    bad |= nvfp4_fake_quant_dual(0, 4, 0, 0, 0, 0, 0, 0) != NVFP4_ERR_SHAPE;
+    bad |= nvfp4_quantize_pack(0, -1, 16, 0, 0, 0, 0, 0, 0) != NVFP4_ERR_SHAPE;
+    bad |= nvfp4_dequant_unpack(0, 0, 0, 4, 16, 0, 0) != NVFP4_ERR_NULL;
+    bad |= nvfp4_linear(0, 4, 48, 0, 0, 0, 8, 0, 0, 0) != NVFP4_ERR_SHAPE;
+    bad |= nvfp4_observer_update(0, 0, NVFP4_OBS_EMA, 0.5f, 0) != NVFP4_ERR_NULL;
+    bad |= strcmp(nvfp4_strerror(NVFP4_OK), "ok") != 0;
+    printf("%s\n", bad ? "FAIL" : "OK");
+    return bad;
+}
+"""
+
+
+def test_header_is_c99_and_links(tmp_path):
+    """include/nvfp4.h compiles as C99 and a C program links and calls the library."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(nv.library_path)
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                           str(src), "-o", str(exe), "-L", libdir, "-lnvfp4", "-Wl,-rpath," + libdir])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0 and out.stdout.strip() == "OK", out.stdout + out.stderr
+
+
 def test_strerror_names_every_status():
     for s in range(7):
         assert nv.nvfp4_strerror(s) and nv.nvfp4_strerror(s) != "unknown status"
