@@ -165,8 +165,21 @@ def secondary(nv, synth, np, torch, dev, reps=20):
         nv.nvfp4_fake_quant_dual(x, st_s, st_e, y0=y1, y1=y2)
     # same outputs from one read of x: 8 bytes per element of traffic instead of 10
     out["c4_activation_step_dual_fake_quant"] = timed(c4act_dual, 8.0 * x.numel())
+    # the same step as one call: 4 launches (reset, amax, both observer steps, dual
+    # fake-quant) instead of 5
+    out["c4_activation_step_observe_fake_quant"] = timed(
+        lambda: nv.nvfp4_observe_fake_quant(x, st_s, nv.OBS_STATIC_MINMAX, 0.0, st_e, nv.OBS_EMA, 0.01,
+                                            y0=y1, y1=y2, cur=cur), 8.0 * x.numel())
     out["c4_activation_cached_fake_quant"] = timed(lambda: nv.nvfp4_fake_quant(x, y=y1, amax_in=st_s),
                                                    4.0 * x.numel())
+    out["c4_activation_fused_amax_fake_quant"] = timed(
+        lambda: nv.nvfp4_fake_quant(x, y=y1, amax_out=cur), 6.0 * x.numel())
+    pa = torch.empty((x.shape[0], x.shape[1] // 2), dtype=torch.uint8, device=dev)
+    sa = torch.empty((x.shape[0], x.shape[1] // 16), dtype=torch.uint8, device=dev)
+    ga = torch.empty(1, dtype=torch.float32, device=dev)
+    out["c4_activation_fused_amax_quantize_pack"] = timed(
+        lambda: nv.nvfp4_quantize_pack(x, amax_out=cur, packed=pa, scales=sa, global_scale=ga), 4.5625 * x.numel())
+    del pa, sa
     del x, y1, y2
 
     w = to_dev(synth.c4_weight())

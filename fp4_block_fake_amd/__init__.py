@@ -17,7 +17,7 @@ __all__ = [
     "NVFP4Error", "OBS_STATIC_MINMAX", "OBS_EMA", "lib", "library_path",
     "nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
     "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
-    "nvfp4_strerror", "FakeQuantSTE", "blocks_per_row",
+    "nvfp4_strerror", "FakeQuantSTE", "blocks_per_row", "nvfp4_observe_fake_quant",
 ]
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
@@ -27,7 +27,7 @@ OBS_EMA = 1
 
 _EXPORTS = ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
             "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
-            "nvfp4_strerror")
+            "nvfp4_observe_fake_quant", "nvfp4_strerror")
 
 
 class NVFP4Error(RuntimeError):
@@ -50,10 +50,13 @@ def _load() -> ctypes.CDLL:
     so.nvfp4_dequant_unpack.argtypes = [P, P, P, I64, I64, P, P]
     so.nvfp4_linear.argtypes = [P, I64, I64, P, P, P, I64, P, P, P]
     so.nvfp4_observer_update.argtypes = [P, P, I, ctypes.c_float, P]
+    F = ctypes.c_float
+    so.nvfp4_observe_fake_quant.argtypes = [P, I64, I64, P, P, I, F, P, P, I, F, P, P]
     so.nvfp4_strerror.argtypes = [I]
     so.nvfp4_strerror.restype = ctypes.c_char_p
-    for name in _EXPORTS[:-1]:
-        getattr(so, name).restype = I
+    for name in _EXPORTS:
+        if name != "nvfp4_strerror":
+            getattr(so, name).restype = I
     return so
 
 
@@ -261,6 +264,31 @@ def nvfp4_observer_update(state: torch.Tensor, cur: torch.Tensor, mode: int = OB
     _check(lib.nvfp4_observer_update(_ptr(state), _ptr(cur), int(mode), float(decay),
                                      _stream(state.device)), "nvfp4_observer_update")
     return state
+
+
+def nvfp4_observe_fake_quant(x: torch.Tensor, state0: torch.Tensor, mode0: int = OBS_STATIC_MINMAX,
+                             decay0: float = 0.01, state1: torch.Tensor | None = None,
+                             mode1: int = OBS_EMA, decay1: float = 0.01,
+                             y0: torch.Tensor | None = None, y1: torch.Tensor | None = None,
+                             cur: torch.Tensor | None = None):
+    """One activation step: cur = max|x|, each observer state steps on cur (in place),
+    and x is fake-quantized with each new state -> y0, or (y0, y1) with two observers."""
+    rows, cols = _matrix(x, "x")
+    dev = x.device
+    _scalar(dev, state0)
+    if state1 is not None:
+        _scalar(dev, state1)
+    cur = _scalar(dev, cur)
+    y0 = torch.empty_like(x) if y0 is None else y0
+    if state1 is not None and y1 is None:
+        y1 = torch.empty_like(x)
+    for name, y in (("y0", y0), ("y1", y1)):
+        if y is not None and _matrix(y, name) != x.shape:
+            raise ValueError("%s must have the shape of x" % name)
+    _check(lib.nvfp4_observe_fake_quant(_ptr(x), rows, cols, _ptr(cur), _ptr(state0), int(mode0),
+                                        float(decay0), _ptr(y0), _ptr(state1), int(mode1), float(decay1),
+                                        _ptr(y1), _stream(dev)), "nvfp4_observe_fake_quant")
+    return y0 if state1 is None else (y0, y1)
 
 
 class FakeQuantSTE(torch.autograd.Function):

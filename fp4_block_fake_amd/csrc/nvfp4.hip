@@ -1177,21 +1177,31 @@ __global__ __launch_bounds__(64 * W) void k_linear(const uint16_t* __restrict__ 
     }
 }
 
-__global__ void k_observer(float* state, const float* cur, int mode, float decay)
+// Observer steps of up to two states on the same step amax *cur.
+struct ObserverArgs {
+    float* state[2];
+    int mode[2];
+    float decay[2];
+};
+
+__global__ void k_observer(const float* cur, ObserverArgs o, int n)
 {
-    const float s = *state, c = *cur;
-    float r;
-    if (s < 0.0f) {
-        r = c;                                     // first observation
-    } else if (mode == NVFP4_OBS_STATIC_MINMAX) {
-        r = c > s ? c : s;
-    } else {
-        const float keep = 1.0f - decay;
-        const float a = keep * s;
-        const float b = decay * c;
-        r = a + b;                                 // no contraction: -ffp-contract=off
+    const float c = *cur;
+    for (int i = 0; i < n; ++i) {
+        const float s = *o.state[i];
+        float r;
+        if (s < 0.0f) {
+            r = c;                                 // first observation
+        } else if (o.mode[i] == NVFP4_OBS_STATIC_MINMAX) {
+            r = c > s ? c : s;
+        } else {
+            const float keep = 1.0f - o.decay[i];
+            const float a = keep * s;
+            const float b = o.decay[i] * c;
+            r = a + b;                             // no contraction: -ffp-contract=off
+        }
+        *o.state[i] = r;
     }
-    *state = r;
 }
 
 // ---------------------------------------------------------------- host helpers
@@ -1424,6 +1434,37 @@ nvfp4_status enqueue_linear_mt(const void* x, int64_t m, int64_t k, const uint8_
         return enqueue_linear_w<MT, 2>(NVFP4_LIN_ARGS);
     return enqueue_linear_w<MT, 1>(NVFP4_LIN_ARGS);
 #undef NVFP4_LIN_ARGS
+}
+
+// A device region an entry point reads or writes.
+struct Region {
+    const void* p;
+    uint64_t bytes;
+};
+
+// Outputs must be disjoint from each other and from the inputs, except that an
+// output with the start and size of in[0] may be in[0] itself (exact in-place)
+// when inplace_ok.  Empty regions overlap nothing.
+nvfp4_status check_regions(const Region* in, int nin, const Region* out, int nout, bool inplace_ok)
+{
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j) {
+            const bool same = inplace_ok && j == 0 && out[i].p == in[0].p && out[i].bytes == in[0].bytes;
+            if (!same && overlap(out[i].p, out[i].bytes, in[j].p, in[j].bytes))
+                return NVFP4_ERR_OVERLAP;
+        }
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(out[i].p, out[i].bytes, out[j].p, out[j].bytes))
+                return NVFP4_ERR_OVERLAP;
+    }
+    return NVFP4_OK;
+}
+
+bool observer_args_ok(int mode, float decay)
+{
+    if (mode != NVFP4_OBS_STATIC_MINMAX && mode != NVFP4_OBS_EMA)
+        return false;
+    return mode != NVFP4_OBS_EMA || (decay > 0.0f && decay <= 1.0f);
 }
 
 }  // namespace
@@ -1698,13 +1739,55 @@ nvfp4_status nvfp4_observer_update(float* state, const float* cur, int mode, flo
         return NVFP4_ERR_NULL;
     if (!aligned(state, 4) || !aligned(cur, 4))
         return NVFP4_ERR_ALIGN;
-    if (mode != NVFP4_OBS_STATIC_MINMAX && mode != NVFP4_OBS_EMA)
-        return NVFP4_ERR_ARG;
-    if (mode == NVFP4_OBS_EMA && !(decay > 0.0f && decay <= 1.0f))
+    if (!observer_args_ok(mode, decay))
         return NVFP4_ERR_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    k_observer<<<1, 1, 0, s>>>(state, cur, mode, decay);
+    k_observer<<<1, 1, 0, s>>>(cur, ObserverArgs{{state, nullptr}, {mode, 0}, {decay, 0.0f}}, 1);
+    return launched();
+}
+
+nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols, float* cur,
+                                      float* state0, int mode0, float decay0, void* y0,
+                                      float* state1, int mode1, float decay1, void* y1, void* stream)
+{
+    Matrix m;
+    nvfp4_status st = check_matrix(rows, cols, &m);
+    if (st != NVFP4_OK)
+        return st;
+    const bool two = state1 != nullptr;
+    if (!cur || !state0 || (m.numel > 0 && (!x || !y0 || (two && !y1))))
+        return NVFP4_ERR_NULL;
+    if ((!two && y1) || !observer_args_ok(mode0, decay0) || (two && !observer_args_ok(mode1, decay1)))
+        return NVFP4_ERR_ARG;
+    if (!aligned(x, 16) || !aligned(y0, 16) || !aligned(y1, 16) || !aligned(cur, 4) || !aligned(state0, 4) ||
+        !aligned(state1, 4))
+        return NVFP4_ERR_ALIGN;
+    const uint64_t bytes = 2 * (uint64_t)m.numel;
+    const Region in[1] = {{x, bytes}};
+    const Region out[5] = {{y0, y0 ? bytes : 0u}, {y1, y1 ? bytes : 0u}, {cur, 4}, {state0, 4},
+                           {state1, two ? 4u : 0u}};
+    if (check_regions(in, 1, out, 5, true) != NVFP4_OK)
+        return NVFP4_ERR_OVERLAP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    st = enqueue_amax_one(x, m.numel, cur, s);
+    if (st != NVFP4_OK)
+        return st;
+    k_observer<<<1, 1, 0, s>>>(cur, ObserverArgs{{state0, state1}, {mode0, mode1}, {decay0, decay1}}, two ? 2 : 1);
+    if ((st = launched()) != NVFP4_OK || m.numel == 0)
+        return st;
+    if (!two)
+        return enqueue_fake_quant(x, y0, cols, m, state0, s);
+    if (m.ragged) {
+        // two passes; an output written in place goes last, after x has been read
+        const bool swap = y0 == x;
+        st = enqueue_fake_quant(x, swap ? y1 : y0, cols, m, swap ? state1 : state0, s);
+        return st != NVFP4_OK ? st : enqueue_fake_quant(x, swap ? y0 : y1, cols, m, swap ? state0 : state1, s);
+    }
+    k_fake_quant_dual<<<persistent_grid(2 * m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
+        static_cast<const uint4*>(x), static_cast<uint4*>(y0), static_cast<uint4*>(y1), 2 * m.nblocks, state0,
+        state1);
     return launched();
 }
 

@@ -222,6 +222,36 @@ nvfp4_status nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* pa
 nvfp4_status nvfp4_observer_update(float* state, const float* cur, int mode, float decay,
                                    void* stream);
 
+/*
+ * nvfp4_observe_fake_quant -- the activation step of a W4A4 layer with one or
+ * two observers, as one call (verl QATLinear page, section 5: the step's amax
+ * updates the observer, and the activation is fake-quantized with the updated
+ * state):
+ *   *cur     := max|x|                      (as nvfp4_amax)
+ *   *state_i := one nvfp4_observer_update step of *state_i on *cur
+ *   y_i      := nvfp4_fake_quant(x) with amax_in = the new *state_i
+ * With two observers x is read once for both outputs.  The results are those
+ * of the separate calls, bit for bit.
+ *
+ *   x               device bf16 [rows, cols], 16-byte aligned
+ *   cur             device fp32, 4-byte aligned: receives the step amax
+ *   state0, y0      first observer state (device fp32, 4-byte aligned) and its
+ *                   output (device bf16 [rows, cols], 16-byte aligned; y0 == x
+ *                   allowed)
+ *   state1, y1      second observer and its output, or both NULL for one
+ *                   observer (y1 == x allowed when y0 != x)
+ *   mode_i, decay_i as for nvfp4_observer_update
+ * x, y0 and y1 may be NULL when rows == 0; the states still step on *cur = +0.
+ * The amax is the local one: a data-parallel caller that all-reduces the step
+ * amax before the observer update uses the separate calls instead.
+ * Errors: SHAPE, NULL, ALIGN, OVERLAP, ARG (bad mode or decay, or y1 without
+ * state1), HIP.
+ */
+nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols, float* cur,
+                                      float* state0, int mode0, float decay0, void* y0,
+                                      float* state1, int mode1, float decay1, void* y1,
+                                      void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* nvfp4_strerror(int status);
 

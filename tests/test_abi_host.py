@@ -33,7 +33,7 @@ def test_header_declares_every_call():
     names = declared_functions()
     for n in ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
               "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
-              "nvfp4_strerror"):
+              "nvfp4_observe_fake_quant", "nvfp4_strerror"):
         assert n in names
 
 
@@ -63,6 +63,7 @@ int main(void)
     bad |= nvfp4_dequant_unpack(0, 0, 0, 4, 16, 0, 0) != NVFP4_ERR_NULL;
     bad |= nvfp4_linear(0, 4, 48, 0, 0, 0, 8, 0, 0, 0) != NVFP4_ERR_SHAPE;
     bad |= nvfp4_observer_update(0, 0, NVFP4_OBS_EMA, 0.5f, 0) != NVFP4_ERR_NULL;
+    bad |= nvfp4_observe_fake_quant(0, 4, 16, 0, 0, 0, 0.0f, 0, 0, 0, 0.0f, 0, 0) != NVFP4_ERR_NULL;
     bad |= strcmp(nvfp4_strerror(NVFP4_OK), "ok") != 0;
     printf("%s\n", bad ? "FAIL" : "OK");
     return bad;
@@ -252,3 +253,40 @@ def test_binding_refuses_cpu_tensors():
         nv.nvfp4_quantize_pack(x)
     with pytest.raises(ValueError):
         nv.nvfp4_amax([x])
+
+
+def test_observe_fake_quant_validation():
+    f = nv.lib.nvfp4_observe_fake_quant
+    G = 1 << 30
+    x, y0, y1, s0, s1, c = A, A + G, A + 2 * G, A + 3 * G, A + 4 * G, A + 5 * G
+    S, E = nv.OBS_STATIC_MINMAX, nv.OBS_EMA
+
+    def call(x=x, rows=4, cols=16, cur=c, st0=s0, m0=S, d0=0.0, out0=y0, st1=s1, m1=E, d1=0.01, out1=y1):
+        return f(P(x), rows, cols, P(cur), P(st0), m0, d0, P(out0), P(st1), m1, d1, P(out1), None)
+
+    assert call(cols=0) == ERR_SHAPE
+    assert call(rows=-2) == ERR_SHAPE
+    assert call(x=None) == ERR_NULL
+    assert call(cur=None) == ERR_NULL                           # the step amax goes somewhere
+    assert call(st0=None) == ERR_NULL
+    assert call(out0=None) == ERR_NULL
+    assert call(out1=None) == ERR_NULL                          # two observers need two outputs
+    assert call(rows=0, x=None, out0=None, out1=None, cur=None) == ERR_NULL
+    assert call(st1=None) == ERR_ARG                            # y1 without a second observer
+    assert call(m0=2) == ERR_ARG
+    assert call(m1=-1) == ERR_ARG
+    assert call(m1=E, d1=0.0) == ERR_ARG
+    assert call(m1=E, d1=1.5) == ERR_ARG
+    assert call(m0=E, d0=float("nan")) == ERR_ARG
+    assert call(out0=y0 + 8) == ERR_ALIGN
+    assert call(x=x + 2) == ERR_ALIGN
+    assert call(st1=s1 + 2) == ERR_ALIGN
+    assert call(cur=c + 1) == ERR_ALIGN
+    assert call(out0=x + 32) == ERR_OVERLAP                     # partial overlap with x
+    assert call(out0=x, out1=x) == ERR_OVERLAP                  # both outputs in place
+    assert call(out1=y0 + 64) == ERR_OVERLAP
+    assert call(st1=s0) == ERR_OVERLAP                          # one state for both observers
+    assert call(cur=s0) == ERR_OVERLAP
+    assert call(cur=s1) == ERR_OVERLAP
+    assert call(st0=x + 4) == ERR_OVERLAP
+    assert call(cur=y1 + 8) == ERR_OVERLAP
