@@ -179,6 +179,13 @@ def secondary(nv, synth, np, torch, dev, reps=20):
     ga = torch.empty(1, dtype=torch.float32, device=dev)
     out["c4_activation_fused_amax_quantize_pack"] = timed(
         lambda: nv.nvfp4_quantize_pack(x, amax_out=cur, packed=pa, scales=sa, global_scale=ga), 4.5625 * x.numel())
+    # the fused calls through a workspace: no clearing launch, no atomics
+    ws = nv.new_workspace(dev)
+    out["c4_activation_fused_amax_fake_quant_ws"] = timed(
+        lambda: nv.nvfp4_fake_quant_ws(x, y=y1, amax_out=cur, workspace=ws), 6.0 * x.numel())
+    out["c4_activation_fused_amax_quantize_pack_ws"] = timed(
+        lambda: nv.nvfp4_quantize_pack_ws(x, amax_out=cur, packed=pa, scales=sa, global_scale=ga, workspace=ws),
+        4.5625 * x.numel())
     del pa, sa
     del x, y1, y2
 
@@ -193,6 +200,11 @@ def secondary(nv, synth, np, torch, dev, reps=20):
     out["c4_weight_fused_amax_quantize_pack_14336x4096"] = timed(
         lambda: nv.nvfp4_quantize_pack(w, amax_out=aw, packed=pk, scales=sc, global_scale=gsw),
         4.5625 * w.numel())
+    out["c4_weight_fused_amax_fake_quant_ws"] = timed(
+        lambda: nv.nvfp4_fake_quant_ws(w, y=yw, amax_out=aw, workspace=ws), 6.0 * w.numel())
+    out["c4_weight_fused_amax_quantize_pack_ws"] = timed(
+        lambda: nv.nvfp4_quantize_pack_ws(w, amax_out=aw, packed=pk, scales=sc, global_scale=gsw, workspace=ws),
+        4.5625 * w.numel())
     del w, yw, pk, sc
 
     # the c5 weight used as a linear layer (packed once), against unpack + torch's bf16 GEMM
@@ -201,7 +213,18 @@ def secondary(nv, synth, np, torch, dev, reps=20):
     n, k = wc.shape
     packed, scales, gsc = nv.nvfp4_quantize_pack(wc)
     wdq = nv.nvfp4_dequant_unpack(packed, scales, gsc)
-    del wc
+    # the fused calls on the c5 weight through the workspace (the step above uses
+    # the three-launch form, whose quantizing kernel the roofline times alone)
+    yc = torch.empty_like(wc)
+    pc = torch.empty_like(packed)
+    scc = torch.empty_like(scales)
+    ac, gc = torch.empty(1, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.float32, device=dev)
+    out["c5_weight_fused_amax_fake_quant_ws"] = timed(
+        lambda: nv.nvfp4_fake_quant_ws(wc, y=yc, amax_out=ac, workspace=ws), 6.0 * wc.numel())
+    out["c5_weight_fused_amax_quantize_pack_ws"] = timed(
+        lambda: nv.nvfp4_quantize_pack_ws(wc, amax_out=ac, packed=pc, scales=scc, global_scale=gc, workspace=ws),
+        4.5625 * wc.numel())
+    del wc, yc, pc, scc
     gen = torch.Generator(device="cpu").manual_seed(7)
     for m in (1, 16, 64):
         xm = torch.randn(m, k, generator=gen).to(torch.bfloat16).to(dev)

@@ -18,16 +18,19 @@ __all__ = [
     "nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
     "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
     "nvfp4_strerror", "FakeQuantSTE", "blocks_per_row", "nvfp4_observe_fake_quant",
+    "WORKSPACE_BYTES", "new_workspace", "nvfp4_fake_quant_ws", "nvfp4_quantize_pack_ws",
 ]
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
 
 OBS_STATIC_MINMAX = 0
 OBS_EMA = 1
+WORKSPACE_BYTES = 2304        # NVFP4_WORKSPACE_BYTES
 
 _EXPORTS = ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
             "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
-            "nvfp4_observe_fake_quant", "nvfp4_strerror")
+            "nvfp4_observe_fake_quant", "nvfp4_fake_quant_ws", "nvfp4_quantize_pack_ws",
+            "nvfp4_strerror")
 
 
 class NVFP4Error(RuntimeError):
@@ -52,6 +55,8 @@ def _load() -> ctypes.CDLL:
     so.nvfp4_observer_update.argtypes = [P, P, I, ctypes.c_float, P]
     F = ctypes.c_float
     so.nvfp4_observe_fake_quant.argtypes = [P, I64, I64, P, P, I, F, P, P, I, F, P, P]
+    so.nvfp4_fake_quant_ws.argtypes = [P, P, I64, I64, P, P, P]
+    so.nvfp4_quantize_pack_ws.argtypes = [P, I64, I64, P, P, P, P, P, P]
     so.nvfp4_strerror.argtypes = [I]
     so.nvfp4_strerror.restype = ctypes.c_char_p
     for name in _EXPORTS:
@@ -289,6 +294,62 @@ def nvfp4_observe_fake_quant(x: torch.Tensor, state0: torch.Tensor, mode0: int =
                                         float(decay0), _ptr(y0), _ptr(state1), int(mode1), float(decay1),
                                         _ptr(y1), _stream(dev)), "nvfp4_observe_fake_quant")
     return y0 if state1 is None else (y0, y1)
+
+
+def new_workspace(device) -> torch.Tensor:
+    """A workspace for the *_ws calls (torch's allocations are 512-byte aligned).
+    Reuse it for calls on one stream."""
+    return torch.empty(WORKSPACE_BYTES, dtype=torch.uint8, device=device)
+
+
+def _workspace(device, ws):
+    if ws is None:
+        return new_workspace(device)
+    if not ws.is_cuda or ws.dtype != torch.uint8 or ws.numel() < WORKSPACE_BYTES or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 CUDA tensor of at least %d bytes"
+                         % WORKSPACE_BYTES)
+    return ws
+
+
+def nvfp4_fake_quant_ws(x: torch.Tensor, y: torch.Tensor | None = None,
+                        amax_out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """nvfp4_fake_quant with the amax computed from x, through a workspace."""
+    rows, cols = _matrix(x, "x")
+    if y is None:
+        y = torch.empty_like(x)
+    if _matrix(y, "y") != x.shape:
+        raise ValueError("y must have the shape of x")
+    if amax_out is not None:
+        _scalar(x.device, amax_out)
+    ws = _workspace(x.device, workspace)
+    _check(lib.nvfp4_fake_quant_ws(_ptr(x), _ptr(y), rows, cols, _ptr(amax_out), _ptr(ws),
+                                   _stream(x.device)), "nvfp4_fake_quant_ws")
+    return y
+
+
+def nvfp4_quantize_pack_ws(x: torch.Tensor, amax_out: torch.Tensor | None = None,
+                           packed: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+                           global_scale: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None):
+    """nvfp4_quantize_pack with the amax computed from x, through a workspace."""
+    rows, cols = _matrix(x, "x")
+    dev = x.device
+    nbr = blocks_per_row(cols)
+    if packed is None:
+        packed = torch.empty((rows, 8 * nbr), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, nbr), dtype=torch.uint8, device=dev)
+    global_scale = _scalar(dev, global_scale)
+    if amax_out is not None:
+        _scalar(dev, amax_out)
+    for t, shape in ((packed, (rows, 8 * nbr)), (scales, (rows, nbr))):
+        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("packed/scales must be contiguous uint8 CUDA tensors of shape %s" % (shape,))
+    ws = _workspace(dev, workspace)
+    _check(lib.nvfp4_quantize_pack_ws(_ptr(x), rows, cols, _ptr(amax_out), _ptr(packed), _ptr(scales),
+                                      _ptr(global_scale), _ptr(ws), _stream(dev)), "nvfp4_quantize_pack_ws")
+    return packed, scales, global_scale
 
 
 class FakeQuantSTE(torch.autograd.Function):

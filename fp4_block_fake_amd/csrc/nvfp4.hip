@@ -78,6 +78,16 @@ namespace {
 #ifndef NVFP4_QP_WG_PER_CU
 #define NVFP4_QP_WG_PER_CU 64
 #endif
+// Tensors below NVFP4_MID_BYTES get at most NVFP4_MID_WG_PER_CU quantizing
+// workgroups per CU: each then covers several iterations (fewer table builds,
+// loads of the next iteration in flight), 2-4 us faster on 64-112 MB tensors
+// and slower on the 470 MB one.
+#ifndef NVFP4_MID_BYTES
+#define NVFP4_MID_BYTES (256LL << 20)
+#endif
+#ifndef NVFP4_MID_WG_PER_CU
+#define NVFP4_MID_WG_PER_CU 8
+#endif
 #ifndef NVFP4_LIN_DEPTH
 #define NVFP4_LIN_DEPTH 2         // K steps of weight loads in flight per linear wave (even)
 #endif
@@ -515,10 +525,14 @@ struct AmaxGroup {
     int64_t alloc_from;                            // chunks from here on load into the caches
 };
 
-// max |x| over a group of tensors; one signed-integer atomic max per workgroup on
-// the fp32 bits of the result (non-negative floats order like their bits, and a
-// negative prior value loses to any of them).
-__global__ __launch_bounds__(kThreads) void k_amax(AmaxGroup g, float* out)
+// max |x| over a group of tensors.  Atomic mode: one signed-integer atomic max
+// per workgroup on the fp32 bits of the result (non-negative floats order like
+// their bits, and a negative prior value loses to any of them).  Partials mode
+// (the workspace calls): workgroup i stores its maximum in partials[i] instead
+// and k_amax_finish reduces them, so no launch clears the amax first and no
+// atomics contend at the end of the pass.
+template <bool Partials>
+__global__ __launch_bounds__(kThreads) void k_amax(AmaxGroup g, float* out, uint32_t* partials)
 {
     constexpr int64_t kChunk = (int64_t)kThreads * kAmaxUnroll;
     uint32_t mx = 0;
@@ -583,6 +597,11 @@ __global__ __launch_bounds__(kThreads) void k_amax(AmaxGroup g, float* out)
     }
     __shared__ uint32_t wave_max[kThreads / 64];
     const uint32_t r = workgroup_max(mx, wave_max);
+    if (Partials) {
+        if (threadIdx.x == 0)
+            partials[blockIdx.x] = r;
+        return;
+    }
     if (threadIdx.x == 0) {
         // Same-address atomics serialise at the coherence point; the maximum only
         // grows, so a workgroup that already sees a value at least as large as its
@@ -592,6 +611,18 @@ __global__ __launch_bounds__(kThreads) void k_amax(AmaxGroup g, float* out)
         if (mine > __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
             atomicMax(dst, mine);
     }
+}
+
+// The amax from the partial maxima (bf16 magnitude bits) of the amax pass.
+__global__ __launch_bounds__(kThreads) void k_amax_finish(const uint32_t* partials, int count, float* amax)
+{
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < count; i += kThreads)
+        m = max(m, partials[i]);
+    __shared__ uint32_t wave_max[kThreads / 64];
+    const uint32_t r = workgroup_max(m, wave_max);
+    if (threadIdx.x == 0)
+        *amax = __uint_as_float(r << 16);
 }
 
 // The kUnroll half blocks of one iteration of a quantizing pass (zeros past the end).
@@ -1274,7 +1305,7 @@ nvfp4_status enqueue_amax(const void* const* xs, const int64_t* numels, int n, f
     // over the same tensor gets there; the rest streams past the caches.
     const int64_t alloc_chunks = (int64_t)NVFP4_AMAX_ALLOC_BYTES / (kChunk * 16);
     g.alloc_from = chunks > alloc_chunks ? chunks - alloc_chunks : 0;
-    k_amax<<<persistent_grid(chunks, 1, NVFP4_AMAX_WG_PER_CU), kThreads, 0, stream>>>(g, amax);
+    k_amax<false><<<persistent_grid(chunks, 1, NVFP4_AMAX_WG_PER_CU), kThreads, 0, stream>>>(g, amax, nullptr);
     return launched();
 }
 
@@ -1316,6 +1347,12 @@ nvfp4_status enqueue_amax_one(const void* x, int64_t numel, float* amax, hipStre
     return enqueue_amax(&x, &numel, 1, amax, stream);
 }
 
+// Workgroups per CU of a quantizing pass over nhalves half blocks.
+int quant_wg_per_cu(int64_t nhalves, int large)
+{
+    return nhalves * 16 < NVFP4_MID_BYTES ? NVFP4_MID_WG_PER_CU : large;
+}
+
 // One fake-quant launch of a single tensor with a device amax.
 nvfp4_status enqueue_fake_quant(const void* x, void* y, int64_t cols, const Matrix& m, const float* a,
                                 hipStream_t s)
@@ -1328,10 +1365,66 @@ nvfp4_status enqueue_fake_quant(const void* x, void* y, int64_t cols, const Matr
             static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), g, a);
         return launched();
     }
-    k_fake_quant<<<persistent_grid(2 * m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
-        static_cast<const uint4*>(x), static_cast<uint4*>(y), 2 * m.nblocks, a);
+    const int64_t nh = 2 * m.nblocks;
+    k_fake_quant<<<persistent_grid(nh, (int64_t)kThreads * kUnroll, quant_wg_per_cu(nh, NVFP4_FQ_WG_PER_CU)),
+                   kThreads, 0, s>>>(static_cast<const uint4*>(x), static_cast<uint4*>(y), nh, a);
     return launched();
 }
+
+
+// One quantize-pack launch of a single tensor (also for an empty one: it still
+// writes the global scale).
+nvfp4_status enqueue_quantize_pack(const void* x, int64_t cols, const Matrix& m, uint8_t* packed, uint8_t* scales,
+                                   float* global_scale, const float* a, hipStream_t s)
+{
+    if (m.ragged) {
+        const RaggedShape g{cols, m.nbr, m.nblocks};
+        k_quantize_pack_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
+            static_cast<const uint16_t*>(x), reinterpret_cast<uint2*>(packed), scales, global_scale, g, a);
+        return launched();
+    }
+    const int64_t nh = 2 * m.nblocks;
+    k_quantize_pack<<<persistent_grid(nh, (int64_t)kThreads * kUnroll, quant_wg_per_cu(nh, NVFP4_QP_WG_PER_CU)),
+                      kThreads, 0, s>>>(static_cast<const uint4*>(x), reinterpret_cast<uint32_t*>(packed), scales,
+                                        global_scale, nh, a);
+    return launched();
+}
+
+// The workspace of the calls that take one: the amax (when the caller asks
+// for none) at byte 0, the amax pass's partial maxima from byte kPartialsOffset.
+constexpr int64_t kPartialsOffset = 256;
+constexpr int kMaxPartials = (int)((NVFP4_WORKSPACE_BYTES - kPartialsOffset) / 4);
+static_assert(kMaxPartials >= 2 * 256, "the workspace holds a partial per amax workgroup");
+
+// Enqueue the amax of one tensor through the workspace: the amax pass in
+// partials mode, then their reduction into *amax.  An empty tensor gets one
+// workgroup, which stores a zero partial.
+nvfp4_status enqueue_amax_ws(const void* x, int64_t numel, void* ws, float* amax, hipStream_t stream)
+{
+    AmaxGroup g{};
+    constexpr int64_t kChunk = (int64_t)kThreads * kAmaxUnroll;
+    g.count = 1;
+    g.vec[0] = static_cast<const uint4*>(x);
+    g.nvec[0] = numel / 8;
+    g.tail[0] = static_cast<const uint16_t*>(x) + (numel & ~(int64_t)7);
+    g.ntail[0] = (int32_t)(numel & 7);
+    const int64_t chunks = (g.nvec[0] + kChunk - 1) / kChunk;
+    g.chunk_end[0] = chunks;
+    const int64_t alloc_chunks = (int64_t)NVFP4_AMAX_ALLOC_BYTES / (kChunk * 16);
+    g.alloc_from = chunks > alloc_chunks ? chunks - alloc_chunks : 0;
+    unsigned grid = persistent_grid(chunks, 1, NVFP4_AMAX_WG_PER_CU);
+    if (grid > (unsigned)kMaxPartials)
+        grid = (unsigned)kMaxPartials;
+    uint32_t* partials = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kPartialsOffset);
+    k_amax<true><<<grid, kThreads, 0, stream>>>(g, nullptr, partials);
+    if (launched() != NVFP4_OK)
+        return NVFP4_ERR_HIP;
+    k_amax_finish<<<1, kThreads, 0, stream>>>(partials, (int)grid, amax);
+    return launched();
+}
+
+// Where a workspace call keeps the amax: the caller's amax_out, else the workspace.
+float* ws_amax(void* ws, float* amax_out) { return amax_out ? amax_out : static_cast<float*>(ws); }
 
 // Collects tensors whose rows are whole blocks and enqueues one group launch
 // per NVFP4_AMAX_GROUP_MAX of them.
@@ -1354,7 +1447,9 @@ struct FakeQuantBatch {
     {
         if (g.count == 0)
             return NVFP4_OK;
-        k_fake_quant_group<<<persistent_grid(chunks, 1, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(g, a);
+        constexpr int64_t kChunk = (int64_t)kThreads * kUnroll;
+        k_fake_quant_group<<<persistent_grid(chunks, 1, quant_wg_per_cu(chunks * kChunk, NVFP4_FQ_WG_PER_CU)),
+                             kThreads, 0, s>>>(g, a);
         g = FqGroup{};
         chunks = 0;
         return launched();
@@ -1649,9 +1744,10 @@ nvfp4_status nvfp4_fake_quant_dual(const void* x, int64_t rows, int64_t cols, co
         st = enqueue_fake_quant(x, y0, cols, m, amax0, s);
         return st != NVFP4_OK ? st : enqueue_fake_quant(x, y1, cols, m, amax1, s);
     }
-    k_fake_quant_dual<<<persistent_grid(2 * m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
-        static_cast<const uint4*>(x), static_cast<uint4*>(y0), static_cast<uint4*>(y1), 2 * m.nblocks,
-        amax0, amax1);
+    const int64_t nh = 2 * m.nblocks;
+    k_fake_quant_dual<<<persistent_grid(nh, (int64_t)kThreads * kUnroll, quant_wg_per_cu(nh, NVFP4_FQ_WG_PER_CU)),
+                        kThreads, 0, s>>>(static_cast<const uint4*>(x), static_cast<uint4*>(y0),
+                                          static_cast<uint4*>(y1), nh, amax0, amax1);
     return launched();
 }
 
@@ -1689,16 +1785,7 @@ nvfp4_status nvfp4_quantize_pack(const void* x, int64_t rows, int64_t cols,
             return st;
         a = amax_out;
     }
-    if (m.ragged) {
-        const RaggedShape g{cols, m.nbr, m.nblocks};
-        k_quantize_pack_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
-            static_cast<const uint16_t*>(x), reinterpret_cast<uint2*>(packed), scales, global_scale, g, a);
-        return launched();
-    }
-    k_quantize_pack<<<persistent_grid(2 * m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_QP_WG_PER_CU), kThreads, 0, s>>>(
-        static_cast<const uint4*>(x), reinterpret_cast<uint32_t*>(packed), scales, global_scale,
-        2 * m.nblocks, a);
-    return launched();
+    return enqueue_quantize_pack(x, cols, m, packed, scales, global_scale, a, s);
 }
 
 nvfp4_status nvfp4_dequant_unpack(const uint8_t* packed, const uint8_t* scales,
@@ -1747,6 +1834,61 @@ nvfp4_status nvfp4_observer_update(float* state, const float* cur, int mode, flo
     return launched();
 }
 
+nvfp4_status nvfp4_fake_quant_ws(const void* x, void* y, int64_t rows, int64_t cols, float* amax_out,
+                                 void* workspace, void* stream)
+{
+    Matrix m;
+    const nvfp4_status st = check_matrix(rows, cols, &m);
+    if (st != NVFP4_OK)
+        return st;
+    if ((m.numel > 0 && (!x || !y)) || !workspace)
+        return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256) || (amax_out && !aligned(amax_out, 4)))
+        return NVFP4_ERR_ALIGN;
+    const uint64_t bytes = 2 * (uint64_t)m.numel;
+    const Region in[1] = {{x, bytes}};
+    const Region out[3] = {{y, bytes}, {amax_out, amax_out ? 4u : 0u}, {workspace, NVFP4_WORKSPACE_BYTES}};
+    if (check_regions(in, 1, out, 3, true) != NVFP4_OK)
+        return NVFP4_ERR_OVERLAP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (m.numel == 0)
+        return amax_out ? enqueue_reset(amax_out, s) : NVFP4_OK;
+    float* a = ws_amax(workspace, amax_out);
+    if (enqueue_amax_ws(x, m.numel, workspace, a, s) != NVFP4_OK)
+        return NVFP4_ERR_HIP;
+    return enqueue_fake_quant(x, y, cols, m, a, s);
+}
+
+nvfp4_status nvfp4_quantize_pack_ws(const void* x, int64_t rows, int64_t cols, float* amax_out,
+                                    uint8_t* packed, uint8_t* scales, float* global_scale, void* workspace,
+                                    void* stream)
+{
+    Matrix m;
+    const nvfp4_status st = check_matrix(rows, cols, &m);
+    if (st != NVFP4_OK)
+        return st;
+    if ((m.numel > 0 && (!x || !packed || !scales)) || !global_scale || !workspace)
+        return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(packed, 8) || !aligned(global_scale, 4) || !aligned(workspace, 256) ||
+        (amax_out && !aligned(amax_out, 4)))
+        return NVFP4_ERR_ALIGN;
+    const Region in[1] = {{x, 2 * (uint64_t)m.numel}};
+    const Region out[5] = {{packed, 8 * (uint64_t)m.nblocks},
+                           {scales, (uint64_t)m.nblocks},
+                           {global_scale, 4},
+                           {amax_out, amax_out ? 4u : 0u},
+                           {workspace, NVFP4_WORKSPACE_BYTES}};
+    if (check_regions(in, 1, out, 5, false) != NVFP4_OK)
+        return NVFP4_ERR_OVERLAP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    float* a = ws_amax(workspace, amax_out);
+    if (enqueue_amax_ws(x, m.numel, workspace, a, s) != NVFP4_OK)
+        return NVFP4_ERR_HIP;
+    return enqueue_quantize_pack(x, cols, m, packed, scales, global_scale, a, s);
+}
+
 nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols, float* cur,
                                       float* state0, int mode0, float decay0, void* y0,
                                       float* state1, int mode1, float decay1, void* y1, void* stream)
@@ -1785,9 +1927,10 @@ nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols,
         st = enqueue_fake_quant(x, swap ? y1 : y0, cols, m, swap ? state1 : state0, s);
         return st != NVFP4_OK ? st : enqueue_fake_quant(x, swap ? y0 : y1, cols, m, swap ? state0 : state1, s);
     }
-    k_fake_quant_dual<<<persistent_grid(2 * m.nblocks, (int64_t)kThreads * kUnroll, NVFP4_FQ_WG_PER_CU), kThreads, 0, s>>>(
-        static_cast<const uint4*>(x), static_cast<uint4*>(y0), static_cast<uint4*>(y1), 2 * m.nblocks, state0,
-        state1);
+    const int64_t nh = 2 * m.nblocks;
+    k_fake_quant_dual<<<persistent_grid(nh, (int64_t)kThreads * kUnroll, quant_wg_per_cu(nh, NVFP4_FQ_WG_PER_CU)),
+                        kThreads, 0, s>>>(static_cast<const uint4*>(x), static_cast<uint4*>(y0),
+                                          static_cast<uint4*>(y1), nh, state0, state1);
     return launched();
 }
 

@@ -223,6 +223,40 @@ nvfp4_status nvfp4_observer_update(float* state, const float* cur, int mode, flo
                                    void* stream);
 
 /*
+ * Workspace calls.  nvfp4_fake_quant and nvfp4_quantize_pack without amax_in
+ * clear the amax, run the amax pass (one atomic max per workgroup into the
+ * amax), then the quantizing pass.  The calls below take a caller-owned
+ * workspace instead: the amax pass leaves one partial maximum per workgroup
+ * there and a one-workgroup launch reduces them, so no atomics contend at the
+ * end of the pass (3-4 us on 32-64 MB tensors).  Same results, bit for bit.
+ *
+ *   workspace  device memory of NVFP4_WORKSPACE_BYTES bytes, 256-byte aligned,
+ *              owned by the caller.  Its contents on entry do not matter and are
+ *              undefined afterwards; it must not overlap any other argument.  A
+ *              call uses it until its last kernel ends: calls that share one
+ *              workspace must be ordered (one stream, or events), or they race.
+ */
+#define NVFP4_WORKSPACE_BYTES 2304
+
+/*
+ * nvfp4_fake_quant_ws -- nvfp4_fake_quant(x) with amax_in = NULL: the same y;
+ * amax_out (device fp32, or NULL to skip it) receives max|x|.  x and y as for
+ * nvfp4_fake_quant (y == x allowed).
+ * Errors: SHAPE, NULL, ALIGN, OVERLAP, HIP.
+ */
+nvfp4_status nvfp4_fake_quant_ws(const void* x, void* y, int64_t rows, int64_t cols,
+                                 float* amax_out, void* workspace, void* stream);
+
+/*
+ * nvfp4_quantize_pack_ws -- nvfp4_quantize_pack(x) with amax_in = NULL: the same
+ * packed, scales and global_scale; amax_out may be NULL.
+ * Errors: SHAPE, NULL, ALIGN, OVERLAP, HIP.
+ */
+nvfp4_status nvfp4_quantize_pack_ws(const void* x, int64_t rows, int64_t cols, float* amax_out,
+                                    uint8_t* packed, uint8_t* scales, float* global_scale,
+                                    void* workspace, void* stream);
+
+/*
  * nvfp4_observe_fake_quant -- the activation step of a W4A4 layer with one or
  * two observers, as one call (verl QATLinear page, section 5: the step's amax
  * updates the observer, and the activation is fake-quantized with the updated

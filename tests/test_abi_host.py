@@ -33,7 +33,8 @@ def test_header_declares_every_call():
     names = declared_functions()
     for n in ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
               "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
-              "nvfp4_observe_fake_quant", "nvfp4_strerror"):
+              "nvfp4_observe_fake_quant", "nvfp4_fake_quant_ws", "nvfp4_quantize_pack_ws",
+              "nvfp4_strerror"):
         assert n in names
 
 
@@ -64,6 +65,9 @@ int main(void)
     bad |= nvfp4_linear(0, 4, 48, 0, 0, 0, 8, 0, 0, 0) != NVFP4_ERR_SHAPE;
     bad |= nvfp4_observer_update(0, 0, NVFP4_OBS_EMA, 0.5f, 0) != NVFP4_ERR_NULL;
     bad |= nvfp4_observe_fake_quant(0, 4, 16, 0, 0, 0, 0.0f, 0, 0, 0, 0.0f, 0, 0) != NVFP4_ERR_NULL;
+    bad |= nvfp4_fake_quant_ws(0, 0, 4, 16, 0, 0, 0) != NVFP4_ERR_NULL;
+    bad |= nvfp4_quantize_pack_ws(0, 4, 0, 0, 0, 0, 0, 0, 0) != NVFP4_ERR_SHAPE;
+    bad |= NVFP4_WORKSPACE_BYTES < 2304;
     bad |= strcmp(nvfp4_strerror(NVFP4_OK), "ok") != 0;
     printf("%s\n", bad ? "FAIL" : "OK");
     return bad;
@@ -290,3 +294,57 @@ def test_observe_fake_quant_validation():
     assert call(cur=s1) == ERR_OVERLAP
     assert call(st0=x + 4) == ERR_OVERLAP
     assert call(cur=y1 + 8) == ERR_OVERLAP
+
+
+def test_workspace_size_matches_binding():
+    with open(os.path.join(ROOT, "include", "nvfp4.h")) as f:
+        m = re.search(r"#define NVFP4_WORKSPACE_BYTES (\d+)", f.read())
+    assert m and int(m.group(1)) == nv.WORKSPACE_BYTES
+
+
+def test_fake_quant_ws_validation():
+    f = nv.lib.nvfp4_fake_quant_ws
+    G = 1 << 30
+    x, y, a, w = A, A + G, A + 2 * G, A + 3 * G
+
+    def call(x=x, y=y, rows=4, cols=16, amax=a, ws=w):
+        return f(P(x), P(y), rows, cols, P(amax), P(ws), None)
+
+    assert call(cols=0) == ERR_SHAPE
+    assert call(rows=-1) == ERR_SHAPE
+    assert call(x=None) == ERR_NULL
+    assert call(y=None) == ERR_NULL
+    assert call(ws=None) == ERR_NULL                            # the workspace is required
+    assert call(rows=0, x=None, y=None, ws=None) == ERR_NULL
+    assert call(x=x + 8) == ERR_ALIGN
+    assert call(ws=w + 128) == ERR_ALIGN                        # 256-byte aligned
+    assert call(amax=a + 2) == ERR_ALIGN
+    assert call(y=x + 16) == ERR_OVERLAP
+    assert call(amax=x + 64) == ERR_OVERLAP
+    assert call(amax=w + 4) == ERR_OVERLAP                      # amax inside the workspace
+    assert call(ws=x) == ERR_OVERLAP
+    assert call(ws=y - 256) == ERR_OVERLAP                      # the workspace runs into y
+
+
+def test_quantize_pack_ws_validation():
+    f = nv.lib.nvfp4_quantize_pack_ws
+    G = 1 << 30
+    x, pk, sc, gs, a, w = A, A + G, A + 2 * G, A + 3 * G, A + 4 * G, A + 5 * G
+
+    def call(x=x, rows=4, cols=32, amax=a, packed=pk, scales=sc, g=gs, ws=w):
+        return f(P(x), rows, cols, P(amax), P(packed), P(scales), P(g), P(ws), None)
+
+    assert call(cols=-3) == ERR_SHAPE
+    assert call(x=None) == ERR_NULL
+    assert call(packed=None) == ERR_NULL
+    assert call(g=None) == ERR_NULL
+    assert call(ws=None) == ERR_NULL
+    assert call(packed=pk + 4) == ERR_ALIGN
+    assert call(ws=w + 64) == ERR_ALIGN
+    assert call(amax=a + 1) == ERR_ALIGN
+    assert call(g=gs + 2) == ERR_ALIGN
+    assert call(packed=x + 32) == ERR_OVERLAP
+    assert call(scales=pk + 8) == ERR_OVERLAP
+    assert call(g=w + 8) == ERR_OVERLAP                         # gs inside the workspace
+    assert call(amax=gs) == ERR_OVERLAP
+    assert call(ws=sc) == ERR_OVERLAP
