@@ -252,7 +252,7 @@ __device__ __forceinline__ uint32_t first_at_or_above(double t)
 // Everything a block needs beyond its own data depends only on its E4M3 scale
 // byte S (0..0x7E), so each workgroup tabulates it once, for all 128 bytes, in
 // LDS.  Entry for S (8 dwords, 32 bytes):
-//   [0]  r = 1 / sq (binary32 bits), the multiplier of the fast path; the sign
+//   [0]  r ~ 1 / sq (binary32 bits), the multiplier of the fast path; the sign
 //        bit is set when the fast path is NOT exact under this S
 //   [1]  sd = decode(S) / gs (binary32 bits), the factor of the outputs
 //   [2]  t4 | t4<<16    [3] t6 | t6<<16    [4] (t2-t6) | (t2-t6)<<16
@@ -269,6 +269,12 @@ __device__ __forceinline__ uint32_t first_at_or_above(double t)
 // input; an S that fails (or whose t0 is not 1) keeps the threshold path.
 constexpr int kEntryWords = 8;
 constexpr uint32_t kNotFast = 0x80000000u;
+// How far (in ulps) the table build looks for a multiplier that passes the
+// check when 1 / sq does not.  With 1 / sq rounded, about 1% of (gs, S) pairs
+// fail, and on some tensors those are the common scale bytes (a third of the
+// blocks of the c4 activations); one ulp either way fixes all that do not sit
+// on an exact tie, which no multiplier can fix.
+constexpr int kMultiplierSteps = 2;
 
 __device__ __forceinline__ float bf16_value(uint32_t bits) { return __uint_as_float(bits << 16); }
 
@@ -298,13 +304,21 @@ __device__ void build_entry(uint32_t s, float gs, uint32_t* dst)
     const uint32_t t5 = first_above((2.5 + 0x1p-23) * q);
     const uint32_t t6 = first_at_or_above((3.5 - 0x1p-23) * q);
     const uint32_t t7 = first_above((5.0 + 0x1p-22) * q);
-    const float r = 1.0f / sq;
-    const bool fast = t0 == 1u &&
-                      fast_agrees(t1, r, 0.25f, true) && fast_agrees(t2, r, 0.75f, false) &&
-                      fast_agrees(t3, r, 1.25f, true) && fast_agrees(t4, r, 1.75f, false) &&
-                      fast_agrees(t5, r, 2.5f, true) && fast_agrees(t6, r, 3.5f, false) &&
-                      fast_agrees(t7, r, 5.0f, true);
-    dst[0] = __float_as_uint(r) | (fast ? 0u : kNotFast);
+    // The multiplier: 1 / sq rounded, or, when that one fails the check, the
+    // nearest binary32 neighbour that passes it (up to kMultiplierSteps ulps
+    // away; any multiplier that passes gives the exact codes).
+    const uint32_t r0 = __float_as_uint(1.0f / sq);
+    uint32_t r = r0;
+    bool fast = false;
+    for (int k = 0; t0 == 1u && !fast && k <= 2 * kMultiplierSteps; ++k) {
+        r = r0 + (uint32_t)((k + 1) / 2 * ((k & 1) ? 1 : -1));      // 0, +1, -1, +2, -2, ...
+        const float rf = __uint_as_float(r);
+        fast = fast_agrees(t1, rf, 0.25f, true) && fast_agrees(t2, rf, 0.75f, false) &&
+               fast_agrees(t3, rf, 1.25f, true) && fast_agrees(t4, rf, 1.75f, false) &&
+               fast_agrees(t5, rf, 2.5f, true) && fast_agrees(t6, rf, 3.5f, false) &&
+               fast_agrees(t7, rf, 5.0f, true);
+    }
+    dst[0] = (fast ? r : r0) | (fast ? 0u : kNotFast);
     dst[1] = __float_as_uint(sd);
     dst[2] = t4 * 0x10001u;
     dst[3] = t6 * 0x10001u;

@@ -252,8 +252,12 @@ def threshold_sweep(amax_value):
     return np.concatenate(blocks)
 
 
-@pytest.mark.parametrize("amax_value", [2.625, 2688.0 / 16, 1.0, 0.37, 1.7e-5, 12345.6, 5e20, 3e-11])
+@pytest.mark.parametrize("amax_value", [2.625, 2688.0 / 16, 1.0, 0.37, 1.7e-5, 12345.6, 5e20, 3e-11,
+                                        196.0, 5.5, 1000.0, 7.0])
 def test_every_magnitude_around_every_threshold(amax_value):
+    """The last four amax values give global scales under which 1 / sq rounded fails
+    the fast-path check for 14-47 of the 126 scale bytes, so the kernels use a
+    neighbouring multiplier there (196 is the c4 activations' amax)."""
     a = float(np.float32(amax_value))
     x = threshold_sweep(a)
     check_all_ops(x, amax_in=a, what="threshold sweep")
