@@ -213,6 +213,22 @@ def secondary(nv, synth, np, torch, dev, reps=20):
     n, k = wc.shape
     packed, scales, gsc = nv.nvfp4_quantize_pack(wc)
     wdq = nv.nvfp4_dequant_unpack(packed, scales, gsc)
+    # one rank's shard of the c5 weight under 8-way row sharding: with the all-reduced
+    # amax given, the shard runs the cached-amax calls (the exchange itself is one fp32)
+    sh = wc[: n // 8]
+    amax_all = nv.nvfp4_amax(wc)
+    ysh = torch.empty_like(sh)
+    psh = torch.empty((sh.shape[0], k // 2), dtype=torch.uint8, device=dev)
+    ssh = torch.empty((sh.shape[0], k // 16), dtype=torch.uint8, device=dev)
+    gsh = torch.empty(1, dtype=torch.float32, device=dev)
+    out["c5_row_shard_3584x8192_cached_fake_quant"] = timed(
+        lambda: nv.nvfp4_fake_quant(sh, y=ysh, amax_in=amax_all), 4.0 * sh.numel())
+    out["c5_row_shard_3584x8192_cached_quantize_pack"] = timed(
+        lambda: nv.nvfp4_quantize_pack(sh, amax_in=amax_all, packed=psh, scales=ssh, global_scale=gsh),
+        2.5625 * sh.numel())
+    out["c5_row_shard_3584x8192_dequant_unpack"] = timed(
+        lambda: nv.nvfp4_dequant_unpack(psh, ssh, gsh, y=ysh), 2.5625 * sh.numel())
+    del sh, ysh, psh, ssh
     # the fused calls on the c5 weight through the workspace (the step above uses
     # the three-launch form, whose quantizing kernel the roofline times alone)
     yc = torch.empty_like(wc)

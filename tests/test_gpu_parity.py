@@ -142,6 +142,37 @@ def test_c5_large_weight_full_path():
     assert_same(host(y)[rows], oracle.fake_quant(w[rows], a), "c5 fake-quant rows")
 
 
+def test_c5_row_shards_with_the_all_reduced_amax():
+    """c5 under 8-way row sharding ([3584, 8192] per rank), the part one GPU can show:
+    each shard's amax, their maximum (the all-reduce), then each shard quantized with
+    it through the cached-amax calls gives exactly the rows of the whole tensor's
+    result."""
+    w = synth.c5_weight()
+    say("c5 row shards %s" % (w.shape,))
+    xt = dev(w)
+    packed, scales, gs = nv.nvfp4_quantize_pack(xt)
+    y = nv.nvfp4_fake_quant(xt)
+    rows = w.shape[0] // 8
+    shard_amax = [nv.nvfp4_amax(xt[r * rows:(r + 1) * rows]) for r in range(8)]
+    global_amax = scalar(-1.0)
+    for a in shard_amax:                       # the MAX all-reduce of one fp32 per rank
+        torch.maximum(global_amax, a, out=global_amax)
+    torch.cuda.synchronize()
+    assert fbits(global_amax.item()) == fbits(oracle.amax(w))
+    for r in (0, 3, 7):
+        shard = xt[r * rows:(r + 1) * rows]
+        p_s, s_s, g_s = nv.nvfp4_quantize_pack(shard, amax_in=global_amax)
+        y_s = nv.nvfp4_fake_quant(shard, amax_in=global_amax)
+        torch.cuda.synchronize()
+        assert fbits(g_s.item()) == fbits(gs.item())
+        assert torch.equal(p_s, packed[r * rows:(r + 1) * rows])
+        assert torch.equal(s_s, scales[r * rows:(r + 1) * rows])
+        assert torch.equal(y_s.view(torch.int16), y[r * rows:(r + 1) * rows].view(torch.int16))
+    sample = sample_rows(rows, 7, k=14)
+    shard7 = w[7 * rows:]
+    assert_same(host(y)[7 * rows:][sample], oracle.fake_quant(shard7[sample], oracle.amax(w)), "shard 7 rows")
+
+
 # ---------------------------------------------------------------- edge tensors
 
 @pytest.mark.parametrize("shape", [(1, 1), (3, 7), (5, 15), (4, 17), (33, 40), (9, 1000), (2, 4097),
