@@ -24,7 +24,7 @@ Prints one JSON line on stdout (logs go to stderr):
   secondary     per-call-sequence times on the other workloads (fused siblings,
                 the activation step with its observers, the mid-size weight)
                 and the packed c5 weight used as a linear layer; --no-secondary
-                skips them
+                skips them, --secondary-only NAME runs only the matching ones
 """
 import argparse
 import hashlib
@@ -106,8 +106,11 @@ def cpu_baseline(x, rows):
     }
 
 
-def secondary(nv, synth, np, torch, dev, reps=20):
-    """Per-call throughput on the other workloads (not part of the headline step)."""
+def secondary(nv, synth, np, torch, dev, reps=20, only=None):
+    """Per-call throughput on the other workloads (not part of the headline step).
+
+    only: run just the lines whose name contains this string (and set up just their
+    workloads), for profiling one workload's calls."""
     stream = torch.cuda.current_stream(dev)
     out = {}
 
@@ -125,131 +128,145 @@ def secondary(nv, synth, np, torch, dev, reps=20):
         return {"us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
                 "pct_of_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
 
+    def line(name, fn, nbytes):
+        if only is None or only in name:
+            out[name] = timed(fn, nbytes)
+
+    def group(prefix):
+        return only is None or only.startswith(prefix) or prefix.startswith(only)
+
     def to_dev(a):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    # c3: shared amax of fused QKV siblings in one launch, then a fake-quant of each
-    sibs = [to_dev(a) for a in synth.c3_siblings()]
-    ys = [torch.empty_like(t) for t in sibs]
-    shared = torch.empty(1, dtype=torch.float32, device=dev)
-    n3 = sum(t.numel() for t in sibs)
-
-    def c3():
-        nv.nvfp4_amax(sibs, amax=shared)
-        for t, y in zip(sibs, ys):
-            nv.nvfp4_fake_quant(t, y=y, amax_in=shared)
-    out["c3_qkv_shared_amax_fake_quant"] = timed(c3, 6.0 * n3)
-    out["c3_qkv_group_fake_quant_one_launch"] = timed(
-        lambda: nv.nvfp4_fake_quant_group(sibs, ys=ys, amax_out=shared), 6.0 * n3)
-    del sibs, ys
-
-    # c4 activation step: amax, both observers, a fake-quant with each observer's amax
-    x = to_dev(synth.c4_activation(0))
-    y1, y2 = torch.empty_like(x), torch.empty_like(x)
-    cur = torch.empty(1, dtype=torch.float32, device=dev)
-    st_s = torch.full((1,), -1.0, dtype=torch.float32, device=dev)
-    st_e = torch.full((1,), -1.0, dtype=torch.float32, device=dev)
-
-    def c4act():
-        nv.nvfp4_amax(x, amax=cur)
-        nv.nvfp4_observer_update(st_s, cur, nv.OBS_STATIC_MINMAX)
-        nv.nvfp4_observer_update(st_e, cur, nv.OBS_EMA, 0.01)
-        nv.nvfp4_fake_quant(x, y=y1, amax_in=st_s)
-        nv.nvfp4_fake_quant(x, y=y2, amax_in=st_e)
-    out["c4_activation_step_8192x4096"] = timed(c4act, 10.0 * x.numel())
-
-    def c4act_dual():
-        nv.nvfp4_amax(x, amax=cur)
-        nv.nvfp4_observer_update(st_s, cur, nv.OBS_STATIC_MINMAX)
-        nv.nvfp4_observer_update(st_e, cur, nv.OBS_EMA, 0.01)
-        nv.nvfp4_fake_quant_dual(x, st_s, st_e, y0=y1, y1=y2)
-    # same outputs from one read of x: 8 bytes per element of traffic instead of 10
-    out["c4_activation_step_dual_fake_quant"] = timed(c4act_dual, 8.0 * x.numel())
-    # the same step as one call: 4 launches (reset, amax, both observer steps, dual
-    # fake-quant) instead of 5
-    out["c4_activation_step_observe_fake_quant"] = timed(
-        lambda: nv.nvfp4_observe_fake_quant(x, st_s, nv.OBS_STATIC_MINMAX, 0.0, st_e, nv.OBS_EMA, 0.01,
-                                            y0=y1, y1=y2, cur=cur), 8.0 * x.numel())
-    out["c4_activation_cached_fake_quant"] = timed(lambda: nv.nvfp4_fake_quant(x, y=y1, amax_in=st_s),
-                                                   4.0 * x.numel())
-    out["c4_activation_fused_amax_fake_quant"] = timed(
-        lambda: nv.nvfp4_fake_quant(x, y=y1, amax_out=cur), 6.0 * x.numel())
-    pa = torch.empty((x.shape[0], x.shape[1] // 2), dtype=torch.uint8, device=dev)
-    sa = torch.empty((x.shape[0], x.shape[1] // 16), dtype=torch.uint8, device=dev)
-    ga = torch.empty(1, dtype=torch.float32, device=dev)
-    out["c4_activation_fused_amax_quantize_pack"] = timed(
-        lambda: nv.nvfp4_quantize_pack(x, amax_out=cur, packed=pa, scales=sa, global_scale=ga), 4.5625 * x.numel())
-    # the fused calls through a workspace: no clearing launch, no atomics
     ws = nv.new_workspace(dev)
-    out["c4_activation_fused_amax_fake_quant_ws"] = timed(
-        lambda: nv.nvfp4_fake_quant_ws(x, y=y1, amax_out=cur, workspace=ws), 6.0 * x.numel())
-    out["c4_activation_fused_amax_quantize_pack_ws"] = timed(
-        lambda: nv.nvfp4_quantize_pack_ws(x, amax_out=cur, packed=pa, scales=sa, global_scale=ga, workspace=ws),
-        4.5625 * x.numel())
-    del pa, sa
-    del x, y1, y2
 
-    w = to_dev(synth.c4_weight())
-    yw = torch.empty_like(w)
-    aw = torch.empty(1, dtype=torch.float32, device=dev)
-    out["c4_weight_fused_amax_fake_quant_14336x4096"] = timed(
-        lambda: nv.nvfp4_fake_quant(w, y=yw, amax_out=aw), 6.0 * w.numel())
-    pk = torch.empty((w.shape[0], w.shape[1] // 2), dtype=torch.uint8, device=dev)
-    sc = torch.empty((w.shape[0], w.shape[1] // 16), dtype=torch.uint8, device=dev)
-    gsw = torch.empty(1, dtype=torch.float32, device=dev)
-    out["c4_weight_fused_amax_quantize_pack_14336x4096"] = timed(
-        lambda: nv.nvfp4_quantize_pack(w, amax_out=aw, packed=pk, scales=sc, global_scale=gsw),
-        4.5625 * w.numel())
-    out["c4_weight_fused_amax_fake_quant_ws"] = timed(
-        lambda: nv.nvfp4_fake_quant_ws(w, y=yw, amax_out=aw, workspace=ws), 6.0 * w.numel())
-    out["c4_weight_fused_amax_quantize_pack_ws"] = timed(
-        lambda: nv.nvfp4_quantize_pack_ws(w, amax_out=aw, packed=pk, scales=sc, global_scale=gsw, workspace=ws),
-        4.5625 * w.numel())
-    del w, yw, pk, sc
+    if group("c3_"):
+        # c3: shared amax of fused QKV siblings in one launch, then a fake-quant of each
+        sibs = [to_dev(a) for a in synth.c3_siblings()]
+        ys = [torch.empty_like(t) for t in sibs]
+        shared = torch.empty(1, dtype=torch.float32, device=dev)
+        n3 = sum(t.numel() for t in sibs)
 
-    # the c5 weight used as a linear layer (packed once), against unpack + torch's bf16 GEMM
-    # and torch's bf16 GEMM on an already unpacked weight (the two on torch are context only)
-    wc = to_dev(synth.c5_weight())
-    n, k = wc.shape
-    packed, scales, gsc = nv.nvfp4_quantize_pack(wc)
-    wdq = nv.nvfp4_dequant_unpack(packed, scales, gsc)
-    # one rank's shard of the c5 weight under 8-way row sharding: with the all-reduced
-    # amax given, the shard runs the cached-amax calls (the exchange itself is one fp32)
-    sh = wc[: n // 8]
-    amax_all = nv.nvfp4_amax(wc)
-    ysh = torch.empty_like(sh)
-    psh = torch.empty((sh.shape[0], k // 2), dtype=torch.uint8, device=dev)
-    ssh = torch.empty((sh.shape[0], k // 16), dtype=torch.uint8, device=dev)
-    gsh = torch.empty(1, dtype=torch.float32, device=dev)
-    out["c5_row_shard_3584x8192_cached_fake_quant"] = timed(
-        lambda: nv.nvfp4_fake_quant(sh, y=ysh, amax_in=amax_all), 4.0 * sh.numel())
-    out["c5_row_shard_3584x8192_cached_quantize_pack"] = timed(
-        lambda: nv.nvfp4_quantize_pack(sh, amax_in=amax_all, packed=psh, scales=ssh, global_scale=gsh),
-        2.5625 * sh.numel())
-    out["c5_row_shard_3584x8192_dequant_unpack"] = timed(
-        lambda: nv.nvfp4_dequant_unpack(psh, ssh, gsh, y=ysh), 2.5625 * sh.numel())
-    del sh, ysh, psh, ssh
-    # the fused calls on the c5 weight through the workspace (the step above uses
-    # the three-launch form, whose quantizing kernel the roofline times alone)
-    yc = torch.empty_like(wc)
-    pc = torch.empty_like(packed)
-    scc = torch.empty_like(scales)
-    ac, gc = torch.empty(1, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.float32, device=dev)
-    out["c5_weight_fused_amax_fake_quant_ws"] = timed(
-        lambda: nv.nvfp4_fake_quant_ws(wc, y=yc, amax_out=ac, workspace=ws), 6.0 * wc.numel())
-    out["c5_weight_fused_amax_quantize_pack_ws"] = timed(
-        lambda: nv.nvfp4_quantize_pack_ws(wc, amax_out=ac, packed=pc, scales=scc, global_scale=gc, workspace=ws),
-        4.5625 * wc.numel())
-    del wc, yc, pc, scc
-    gen = torch.Generator(device="cpu").manual_seed(7)
-    for m in (1, 16, 64):
-        xm = torch.randn(m, k, generator=gen).to(torch.bfloat16).to(dev)
-        ym = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
-        line = timed(lambda: nv.nvfp4_linear(xm, packed, scales, gsc, y=ym), n * k * 0.5625 + 2.0 * m * (k + n))
-        line["unpack_plus_torch_gemm_us"] = timed(
-            lambda: torch.nn.functional.linear(xm, nv.nvfp4_dequant_unpack(packed, scales, gsc, y=wdq)), 1.0)["us"]
-        line["torch_bf16_gemm_us"] = timed(lambda: torch.nn.functional.linear(xm, wdq), 1.0)["us"]
-        out["c5_weight_linear_%dx8192_by_28672x8192" % m] = line
+        def c3():
+            nv.nvfp4_amax(sibs, amax=shared)
+            for t, y in zip(sibs, ys):
+                nv.nvfp4_fake_quant(t, y=y, amax_in=shared)
+        line("c3_qkv_shared_amax_fake_quant", c3, 6.0 * n3)
+        line("c3_qkv_group_fake_quant_one_launch",
+             lambda: nv.nvfp4_fake_quant_group(sibs, ys=ys, amax_out=shared), 6.0 * n3)
+        del sibs, ys
+
+    if group("c4_activation"):
+        # c4 activation step: amax, both observers, a fake-quant with each observer's amax
+        x = to_dev(synth.c4_activation(0))
+        n4 = x.numel()
+        y1, y2 = torch.empty_like(x), torch.empty_like(x)
+        cur = torch.empty(1, dtype=torch.float32, device=dev)
+        st_s = torch.full((1,), -1.0, dtype=torch.float32, device=dev)
+        st_e = torch.full((1,), -1.0, dtype=torch.float32, device=dev)
+
+        def c4act():
+            nv.nvfp4_amax(x, amax=cur)
+            nv.nvfp4_observer_update(st_s, cur, nv.OBS_STATIC_MINMAX)
+            nv.nvfp4_observer_update(st_e, cur, nv.OBS_EMA, 0.01)
+            nv.nvfp4_fake_quant(x, y=y1, amax_in=st_s)
+            nv.nvfp4_fake_quant(x, y=y2, amax_in=st_e)
+        line("c4_activation_step_8192x4096", c4act, 10.0 * n4)
+
+        def c4act_dual():
+            nv.nvfp4_amax(x, amax=cur)
+            nv.nvfp4_observer_update(st_s, cur, nv.OBS_STATIC_MINMAX)
+            nv.nvfp4_observer_update(st_e, cur, nv.OBS_EMA, 0.01)
+            nv.nvfp4_fake_quant_dual(x, st_s, st_e, y0=y1, y1=y2)
+        # same outputs from one read of x: 8 bytes per element of traffic instead of 10
+        line("c4_activation_step_dual_fake_quant", c4act_dual, 8.0 * n4)
+        # the same step as one call: 4 launches (reset, amax, both observer steps, dual
+        # fake-quant) instead of 5
+        line("c4_activation_step_observe_fake_quant",
+             lambda: nv.nvfp4_observe_fake_quant(x, st_s, nv.OBS_STATIC_MINMAX, 0.0, st_e, nv.OBS_EMA, 0.01,
+                                                 y0=y1, y1=y2, cur=cur), 8.0 * n4)
+        line("c4_activation_cached_fake_quant", lambda: nv.nvfp4_fake_quant(x, y=y1, amax_in=st_s), 4.0 * n4)
+        line("c4_activation_fused_amax_fake_quant", lambda: nv.nvfp4_fake_quant(x, y=y1, amax_out=cur), 6.0 * n4)
+        pa = torch.empty((x.shape[0], x.shape[1] // 2), dtype=torch.uint8, device=dev)
+        sa = torch.empty((x.shape[0], x.shape[1] // 16), dtype=torch.uint8, device=dev)
+        ga = torch.empty(1, dtype=torch.float32, device=dev)
+        line("c4_activation_fused_amax_quantize_pack",
+             lambda: nv.nvfp4_quantize_pack(x, amax_out=cur, packed=pa, scales=sa, global_scale=ga), 4.5625 * n4)
+        # the fused calls through a workspace: no clearing launch, no atomics
+        line("c4_activation_fused_amax_fake_quant_ws",
+             lambda: nv.nvfp4_fake_quant_ws(x, y=y1, amax_out=cur, workspace=ws), 6.0 * n4)
+        line("c4_activation_fused_amax_quantize_pack_ws",
+             lambda: nv.nvfp4_quantize_pack_ws(x, amax_out=cur, packed=pa, scales=sa, global_scale=ga,
+                                               workspace=ws), 4.5625 * n4)
+        del pa, sa, x, y1, y2
+
+    if group("c4_weight"):
+        w = to_dev(synth.c4_weight())
+        nw = w.numel()
+        yw = torch.empty_like(w)
+        aw = torch.empty(1, dtype=torch.float32, device=dev)
+        pk = torch.empty((w.shape[0], w.shape[1] // 2), dtype=torch.uint8, device=dev)
+        sc = torch.empty((w.shape[0], w.shape[1] // 16), dtype=torch.uint8, device=dev)
+        gsw = torch.empty(1, dtype=torch.float32, device=dev)
+        line("c4_weight_fused_amax_fake_quant_14336x4096",
+             lambda: nv.nvfp4_fake_quant(w, y=yw, amax_out=aw), 6.0 * nw)
+        line("c4_weight_fused_amax_quantize_pack_14336x4096",
+             lambda: nv.nvfp4_quantize_pack(w, amax_out=aw, packed=pk, scales=sc, global_scale=gsw), 4.5625 * nw)
+        line("c4_weight_fused_amax_fake_quant_ws",
+             lambda: nv.nvfp4_fake_quant_ws(w, y=yw, amax_out=aw, workspace=ws), 6.0 * nw)
+        line("c4_weight_fused_amax_quantize_pack_ws",
+             lambda: nv.nvfp4_quantize_pack_ws(w, amax_out=aw, packed=pk, scales=sc, global_scale=gsw,
+                                               workspace=ws), 4.5625 * nw)
+        del w, yw, pk, sc
+
+    if group("c5_"):
+        wc = to_dev(synth.c5_weight())
+        n, k = wc.shape
+        # one rank's shard of the c5 weight under 8-way row sharding: with the all-reduced
+        # amax given, the shard runs the cached-amax calls (the exchange itself is one fp32)
+        sh = wc[: n // 8]
+        amax_all = nv.nvfp4_amax(wc)
+        ysh = torch.empty_like(sh)
+        psh = torch.empty((sh.shape[0], k // 2), dtype=torch.uint8, device=dev)
+        ssh = torch.empty((sh.shape[0], k // 16), dtype=torch.uint8, device=dev)
+        gsh = torch.empty(1, dtype=torch.float32, device=dev)
+        line("c5_row_shard_3584x8192_cached_fake_quant",
+             lambda: nv.nvfp4_fake_quant(sh, y=ysh, amax_in=amax_all), 4.0 * sh.numel())
+        line("c5_row_shard_3584x8192_cached_quantize_pack",
+             lambda: nv.nvfp4_quantize_pack(sh, amax_in=amax_all, packed=psh, scales=ssh, global_scale=gsh),
+             2.5625 * sh.numel())
+        line("c5_row_shard_3584x8192_dequant_unpack",
+             lambda: nv.nvfp4_dequant_unpack(psh, ssh, gsh, y=ysh), 2.5625 * sh.numel())
+        del sh, ysh, psh, ssh
+        # the fused calls on the c5 weight through the workspace (the step uses the
+        # three-launch form, whose quantizing kernel the roofline times alone)
+        yc = torch.empty_like(wc)
+        pc = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+        scc = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+        ac, gc = torch.empty(1, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.float32, device=dev)
+        line("c5_weight_fused_amax_fake_quant_ws",
+             lambda: nv.nvfp4_fake_quant_ws(wc, y=yc, amax_out=ac, workspace=ws), 6.0 * wc.numel())
+        line("c5_weight_fused_amax_quantize_pack_ws",
+             lambda: nv.nvfp4_quantize_pack_ws(wc, amax_out=ac, packed=pc, scales=scc, global_scale=gc,
+                                               workspace=ws), 4.5625 * wc.numel())
+        del yc, pc, scc
+        # the c5 weight used as a linear layer (packed once), against unpack + torch's bf16
+        # GEMM and torch's bf16 GEMM on an already unpacked weight (context only)
+        if only is None or only in "c5_weight_linear":
+            packed, scales, gsc = nv.nvfp4_quantize_pack(wc)
+            wdq = nv.nvfp4_dequant_unpack(packed, scales, gsc)
+            del wc
+            gen = torch.Generator(device="cpu").manual_seed(7)
+            for m in (1, 16, 64):
+                xm = torch.randn(m, k, generator=gen).to(torch.bfloat16).to(dev)
+                ym = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+                res = timed(lambda: nv.nvfp4_linear(xm, packed, scales, gsc, y=ym),
+                            n * k * 0.5625 + 2.0 * m * (k + n))
+                res["unpack_plus_torch_gemm_us"] = timed(
+                    lambda: torch.nn.functional.linear(xm, nv.nvfp4_dequant_unpack(packed, scales, gsc, y=wdq)),
+                    1.0)["us"]
+                res["torch_bf16_gemm_us"] = timed(lambda: torch.nn.functional.linear(xm, wdq), 1.0)["us"]
+                out["c5_weight_linear_%dx8192_by_28672x8192" % m] = res
     return out
 
 
@@ -263,6 +280,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=28672,
                     help="rows of the oracle's CPU sample (default: the whole c5 weight, ~13 s; 0: skip)")
     ap.add_argument("--no-secondary", action="store_true", help="skip the c3/c4 per-call lines")
+    ap.add_argument("--secondary-only", metavar="NAME", default=None,
+                    help="diagnostic mode: skip the step and run only the secondary lines whose name "
+                         "contains NAME (prints their JSON, not the bench line); for profiling")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -278,6 +298,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.secondary_only is not None:
+        print(json.dumps({"secondary": secondary(nv, synth, np, torch, dev, only=args.secondary_only)}),
+              flush=True)
+        return
     log("generating c5 weight %dx%d" % (args.rows, args.cols))
     x_host = synth.c5_weight(rows=args.rows, cols=args.cols)
     rows, cols = x_host.shape
