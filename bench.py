@@ -128,9 +128,30 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
         return {"us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
                 "pct_of_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
 
-    def line(name, fn, nbytes):
+    flush = torch.ones((1 << 30) // 4, dtype=torch.int32, device=dev)
+
+    def cold_us(fn, reps=9):
+        """Median time of single calls, each after a 1 GiB read has evicted the
+        Infinity Cache and the L2s (outside the events)."""
+        ts = []
+        for _ in range(reps):
+            flush.sum()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return round(sorted(ts)[len(ts) // 2], 2)
+
+    def line(name, fn, nbytes, cold=False):
         if only is None or only in name:
             out[name] = timed(fn, nbytes)
+            if cold:
+                c = cold_us(fn)
+                out[name]["cold_us"] = c
+                out[name]["cold_pct_of_hbm_peak"] = round(100 * nbytes / (c * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)
 
     def group(prefix):
         return only is None or only.startswith(prefix) or prefix.startswith(only)
@@ -186,18 +207,20 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
              lambda: nv.nvfp4_observe_fake_quant(x, st_s, nv.OBS_STATIC_MINMAX, 0.0, st_e, nv.OBS_EMA, 0.01,
                                                  y0=y1, y1=y2, cur=cur), 8.0 * n4)
         line("c4_activation_cached_fake_quant", lambda: nv.nvfp4_fake_quant(x, y=y1, amax_in=st_s), 4.0 * n4)
-        line("c4_activation_fused_amax_fake_quant", lambda: nv.nvfp4_fake_quant(x, y=y1, amax_out=cur), 6.0 * n4)
+        line("c4_activation_fused_amax_fake_quant", lambda: nv.nvfp4_fake_quant(x, y=y1, amax_out=cur), 6.0 * n4,
+             cold=True)
         pa = torch.empty((x.shape[0], x.shape[1] // 2), dtype=torch.uint8, device=dev)
         sa = torch.empty((x.shape[0], x.shape[1] // 16), dtype=torch.uint8, device=dev)
         ga = torch.empty(1, dtype=torch.float32, device=dev)
         line("c4_activation_fused_amax_quantize_pack",
-             lambda: nv.nvfp4_quantize_pack(x, amax_out=cur, packed=pa, scales=sa, global_scale=ga), 4.5625 * n4)
+             lambda: nv.nvfp4_quantize_pack(x, amax_out=cur, packed=pa, scales=sa, global_scale=ga), 4.5625 * n4,
+             cold=True)
         # the fused calls through a workspace: no clearing launch, no atomics
         line("c4_activation_fused_amax_fake_quant_ws",
-             lambda: nv.nvfp4_fake_quant_ws(x, y=y1, amax_out=cur, workspace=ws), 6.0 * n4)
+             lambda: nv.nvfp4_fake_quant_ws(x, y=y1, amax_out=cur, workspace=ws), 6.0 * n4, cold=True)
         line("c4_activation_fused_amax_quantize_pack_ws",
              lambda: nv.nvfp4_quantize_pack_ws(x, amax_out=cur, packed=pa, scales=sa, global_scale=ga,
-                                               workspace=ws), 4.5625 * n4)
+                                               workspace=ws), 4.5625 * n4, cold=True)
         del pa, sa, x, y1, y2
 
     if group("c4_weight"):
@@ -209,14 +232,15 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
         sc = torch.empty((w.shape[0], w.shape[1] // 16), dtype=torch.uint8, device=dev)
         gsw = torch.empty(1, dtype=torch.float32, device=dev)
         line("c4_weight_fused_amax_fake_quant_14336x4096",
-             lambda: nv.nvfp4_fake_quant(w, y=yw, amax_out=aw), 6.0 * nw)
+             lambda: nv.nvfp4_fake_quant(w, y=yw, amax_out=aw), 6.0 * nw, cold=True)
         line("c4_weight_fused_amax_quantize_pack_14336x4096",
-             lambda: nv.nvfp4_quantize_pack(w, amax_out=aw, packed=pk, scales=sc, global_scale=gsw), 4.5625 * nw)
+             lambda: nv.nvfp4_quantize_pack(w, amax_out=aw, packed=pk, scales=sc, global_scale=gsw), 4.5625 * nw,
+             cold=True)
         line("c4_weight_fused_amax_fake_quant_ws",
-             lambda: nv.nvfp4_fake_quant_ws(w, y=yw, amax_out=aw, workspace=ws), 6.0 * nw)
+             lambda: nv.nvfp4_fake_quant_ws(w, y=yw, amax_out=aw, workspace=ws), 6.0 * nw, cold=True)
         line("c4_weight_fused_amax_quantize_pack_ws",
              lambda: nv.nvfp4_quantize_pack_ws(w, amax_out=aw, packed=pk, scales=sc, global_scale=gsw,
-                                               workspace=ws), 4.5625 * nw)
+                                               workspace=ws), 4.5625 * nw, cold=True)
         del w, yw, pk, sc
 
     if group("c5_"):
