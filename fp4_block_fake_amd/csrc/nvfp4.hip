@@ -1298,27 +1298,37 @@ nvfp4_status launched()
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-// Enqueue max|x| of up to NVFP4_AMAX_GROUP_MAX tensors into *amax (atomic max).
-nvfp4_status enqueue_amax(const void* const* xs, const int64_t* numels, int n, float* amax,
-                          hipStream_t stream)
+// The amax pass's description of up to NVFP4_AMAX_GROUP_MAX tensors; *chunks
+// receives the number of chunks it walks.
+AmaxGroup amax_group(const void* const* xs, const int64_t* numels, int n, int64_t* chunks)
 {
     AmaxGroup g{};
     constexpr int64_t kChunk = (int64_t)kThreads * kAmaxUnroll;
-    int64_t chunks = 0;
+    int64_t c = 0;
     g.count = n;
     for (int i = 0; i < n; ++i) {
         g.vec[i] = static_cast<const uint4*>(xs[i]);
         g.nvec[i] = numels[i] / 8;
         g.tail[i] = static_cast<const uint16_t*>(xs[i]) + (numels[i] & ~(int64_t)7);
         g.ntail[i] = (int32_t)(numels[i] & 7);
-        chunks += (g.nvec[i] + kChunk - 1) / kChunk;
-        g.chunk_end[i] = chunks;
+        c += (g.nvec[i] + kChunk - 1) / kChunk;
+        g.chunk_end[i] = c;
     }
     // Only the last NVFP4_AMAX_ALLOC_BYTES of the group are read with allocating
     // loads: that is what the Infinity Cache still holds when the quantizing pass
     // over the same tensor gets there; the rest streams past the caches.
     const int64_t alloc_chunks = (int64_t)NVFP4_AMAX_ALLOC_BYTES / (kChunk * 16);
-    g.alloc_from = chunks > alloc_chunks ? chunks - alloc_chunks : 0;
+    g.alloc_from = c > alloc_chunks ? c - alloc_chunks : 0;
+    *chunks = c;
+    return g;
+}
+
+// Enqueue max|x| of up to NVFP4_AMAX_GROUP_MAX tensors into *amax (atomic max).
+nvfp4_status enqueue_amax(const void* const* xs, const int64_t* numels, int n, float* amax,
+                          hipStream_t stream)
+{
+    int64_t chunks;
+    const AmaxGroup g = amax_group(xs, numels, n, &chunks);
     k_amax<false><<<persistent_grid(chunks, 1, NVFP4_AMAX_WG_PER_CU), kThreads, 0, stream>>>(g, amax, nullptr);
     return launched();
 }
@@ -1385,7 +1395,6 @@ nvfp4_status enqueue_fake_quant(const void* x, void* y, int64_t cols, const Matr
     return launched();
 }
 
-
 // One quantize-pack launch of a single tensor (also for an empty one: it still
 // writes the global scale).
 nvfp4_status enqueue_quantize_pack(const void* x, int64_t cols, const Matrix& m, uint8_t* packed, uint8_t* scales,
@@ -1415,17 +1424,8 @@ static_assert(kMaxPartials >= 2 * 256, "the workspace holds a partial per amax w
 // workgroup, which stores a zero partial.
 nvfp4_status enqueue_amax_ws(const void* x, int64_t numel, void* ws, float* amax, hipStream_t stream)
 {
-    AmaxGroup g{};
-    constexpr int64_t kChunk = (int64_t)kThreads * kAmaxUnroll;
-    g.count = 1;
-    g.vec[0] = static_cast<const uint4*>(x);
-    g.nvec[0] = numel / 8;
-    g.tail[0] = static_cast<const uint16_t*>(x) + (numel & ~(int64_t)7);
-    g.ntail[0] = (int32_t)(numel & 7);
-    const int64_t chunks = (g.nvec[0] + kChunk - 1) / kChunk;
-    g.chunk_end[0] = chunks;
-    const int64_t alloc_chunks = (int64_t)NVFP4_AMAX_ALLOC_BYTES / (kChunk * 16);
-    g.alloc_from = chunks > alloc_chunks ? chunks - alloc_chunks : 0;
+    int64_t chunks;
+    const AmaxGroup g = amax_group(&x, &numel, 1, &chunks);
     unsigned grid = persistent_grid(chunks, 1, NVFP4_AMAX_WG_PER_CU);
     if (grid > (unsigned)kMaxPartials)
         grid = (unsigned)kMaxPartials;
