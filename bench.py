@@ -281,7 +281,7 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
             wdq = nv.nvfp4_dequant_unpack(packed, scales, gsc)
             del wc
             gen = torch.Generator(device="cpu").manual_seed(7)
-            for m in (1, 16, 64):
+            for m in (1, 16, 64, 128, 256, 1024):
                 xm = torch.randn(m, k, generator=gen).to(torch.bfloat16).to(dev)
                 ym = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
                 res = timed(lambda: nv.nvfp4_linear(xm, packed, scales, gsc, y=ym),

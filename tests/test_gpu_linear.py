@@ -92,9 +92,13 @@ def test_linear_within_the_rounding_bound(m, n, k, with_bias):
 
 # Launch shapes the tile choice reaches: 256-wide steps whose scale bytes are not 4-byte
 # aligned (k % 64 == 32, up to 16 rows of x), one workgroup per CU for widths n = 4096 c
-# (c tiles of 16 weight rows per workgroup, c = 1, 3, 5, 8), and several 16-row tiles of x.
+# (c tiles of 16 weight rows per workgroup, c = 1, 3, 5, 8), several 16-row tiles of x,
+# and the tiled kernel from 65 rows of x (64- and 128-row tiles, 32- and 64-wide K steps,
+# ragged rows of x and a width that is not a multiple of the 128-row weight tile).
 @pytest.mark.parametrize("m,n,k", [(5, 40, 288), (16, 130, 800), (4, 12288, 256), (2, 20480, 128),
-                                   (64, 32768, 64), (33, 4096, 96), (48, 8192, 160)])
+                                   (64, 32768, 64), (33, 4096, 96), (48, 8192, 160),
+                                   (129, 256, 1024), (300, 200, 2048), (1024, 520, 256), (128, 4096, 4096),
+                                   (128, 96, 192)])
 def test_linear_launch_shapes(m, n, k):
     packed, scales, gs = weight(n, k, 11 * m + n + k)
     rng = np.random.default_rng(m * 5 + n + k)
