@@ -112,21 +112,23 @@ def test_linear_launch_shapes(m, n, k):
 
 def test_c5_weight_as_a_layer():
     """The c5 weight (28672 x 8192) quantized on the device, then used as a linear layer
-    on 16 tokens; sampled output columns are checked against the oracle."""
+    on 16 tokens (the register-decode kernel) and on 256 tokens (the tiled kernel), the
+    shapes the bench times; sampled output columns are checked against the oracle."""
     w = synth.c5_weight()
     say("linear on the c5 weight")
     packed, scales, gs = nv.nvfp4_quantize_pack(dev(w))
     rng = np.random.default_rng(55)
-    x = synth.to_bf16_bits(rng.standard_normal((16, w.shape[1])).astype(np.float32))
-    y = nv.nvfp4_linear(dev(x), packed, scales, gs)
-    torch.cuda.synchronize()
     cols = np.unique(np.concatenate([[0, w.shape[0] - 1], rng.choice(w.shape[0], 62, replace=False)]))
     p_rows, s_rows = packed.cpu().numpy()[cols], scales.cpu().numpy()[cols]
     g = float(gs.item())
     p_ref, s_ref, g_ref = oracle.quantize(w[cols], oracle.amax(w))
     assert_same(p_rows, p_ref, "c5 packed rows")
     assert_same(s_rows, s_ref, "c5 scale rows")
-    check_bound(host(y)[:, cols], x, p_rows, s_rows, g, w.shape[1], None, "c5 sampled columns")
+    for m in (16, 256):
+        x = synth.to_bf16_bits(rng.standard_normal((m, w.shape[1])).astype(np.float32))
+        y = nv.nvfp4_linear(dev(x), packed, scales, gs)
+        torch.cuda.synchronize()
+        check_bound(host(y)[:, cols], x, p_rows, s_rows, g, w.shape[1], None, "c5 sampled columns, m=%d" % m)
 
 
 def test_empty_and_rejected_shapes():
