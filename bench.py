@@ -201,11 +201,11 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
             nv.nvfp4_fake_quant_dual(x, st_s, st_e, y0=y1, y1=y2)
         # same outputs from one read of x: 8 bytes per element of traffic instead of 10
         line("c4_activation_step_dual_fake_quant", c4act_dual, 8.0 * n4)
-        # the same step as one call: 4 launches (reset, amax, both observer steps, dual
-        # fake-quant) instead of 5
+        # the same step as one call: 3 launches (amax to partial maxima, their reduction
+        # with both observer steps, dual fake-quant) instead of 5
         line("c4_activation_step_observe_fake_quant",
              lambda: nv.nvfp4_observe_fake_quant(x, st_s, nv.OBS_STATIC_MINMAX, 0.0, st_e, nv.OBS_EMA, 0.01,
-                                                 y0=y1, y1=y2, cur=cur), 8.0 * n4)
+                                                 y0=y1, y1=y2, cur=cur, workspace=ws), 8.0 * n4)
         line("c4_activation_cached_fake_quant", lambda: nv.nvfp4_fake_quant(x, y=y1, amax_in=st_s), 4.0 * n4)
         line("c4_activation_fused_amax_fake_quant", lambda: nv.nvfp4_fake_quant(x, y=y1, amax_out=cur), 6.0 * n4,
              cold=True)

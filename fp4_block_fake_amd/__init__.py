@@ -54,7 +54,7 @@ def _load() -> ctypes.CDLL:
     so.nvfp4_linear.argtypes = [P, I64, I64, P, P, P, I64, P, P, P]
     so.nvfp4_observer_update.argtypes = [P, P, I, ctypes.c_float, P]
     F = ctypes.c_float
-    so.nvfp4_observe_fake_quant.argtypes = [P, I64, I64, P, P, I, F, P, P, I, F, P, P]
+    so.nvfp4_observe_fake_quant.argtypes = [P, I64, I64, P, P, I, F, P, P, I, F, P, P, P]
     so.nvfp4_fake_quant_ws.argtypes = [P, P, I64, I64, P, P, P]
     so.nvfp4_quantize_pack_ws.argtypes = [P, I64, I64, P, P, P, P, P, P]
     so.nvfp4_strerror.argtypes = [I]
@@ -283,9 +283,10 @@ def nvfp4_observe_fake_quant(x: torch.Tensor, state0: torch.Tensor, mode0: int =
                              decay0: float = 0.01, state1: torch.Tensor | None = None,
                              mode1: int = OBS_EMA, decay1: float = 0.01,
                              y0: torch.Tensor | None = None, y1: torch.Tensor | None = None,
-                             cur: torch.Tensor | None = None):
+                             cur: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """One activation step: cur = max|x|, each observer state steps on cur (in place),
-    and x is fake-quantized with each new state -> y0, or (y0, y1) with two observers."""
+    and x is fake-quantized with each new state -> y0, or (y0, y1) with two observers.
+    workspace: as for the *_ws calls (a fresh one when not given)."""
     rows, cols = _matrix(x, "x")
     dev = x.device
     _scalar(dev, state0)
@@ -298,9 +299,10 @@ def nvfp4_observe_fake_quant(x: torch.Tensor, state0: torch.Tensor, mode0: int =
     for name, y in (("y0", y0), ("y1", y1)):
         if y is not None and _matrix(y, name) != x.shape:
             raise ValueError("%s must have the shape of x" % name)
+    ws = _workspace(dev, workspace)
     _check(lib.nvfp4_observe_fake_quant(_ptr(x), rows, cols, _ptr(cur), _ptr(state0), int(mode0),
                                         float(decay0), _ptr(y0), _ptr(state1), int(mode1), float(decay1),
-                                        _ptr(y1), _stream(dev)), "nvfp4_observe_fake_quant")
+                                        _ptr(y1), _ptr(ws), _stream(dev)), "nvfp4_observe_fake_quant")
     return y0 if state1 is None else (y0, y1)
 
 

@@ -648,18 +648,6 @@ __global__ __launch_bounds__(kThreads) void k_amax(AmaxGroup g, float* out, uint
     }
 }
 
-// The amax from the partial maxima (bf16 magnitude bits) of the amax pass.
-__global__ __launch_bounds__(kThreads) void k_amax_finish(const uint32_t* partials, int count, float* amax)
-{
-    uint32_t m = 0;
-    for (int i = threadIdx.x; i < count; i += kThreads)
-        m = max(m, partials[i]);
-    __shared__ uint32_t wave_max[kThreads / 64];
-    const uint32_t r = workgroup_max(m, wave_max);
-    if (threadIdx.x == 0)
-        *amax = __uint_as_float(r << 16);
-}
-
 // The kUnroll half blocks of one iteration of a quantizing pass (zeros past the end).
 template <bool NtLd>
 __device__ __forceinline__ void load_halves(const uint4* x, int64_t base, int64_t nhalves,
@@ -1417,9 +1405,8 @@ struct ObserverArgs {
     float decay[2];
 };
 
-__global__ void k_observer(const float* cur, ObserverArgs o, int n)
+__device__ void observer_steps(float c, const ObserverArgs& o, int n)
 {
-    const float c = *cur;
     for (int i = 0; i < n; ++i) {
         const float s = *o.state[i];
         float r;
@@ -1434,6 +1421,28 @@ __global__ void k_observer(const float* cur, ObserverArgs o, int n)
             r = a + b;                             // no contraction: -ffp-contract=off
         }
         *o.state[i] = r;
+    }
+}
+
+__global__ void k_observer(const float* cur, ObserverArgs o, int n)
+{
+    observer_steps(*cur, o, n);
+}
+
+// The amax from the partial maxima (bf16 magnitude bits) of the amax pass, then
+// n observer steps on it (n = 0: none).
+__global__ __launch_bounds__(kThreads) void k_amax_finish(const uint32_t* partials, int count, float* amax,
+                                                          ObserverArgs o, int n)
+{
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < count; i += kThreads)
+        m = max(m, partials[i]);
+    __shared__ uint32_t wave_max[kThreads / 64];
+    const uint32_t r = workgroup_max(m, wave_max);
+    if (threadIdx.x == 0) {
+        const float v = __uint_as_float(r << 16);
+        *amax = v;
+        observer_steps(v, o, n);
     }
 }
 
@@ -1608,9 +1617,10 @@ constexpr int kMaxPartials = (int)((NVFP4_WORKSPACE_BYTES - kPartialsOffset) / 4
 static_assert(kMaxPartials >= 2 * 256, "the workspace holds a partial per amax workgroup");
 
 // Enqueue the amax of one tensor through the workspace: the amax pass in
-// partials mode, then their reduction into *amax.  An empty tensor gets one
-// workgroup, which stores a zero partial.
-nvfp4_status enqueue_amax_ws(const void* x, int64_t numel, void* ws, float* amax, hipStream_t stream)
+// partials mode, then their reduction into *amax, followed by nobs observer steps
+// on it.  An empty tensor gets one workgroup, which stores a zero partial.
+nvfp4_status enqueue_amax_ws(const void* x, int64_t numel, void* ws, float* amax, hipStream_t stream,
+                             const ObserverArgs& obs = ObserverArgs{}, int nobs = 0)
 {
     int64_t chunks;
     const AmaxGroup g = amax_group(&x, &numel, 1, &chunks);
@@ -1621,7 +1631,7 @@ nvfp4_status enqueue_amax_ws(const void* x, int64_t numel, void* ws, float* amax
     k_amax<true><<<grid, kThreads, 0, stream>>>(g, nullptr, partials);
     if (launched() != NVFP4_OK)
         return NVFP4_ERR_HIP;
-    k_amax_finish<<<1, kThreads, 0, stream>>>(partials, (int)grid, amax);
+    k_amax_finish<<<1, kThreads, 0, stream>>>(partials, (int)grid, amax, obs, nobs);
     return launched();
 }
 
@@ -2115,34 +2125,36 @@ nvfp4_status nvfp4_quantize_pack_ws(const void* x, int64_t rows, int64_t cols, f
 
 nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols, float* cur,
                                       float* state0, int mode0, float decay0, void* y0,
-                                      float* state1, int mode1, float decay1, void* y1, void* stream)
+                                      float* state1, int mode1, float decay1, void* y1, void* workspace,
+                                      void* stream)
 {
     Matrix m;
     nvfp4_status st = check_matrix(rows, cols, &m);
     if (st != NVFP4_OK)
         return st;
     const bool two = state1 != nullptr;
-    if (!cur || !state0 || (m.numel > 0 && (!x || !y0 || (two && !y1))))
+    if (!cur || !state0 || !workspace || (m.numel > 0 && (!x || !y0 || (two && !y1))))
         return NVFP4_ERR_NULL;
     if ((!two && y1) || !observer_args_ok(mode0, decay0) || (two && !observer_args_ok(mode1, decay1)))
         return NVFP4_ERR_ARG;
     if (!aligned(x, 16) || !aligned(y0, 16) || !aligned(y1, 16) || !aligned(cur, 4) || !aligned(state0, 4) ||
-        !aligned(state1, 4))
+        !aligned(state1, 4) || !aligned(workspace, 256))
         return NVFP4_ERR_ALIGN;
     const uint64_t bytes = 2 * (uint64_t)m.numel;
     const Region in[1] = {{x, bytes}};
-    const Region out[5] = {{y0, y0 ? bytes : 0u}, {y1, y1 ? bytes : 0u}, {cur, 4}, {state0, 4},
-                           {state1, two ? 4u : 0u}};
-    if (check_regions(in, 1, out, 5, true) != NVFP4_OK)
+    const Region out[6] = {{y0, y0 ? bytes : 0u}, {y1, y1 ? bytes : 0u}, {cur, 4}, {state0, 4},
+                           {state1, two ? 4u : 0u}, {workspace, NVFP4_WORKSPACE_BYTES}};
+    if (check_regions(in, 1, out, 6, true) != NVFP4_OK)
         return NVFP4_ERR_OVERLAP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    st = enqueue_amax_one(x, m.numel, cur, s);
-    if (st != NVFP4_OK)
-        return st;
-    k_observer<<<1, 1, 0, s>>>(cur, ObserverArgs{{state0, state1}, {mode0, mode1}, {decay0, decay1}}, two ? 2 : 1);
-    if ((st = launched()) != NVFP4_OK || m.numel == 0)
-        return st;
+    // the amax pass, then one workgroup reduces its partial maxima into *cur and
+    // steps both observers on it
+    const ObserverArgs obs{{state0, state1}, {mode0, mode1}, {decay0, decay1}};
+    if (enqueue_amax_ws(x, m.numel, workspace, cur, s, obs, two ? 2 : 1) != NVFP4_OK)
+        return NVFP4_ERR_HIP;
+    if (m.numel == 0)
+        return NVFP4_OK;
     if (!two)
         return enqueue_fake_quant(x, y0, cols, m, state0, s);
     if (m.ragged) {

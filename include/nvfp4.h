@@ -275,6 +275,10 @@ nvfp4_status nvfp4_quantize_pack_ws(const void* x, int64_t rows, int64_t cols, f
  *   state1, y1      second observer and its output, or both NULL for one
  *                   observer (y1 == x allowed when y0 != x)
  *   mode_i, decay_i as for nvfp4_observer_update
+ *   workspace       as for the workspace calls above (NVFP4_WORKSPACE_BYTES,
+ *                   256-byte aligned, caller-owned, contents irrelevant)
+ * Launches: the amax pass (partial maxima into the workspace), one workgroup
+ * that reduces them into *cur and steps the observers, and the fake-quant pass.
  * x, y0 and y1 may be NULL when rows == 0; the states still step on *cur = +0.
  * The amax is the local one: a data-parallel caller that all-reduces the step
  * amax before the observer update uses the separate calls instead.
@@ -284,7 +288,7 @@ nvfp4_status nvfp4_quantize_pack_ws(const void* x, int64_t rows, int64_t cols, f
 nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols, float* cur,
                                       float* state0, int mode0, float decay0, void* y0,
                                       float* state1, int mode1, float decay1, void* y1,
-                                      void* stream);
+                                      void* workspace, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* nvfp4_strerror(int status);

@@ -64,7 +64,7 @@ int main(void)
     bad |= nvfp4_dequant_unpack(0, 0, 0, 4, 16, 0, 0) != NVFP4_ERR_NULL;
     bad |= nvfp4_linear(0, 4, 48, 0, 0, 0, 8, 0, 0, 0) != NVFP4_ERR_SHAPE;
     bad |= nvfp4_observer_update(0, 0, NVFP4_OBS_EMA, 0.5f, 0) != NVFP4_ERR_NULL;
-    bad |= nvfp4_observe_fake_quant(0, 4, 16, 0, 0, 0, 0.0f, 0, 0, 0, 0.0f, 0, 0) != NVFP4_ERR_NULL;
+    bad |= nvfp4_observe_fake_quant(0, 4, 16, 0, 0, 0, 0.0f, 0, 0, 0, 0.0f, 0, 0, 0) != NVFP4_ERR_NULL;
     bad |= nvfp4_fake_quant_ws(0, 0, 4, 16, 0, 0, 0) != NVFP4_ERR_NULL;
     bad |= nvfp4_quantize_pack_ws(0, 4, 0, 0, 0, 0, 0, 0, 0) != NVFP4_ERR_SHAPE;
     bad |= NVFP4_WORKSPACE_BYTES < 2304;
@@ -262,11 +262,11 @@ def test_binding_refuses_cpu_tensors():
 def test_observe_fake_quant_validation():
     f = nv.lib.nvfp4_observe_fake_quant
     G = 1 << 30
-    x, y0, y1, s0, s1, c = A, A + G, A + 2 * G, A + 3 * G, A + 4 * G, A + 5 * G
+    x, y0, y1, s0, s1, c, w = A, A + G, A + 2 * G, A + 3 * G, A + 4 * G, A + 5 * G, A + 6 * G
     S, E = nv.OBS_STATIC_MINMAX, nv.OBS_EMA
 
-    def call(x=x, rows=4, cols=16, cur=c, st0=s0, m0=S, d0=0.0, out0=y0, st1=s1, m1=E, d1=0.01, out1=y1):
-        return f(P(x), rows, cols, P(cur), P(st0), m0, d0, P(out0), P(st1), m1, d1, P(out1), None)
+    def call(x=x, rows=4, cols=16, cur=c, st0=s0, m0=S, d0=0.0, out0=y0, st1=s1, m1=E, d1=0.01, out1=y1, ws=w):
+        return f(P(x), rows, cols, P(cur), P(st0), m0, d0, P(out0), P(st1), m1, d1, P(out1), P(ws), None)
 
     assert call(cols=0) == ERR_SHAPE
     assert call(rows=-2) == ERR_SHAPE
@@ -294,6 +294,10 @@ def test_observe_fake_quant_validation():
     assert call(cur=s1) == ERR_OVERLAP
     assert call(st0=x + 4) == ERR_OVERLAP
     assert call(cur=y1 + 8) == ERR_OVERLAP
+    assert call(ws=None) == ERR_NULL
+    assert call(ws=w + 64) == ERR_ALIGN
+    assert call(ws=y0) == ERR_OVERLAP
+    assert call(cur=w + 8) == ERR_OVERLAP                       # cur inside the workspace
 
 
 def test_workspace_size_matches_binding():

@@ -152,6 +152,25 @@ def test_matches_the_separate_calls():
     assert torch.equal(y1.view(torch.int16), z1.view(torch.int16))
 
 
+def test_workspace_is_reused_and_its_contents_do_not_matter():
+    """One workspace for calls of different sizes, filled with garbage before each."""
+    rng = np.random.default_rng(29)
+    ws = nv.new_workspace(DEV)
+    state = scalar(-1.0)
+    r = -1.0
+    for step, shape in enumerate([(2048, 4096), (3, 48), (1024, 1024), (0, 16)]):
+        x = random_bf16(rng, shape, spread=2.0)
+        ws.fill_(0x5A + step)
+        say("observe reused workspace %s" % (shape,))
+        y = nv.nvfp4_observe_fake_quant(dev(x), state, nv.OBS_EMA, 0.25, workspace=ws)
+        torch.cuda.synchronize()
+        a = oracle.amax(x) if x.size else 0.0
+        r = oracle.observer(r, a, E, float(np.float32(0.25)))
+        assert fbits(state.item()) == fbits(r), "step %d" % step
+        if x.size:
+            assert_same(host(y), oracle.fake_quant(x, r), "step %d y" % step)
+
+
 def test_rejects_shared_state_and_bad_mode():
     t = torch.zeros((4, 16), dtype=torch.bfloat16, device=DEV)
     s = scalar(-1.0)
@@ -171,9 +190,11 @@ def test_replays_in_a_graph():
     s0, s1, cur = scalar(-1.0), scalar(-1.0), scalar(0.0)
     y0, y1 = torch.empty_like(xt), torch.empty_like(xt)
 
+    ws = nv.new_workspace(DEV)
+
     def step():
         nv.nvfp4_observe_fake_quant(xt, s0, nv.OBS_STATIC_MINMAX, 0.0, s1, nv.OBS_EMA, 0.01, y0=y0, y1=y1,
-                                    cur=cur)
+                                    cur=cur, workspace=ws)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -194,6 +215,7 @@ def test_replays_in_a_graph():
         y0.fill_(float(replay + 1))
         y1.fill_(float(replay + 1))
         cur.fill_(-5.0)
+        ws.fill_(0xA5 + replay)
         torch.cuda.synchronize()
         say("observe graph replay %d" % replay)
         graph.replay()
