@@ -175,6 +175,8 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
         line("c3_qkv_shared_amax_fake_quant", c3, 6.0 * n3)
         line("c3_qkv_group_fake_quant_one_launch",
              lambda: nv.nvfp4_fake_quant_group(sibs, ys=ys, amax_out=shared), 6.0 * n3)
+        line("c3_qkv_group_fake_quant_ws",
+             lambda: nv.nvfp4_fake_quant_group_ws(sibs, ys=ys, amax_out=shared, workspace=ws), 6.0 * n3)
         del sibs, ys
 
     if group("c4_activation"):

@@ -19,6 +19,7 @@ __all__ = [
     "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
     "nvfp4_strerror", "FakeQuantSTE", "blocks_per_row", "nvfp4_observe_fake_quant",
     "WORKSPACE_BYTES", "new_workspace", "nvfp4_fake_quant_ws", "nvfp4_quantize_pack_ws",
+    "nvfp4_fake_quant_group_ws",
 ]
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
@@ -30,7 +31,7 @@ WORKSPACE_BYTES = 2304        # NVFP4_WORKSPACE_BYTES
 _EXPORTS = ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
             "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
             "nvfp4_observe_fake_quant", "nvfp4_fake_quant_ws", "nvfp4_quantize_pack_ws",
-            "nvfp4_strerror")
+            "nvfp4_fake_quant_group_ws", "nvfp4_strerror")
 
 
 class NVFP4Error(RuntimeError):
@@ -57,6 +58,7 @@ def _load() -> ctypes.CDLL:
     so.nvfp4_observe_fake_quant.argtypes = [P, I64, I64, P, P, I, F, P, P, I, F, P, P, P]
     so.nvfp4_fake_quant_ws.argtypes = [P, P, I64, I64, P, P, P]
     so.nvfp4_quantize_pack_ws.argtypes = [P, I64, I64, P, P, P, P, P, P]
+    so.nvfp4_fake_quant_group_ws.argtypes = [P, P, P, P, I, P, P, P]
     so.nvfp4_strerror.argtypes = [I]
     so.nvfp4_strerror.restype = ctypes.c_char_p
     for name in _EXPORTS:
@@ -145,13 +147,10 @@ def nvfp4_fake_quant(x: torch.Tensor, y: torch.Tensor | None = None,
     return y
 
 
-def nvfp4_fake_quant_group(xs, ys=None, amax_in: torch.Tensor | None = None,
-                           amax_out: torch.Tensor | None = None):
-    """Fake-quantize fused siblings with one shared amax -> list of bf16 outputs.
-    Without amax_in the amax over all of xs is computed first, into amax_out."""
+def _group_args(xs, ys, what):
     xs = list(xs)
     if not xs:
-        raise ValueError("nvfp4_fake_quant_group needs at least one tensor")
+        raise ValueError("%s needs at least one tensor" % what)
     shapes = [_matrix(x, "xs[%d]" % i) for i, x in enumerate(xs)]
     dev = xs[0].device
     ys = [torch.empty_like(x) for x in xs] if ys is None else list(ys)
@@ -160,17 +159,36 @@ def nvfp4_fake_quant_group(xs, ys=None, amax_in: torch.Tensor | None = None,
     for i, (x, y) in enumerate(zip(xs, ys)):
         if _matrix(y, "ys[%d]" % i) != x.shape or x.device != dev or y.device != dev:
             raise ValueError("ys[%d] must match xs[%d] in shape and device" % (i, i))
+    n = len(xs)
+    arrays = ((ctypes.c_void_p * n)(*[x.data_ptr() for x in xs]), (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys]),
+              (ctypes.c_int64 * n)(*[r for r, _ in shapes]), (ctypes.c_int64 * n)(*[c for _, c in shapes]), n)
+    return dev, ys, arrays
+
+
+def nvfp4_fake_quant_group(xs, ys=None, amax_in: torch.Tensor | None = None,
+                           amax_out: torch.Tensor | None = None):
+    """Fake-quantize fused siblings with one shared amax -> list of bf16 outputs.
+    Without amax_in the amax over all of xs is computed first, into amax_out."""
+    dev, ys, arrays = _group_args(xs, ys, "nvfp4_fake_quant_group")
     if amax_in is not None:
         _scalar(dev, amax_in)
     elif amax_out is None:
         amax_out = _scalar(dev)
-    n = len(xs)
-    xp = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
-    yp = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
-    rs = (ctypes.c_int64 * n)(*[r for r, _ in shapes])
-    cs = (ctypes.c_int64 * n)(*[c for _, c in shapes])
-    _check(lib.nvfp4_fake_quant_group(xp, yp, rs, cs, n, _ptr(amax_in), _ptr(amax_out), _stream(dev)),
+    _check(lib.nvfp4_fake_quant_group(*arrays, _ptr(amax_in), _ptr(amax_out), _stream(dev)),
            "nvfp4_fake_quant_group")
+    return ys
+
+
+def nvfp4_fake_quant_group_ws(xs, ys=None, amax_out: torch.Tensor | None = None,
+                              workspace: torch.Tensor | None = None):
+    """nvfp4_fake_quant_group with the shared amax computed from xs (at most 8 tensors),
+    through a workspace."""
+    dev, ys, arrays = _group_args(xs, ys, "nvfp4_fake_quant_group_ws")
+    if amax_out is not None:
+        _scalar(dev, amax_out)
+    ws = _workspace(dev, workspace)
+    _check(lib.nvfp4_fake_quant_group_ws(*arrays, _ptr(amax_out), _ptr(ws), _stream(dev)),
+           "nvfp4_fake_quant_group_ws")
     return ys
 
 

@@ -1616,14 +1616,15 @@ constexpr int64_t kPartialsOffset = 256;
 constexpr int kMaxPartials = (int)((NVFP4_WORKSPACE_BYTES - kPartialsOffset) / 4);
 static_assert(kMaxPartials >= 2 * 256, "the workspace holds a partial per amax workgroup");
 
-// Enqueue the amax of one tensor through the workspace: the amax pass in
-// partials mode, then their reduction into *amax, followed by nobs observer steps
-// on it.  An empty tensor gets one workgroup, which stores a zero partial.
-nvfp4_status enqueue_amax_ws(const void* x, int64_t numel, void* ws, float* amax, hipStream_t stream,
-                             const ObserverArgs& obs = ObserverArgs{}, int nobs = 0)
+// Enqueue the amax of up to NVFP4_AMAX_GROUP_MAX tensors through the workspace:
+// the amax pass in partials mode, then their reduction into *amax, followed by
+// nobs observer steps on it.  An all-empty group gets one workgroup, which stores
+// a zero partial.
+nvfp4_status enqueue_amax_ws(const void* const* xs, const int64_t* numels, int n, void* ws, float* amax,
+                             hipStream_t stream, const ObserverArgs& obs = ObserverArgs{}, int nobs = 0)
 {
     int64_t chunks;
-    const AmaxGroup g = amax_group(&x, &numel, 1, &chunks);
+    const AmaxGroup g = amax_group(xs, numels, n, &chunks);
     unsigned grid = persistent_grid(chunks, 1, NVFP4_AMAX_WG_PER_CU);
     if (grid > (unsigned)kMaxPartials)
         grid = (unsigned)kMaxPartials;
@@ -1789,6 +1790,54 @@ nvfp4_status check_regions(const Region* in, int nin, const Region* out, int nou
     return NVFP4_OK;
 }
 
+// Shapes, pointers, alignment and overlaps of the members of a group call:
+// every y_i may be x_i itself (exact in-place) and must not touch anything else.
+nvfp4_status check_group_members(const void* const* xs, void* const* ys, const int64_t* rows,
+                                 const int64_t* cols, int n)
+{
+    for (int i = 0; i < n; ++i) {
+        Matrix m;
+        const nvfp4_status st = check_matrix(rows[i], cols[i], &m);
+        if (st != NVFP4_OK)
+            return st;
+        if (m.numel > 0 && (!xs[i] || !ys[i]))
+            return NVFP4_ERR_NULL;
+    }
+    for (int i = 0; i < n; ++i)
+        if (!aligned(xs[i], 16) || !aligned(ys[i], 16))
+            return NVFP4_ERR_ALIGN;
+    for (int i = 0; i < n; ++i) {
+        const uint64_t bi = 2 * (uint64_t)(rows[i] * cols[i]);
+        for (int j = 0; j < n; ++j) {
+            const uint64_t bj = 2 * (uint64_t)(rows[j] * cols[j]);
+            if (!(i == j && xs[i] == ys[i]) && overlap(ys[i], bi, xs[j], bj))
+                return NVFP4_ERR_OVERLAP;
+            if (j > i && overlap(ys[i], bi, ys[j], bj))
+                return NVFP4_ERR_OVERLAP;
+        }
+    }
+    return NVFP4_OK;
+}
+
+// The fake-quant of every member with the device amax a: members whose rows are
+// whole blocks share group launches, ragged ones get a launch each.
+nvfp4_status enqueue_group_fake_quant(const void* const* xs, void* const* ys, const int64_t* rows,
+                                      const int64_t* cols, int n, const float* a, hipStream_t s)
+{
+    FakeQuantBatch batch;
+    for (int i = 0; i < n; ++i) {
+        Matrix m;
+        check_matrix(rows[i], cols[i], &m);
+        if (m.numel == 0)
+            continue;
+        const nvfp4_status st = m.ragged ? enqueue_fake_quant(xs[i], ys[i], cols[i], m, a, s)
+                                         : batch.add(xs[i], ys[i], m.nblocks, a, s);
+        if (st != NVFP4_OK)
+            return st;
+    }
+    return batch.flush(a, s);
+}
+
 bool observer_args_ok(int mode, float decay)
 {
     if (mode != NVFP4_OBS_STATIC_MINMAX && mode != NVFP4_OBS_EMA)
@@ -1888,30 +1937,15 @@ nvfp4_status nvfp4_fake_quant_group(const void* const* xs, void* const* ys, cons
         return NVFP4_ERR_NULL;
     if (n < 1)
         return NVFP4_ERR_ARG;
-    for (int i = 0; i < n; ++i) {
-        Matrix m;
-        const nvfp4_status st = check_matrix(rows[i], cols[i], &m);
-        if (st != NVFP4_OK)
-            return st;
-        if (m.numel > 0 && (!xs[i] || !ys[i]))
-            return NVFP4_ERR_NULL;
-    }
+    nvfp4_status st = check_group_members(xs, ys, rows, cols, n);
+    if (st != NVFP4_OK)
+        return st;
     if (!amax_in && !amax_out)
         return NVFP4_ERR_NULL;
     if ((amax_in && !aligned(amax_in, 4)) || (!amax_in && !aligned(amax_out, 4)))
         return NVFP4_ERR_ALIGN;
-    for (int i = 0; i < n; ++i)
-        if (!aligned(xs[i], 16) || !aligned(ys[i], 16))
-            return NVFP4_ERR_ALIGN;
     for (int i = 0; i < n; ++i) {
         const uint64_t bi = 2 * (uint64_t)(rows[i] * cols[i]);
-        for (int j = 0; j < n; ++j) {
-            const uint64_t bj = 2 * (uint64_t)(rows[j] * cols[j]);
-            if (!(i == j && xs[i] == ys[i]) && overlap(ys[i], bi, xs[j], bj))
-                return NVFP4_ERR_OVERLAP;
-            if (j > i && overlap(ys[i], bi, ys[j], bj))
-                return NVFP4_ERR_OVERLAP;
-        }
         if (!amax_in && (overlap(amax_out, 4, xs[i], bi) || overlap(amax_out, 4, ys[i], bi)))
             return NVFP4_ERR_OVERLAP;
         if (amax_in && overlap(amax_in, 4, ys[i], bi))
@@ -1919,7 +1953,6 @@ nvfp4_status nvfp4_fake_quant_group(const void* const* xs, void* const* ys, cons
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    nvfp4_status st;
     const float* a = amax_in;
     if (!a) {
         if (enqueue_reset(amax_out, s) != NVFP4_OK)
@@ -1932,19 +1965,42 @@ nvfp4_status nvfp4_fake_quant_group(const void* const* xs, void* const* ys, cons
             return st;
         a = amax_out;
     }
-    FakeQuantBatch batch;
-    for (int i = 0; i < n; ++i) {
-        Matrix m;
-        check_matrix(rows[i], cols[i], &m);
-        if (m.numel == 0)
-            continue;
-        st = m.ragged ? enqueue_fake_quant(xs[i], ys[i], cols[i], m, a, s)
-                      : batch.add(xs[i], ys[i], m.nblocks, a, s);
-        if (st != NVFP4_OK)
-            return st;
-    }
-    return batch.flush(a, s);
+    return enqueue_group_fake_quant(xs, ys, rows, cols, n, a, s);
 }
+
+nvfp4_status nvfp4_fake_quant_group_ws(const void* const* xs, void* const* ys, const int64_t* rows,
+                                       const int64_t* cols, int n, float* amax_out, void* workspace,
+                                       void* stream)
+{
+    if (!xs || !ys || !rows || !cols || !workspace)
+        return NVFP4_ERR_NULL;
+    if (n < 1 || n > NVFP4_AMAX_GROUP_MAX)
+        return NVFP4_ERR_ARG;
+    nvfp4_status st = check_group_members(xs, ys, rows, cols, n);
+    if (st != NVFP4_OK)
+        return st;
+    if (!aligned(workspace, 256) || (amax_out && !aligned(amax_out, 4)))
+        return NVFP4_ERR_ALIGN;
+    const Region extra[2] = {{workspace, NVFP4_WORKSPACE_BYTES}, {amax_out, amax_out ? 4u : 0u}};
+    if (overlap(extra[0].p, extra[0].bytes, extra[1].p, extra[1].bytes))
+        return NVFP4_ERR_OVERLAP;
+    for (int i = 0; i < n; ++i) {
+        const uint64_t bi = 2 * (uint64_t)(rows[i] * cols[i]);
+        for (const Region& e : extra)
+            if (overlap(e.p, e.bytes, xs[i], bi) || overlap(e.p, e.bytes, ys[i], bi))
+                return NVFP4_ERR_OVERLAP;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    int64_t numels[NVFP4_AMAX_GROUP_MAX];
+    for (int i = 0; i < n; ++i)
+        numels[i] = rows[i] * cols[i];
+    float* a = ws_amax(workspace, amax_out);
+    if (enqueue_amax_ws(xs, numels, n, workspace, a, s) != NVFP4_OK)
+        return NVFP4_ERR_HIP;
+    return enqueue_group_fake_quant(xs, ys, rows, cols, n, a, s);
+}
+
 
 nvfp4_status nvfp4_fake_quant_dual(const void* x, int64_t rows, int64_t cols, const float* amax0,
                                    void* y0, const float* amax1, void* y1, void* stream)
@@ -2089,7 +2145,7 @@ nvfp4_status nvfp4_fake_quant_ws(const void* x, void* y, int64_t rows, int64_t c
     if (m.numel == 0)
         return amax_out ? enqueue_reset(amax_out, s) : NVFP4_OK;
     float* a = ws_amax(workspace, amax_out);
-    if (enqueue_amax_ws(x, m.numel, workspace, a, s) != NVFP4_OK)
+    if (enqueue_amax_ws(&x, &m.numel, 1, workspace, a, s) != NVFP4_OK)
         return NVFP4_ERR_HIP;
     return enqueue_fake_quant(x, y, cols, m, a, s);
 }
@@ -2118,7 +2174,7 @@ nvfp4_status nvfp4_quantize_pack_ws(const void* x, int64_t rows, int64_t cols, f
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     float* a = ws_amax(workspace, amax_out);
-    if (enqueue_amax_ws(x, m.numel, workspace, a, s) != NVFP4_OK)
+    if (enqueue_amax_ws(&x, &m.numel, 1, workspace, a, s) != NVFP4_OK)
         return NVFP4_ERR_HIP;
     return enqueue_quantize_pack(x, cols, m, packed, scales, global_scale, a, s);
 }
@@ -2151,7 +2207,7 @@ nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols,
     // the amax pass, then one workgroup reduces its partial maxima into *cur and
     // steps both observers on it
     const ObserverArgs obs{{state0, state1}, {mode0, mode1}, {decay0, decay1}};
-    if (enqueue_amax_ws(x, m.numel, workspace, cur, s, obs, two ? 2 : 1) != NVFP4_OK)
+    if (enqueue_amax_ws(&x, &m.numel, 1, workspace, cur, s, obs, two ? 2 : 1) != NVFP4_OK)
         return NVFP4_ERR_HIP;
     if (m.numel == 0)
         return NVFP4_OK;

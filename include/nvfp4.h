@@ -257,6 +257,17 @@ nvfp4_status nvfp4_quantize_pack_ws(const void* x, int64_t rows, int64_t cols, f
                                     void* workspace, void* stream);
 
 /*
+ * nvfp4_fake_quant_group_ws -- nvfp4_fake_quant_group with amax_in = NULL for a
+ * group of at most NVFP4_AMAX_GROUP_MAX tensors (fused siblings): the same ys;
+ * amax_out (or NULL) receives the shared amax.  Members as for
+ * nvfp4_fake_quant_group.
+ * Errors: NULL, SHAPE, ARG (n < 1 or n > NVFP4_AMAX_GROUP_MAX), ALIGN, OVERLAP, HIP.
+ */
+nvfp4_status nvfp4_fake_quant_group_ws(const void* const* xs, void* const* ys, const int64_t* rows,
+                                       const int64_t* cols, int n, float* amax_out, void* workspace,
+                                       void* stream);
+
+/*
  * nvfp4_observe_fake_quant -- the activation step of a W4A4 layer with one or
  * two observers, as one call (verl QATLinear page, section 5: the step's amax
  * updates the observer, and the activation is fake-quantized with the updated

@@ -34,7 +34,7 @@ def test_header_declares_every_call():
     for n in ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
               "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
               "nvfp4_observe_fake_quant", "nvfp4_fake_quant_ws", "nvfp4_quantize_pack_ws",
-              "nvfp4_strerror"):
+              "nvfp4_fake_quant_group_ws", "nvfp4_strerror"):
         assert n in names
 
 
@@ -67,6 +67,7 @@ int main(void)
     bad |= nvfp4_observe_fake_quant(0, 4, 16, 0, 0, 0, 0.0f, 0, 0, 0, 0.0f, 0, 0, 0) != NVFP4_ERR_NULL;
     bad |= nvfp4_fake_quant_ws(0, 0, 4, 16, 0, 0, 0) != NVFP4_ERR_NULL;
     bad |= nvfp4_quantize_pack_ws(0, 4, 0, 0, 0, 0, 0, 0, 0) != NVFP4_ERR_SHAPE;
+    bad |= nvfp4_fake_quant_group_ws(0, 0, 0, 0, 1, 0, 0, 0) != NVFP4_ERR_NULL;
     bad |= NVFP4_WORKSPACE_BYTES < 2304;
     bad |= strcmp(nvfp4_strerror(NVFP4_OK), "ok") != 0;
     printf("%s\n", bad ? "FAIL" : "OK");
@@ -352,3 +353,33 @@ def test_quantize_pack_ws_validation():
     assert call(g=w + 8) == ERR_OVERLAP                         # gs inside the workspace
     assert call(amax=gs) == ERR_OVERLAP
     assert call(ws=sc) == ERR_OVERLAP
+
+
+def test_fake_quant_group_ws_validation():
+    g = nv.lib.nvfp4_fake_quant_group_ws
+    G = 1 << 30
+    x0, x1, y0, y1, a, w = A, A + G, A + 2 * G, A + 3 * G, A + 4 * G, A + 5 * G
+
+    def call(xs, ys, shapes, amax=a, ws=w, n=None):
+        n = len(xs) if n is None else n
+        k = max(len(xs), 1)
+        xp = (ctypes.c_void_p * k)(*xs)
+        yp = (ctypes.c_void_p * k)(*ys)
+        rs = (ctypes.c_int64 * k)(*[r for r, _ in shapes])
+        cs = (ctypes.c_int64 * k)(*[c for _, c in shapes])
+        return g(xp, yp, rs, cs, n, P(amax), P(ws), None)
+
+    sh = [(4, 16), (8, 32)]
+    assert g(None, None, None, None, 1, None, P(w), None) == ERR_NULL
+    assert call([x0, x1], [y0, y1], sh, ws=None) == ERR_NULL
+    assert call([x0], [y0], [(4, 16)], n=0) == ERR_ARG
+    assert call([A + i * G for i in range(9)], [A + (10 + i) * G for i in range(9)], [(1, 16)] * 9) == ERR_ARG
+    assert call([x0, x1], [y0, y1], [(4, 16), (4, 0)]) == ERR_SHAPE
+    assert call([x0, None], [y0, y1], sh) == ERR_NULL
+    assert call([x0, x1 + 8], [y0, y1], sh) == ERR_ALIGN
+    assert call([x0, x1], [y0, y1], sh, ws=w + 128) == ERR_ALIGN
+    assert call([x0, x1], [y0, y1], sh, amax=a + 2) == ERR_ALIGN
+    assert call([x0, x1], [x1, y1], sh) == ERR_OVERLAP                 # y0 is another member's input
+    assert call([x0, x1], [y0, y1], sh, amax=x0 + 4) == ERR_OVERLAP
+    assert call([x0, x1], [y0, y1], sh, ws=y1) == ERR_OVERLAP
+    assert call([x0, x1], [y0, y1], sh, amax=w + 4) == ERR_OVERLAP    # amax inside the workspace

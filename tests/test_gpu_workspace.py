@@ -2,7 +2,9 @@
 
 nvfp4_fake_quant_ws and nvfp4_quantize_pack_ws must give the oracle's fake-quant
 and quantize-pack of x with its own amax (VideoX-Fun page, the tensor-wide amax
-and the divide-by-gs convention), and max|x| in amax_out.  The workspace is
+and the divide-by-gs convention), and max|x| in amax_out; nvfp4_fake_quant_group_ws
+the fake-quant of every member with the group's shared amax (verl QATLinear page,
+section 4).  The workspace is
 reused between calls of different sizes and is filled with garbage before most
 calls: its contents on entry must not matter.
 """
@@ -141,6 +143,46 @@ def test_workspace_reuse_large_then_small():
     assert fbits(a_big.item()) == fbits(oracle.amax(big)) > fbits(oracle.amax(small))
     assert fbits(a_small.item()) == fbits(oracle.amax(small))
     assert_same(host(y), oracle.fake_quant(small), "small after large")
+
+
+def test_group_ws_c3_siblings():
+    sibs = list(synth.c3_siblings())
+    say("group ws c3")
+    ts = [dev(x) for x in sibs]
+    amax = scalar(-3.0)
+    dirty_workspace()
+    ys = nv.nvfp4_fake_quant_group_ws(ts, amax_out=amax, workspace=WS)
+    torch.cuda.synchronize()
+    a = oracle.amax_group(sibs)
+    assert fbits(amax.item()) == fbits(a)
+    for i, (x, y) in enumerate(zip(sibs, ys)):
+        assert_same(host(y), oracle.fake_quant(x, a), "c3 group ws member %d" % i)
+
+
+# up to 8 members: chunk edges, an empty member, ragged rows (their own launches), an
+# in-place member
+GROUP = [(64, 256), (0, 32), (3, 20), (1025, 16), (37, 4096), (5, 33), (512, 48), (7, 1)]
+
+
+@pytest.mark.parametrize("k", [1, 3, 8])
+def test_group_ws_members(k):
+    rng = np.random.default_rng(90 + k)
+    xs = [random_bf16(rng, shape) for shape in GROUP[:k]]
+    say("group ws %d members" % k)
+    ts = [dev(x) for x in xs]
+    ys = [t if i == 0 else torch.empty_like(t) for i, t in enumerate(ts)]     # member 0 in place
+    dirty_workspace()
+    nv.nvfp4_fake_quant_group_ws(ts, ys=ys, workspace=WS)
+    torch.cuda.synchronize()
+    a = oracle.amax_group(xs) if any(x.size for x in xs) else 0.0
+    for i, (x, y) in enumerate(zip(xs, ys)):
+        assert_same(host(y), oracle.fake_quant(x, a) if x.size else x, "member %d" % i)
+
+
+def test_group_ws_rejects_more_than_eight():
+    ts = [torch.zeros((1, 16), dtype=torch.bfloat16, device=DEV) for _ in range(9)]
+    with pytest.raises(nv.NVFP4Error):
+        nv.nvfp4_fake_quant_group_ws(ts, workspace=WS)
 
 
 def test_workspace_calls_replay_in_a_graph():
