@@ -88,6 +88,8 @@ namespace {
 #ifndef NVFP4_MID_WG_PER_CU
 #define NVFP4_MID_WG_PER_CU 8
 #endif
+// Partial maxima the workspace holds (one per amax workgroup), from byte 256.
+#define NVFP4_MAX_PARTIALS ((NVFP4_WORKSPACE_BYTES - 256) / 4)
 #ifndef NVFP4_LIN_DEPTH
 #define NVFP4_LIN_DEPTH 2         // K steps of weight loads in flight per linear wave (even)
 #endif
@@ -558,6 +560,9 @@ struct AmaxGroup {
     int32_t ntail[NVFP4_AMAX_GROUP_MAX];
     int32_t count;
     int64_t alloc_from;                            // chunks from here on load into the caches
+    const float* snap_from[2];                     // workgroup 0 copies *snap_from[i] to snap_to[i],
+    float* snap_to;                                // i < nsnap (observer states before their step)
+    int32_t nsnap;
 };
 
 // max |x| over a group of tensors.  Atomic mode: one signed-integer atomic max
@@ -570,6 +575,9 @@ template <bool Partials>
 __global__ __launch_bounds__(kThreads) void k_amax(AmaxGroup g, float* out, uint32_t* partials)
 {
     constexpr int64_t kChunk = (int64_t)kThreads * kAmaxUnroll;
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        for (int i = 0; i < g.nsnap; ++i)
+            g.snap_to[i] = *g.snap_from[i];
     uint32_t mx = 0;
     const int64_t total = g.chunk_end[g.count - 1];
     // chunks only grow along the loop, so the current tensor is cached and
@@ -664,13 +672,17 @@ __device__ __forceinline__ void load_halves(const uint4* x, int64_t base, int64_
 // the four dwords of half j.  The first iteration's loads are issued before
 // the workgroup builds its scale-byte table, so the table build hides under
 // their latency.
-template <bool NtLd, typename Build, typename Body>
+// With Fence, the loads issued before the pass (the partial maxima) stay ahead
+// of the loads of x, so build() waits for them alone.
+template <bool NtLd, bool Fence, typename Build, typename Body>
 __device__ __forceinline__ void quantize_pass(const uint4* x, int64_t nhalves, Build build,
                                               Body body)
 {
     const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
     int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
     uint4 v[kUnroll];
+    if (Fence)
+        __builtin_amdgcn_sched_barrier(0);
     load_halves<NtLd>(x, base, nhalves, v);
     build();
     __syncthreads();
@@ -687,6 +699,128 @@ __device__ __forceinline__ void quantize_pass(const uint4* x, int64_t nhalves, B
     }
 }
 
+// Observer states of up to two observers (verl QATLinear page, section 5).
+struct ObserverArgs {
+    float* state[2];
+    int mode[2];
+    float decay[2];
+};
+
+// One observer step: the new state from state s and the step amax c.
+__device__ __forceinline__ float observer_value(float s, float c, int mode, float decay)
+{
+    if (s < 0.0f)
+        return c;                                  // first observation
+    if (mode == NVFP4_OBS_STATIC_MINMAX)
+        return c > s ? c : s;
+    const float keep = 1.0f - decay;
+    const float a = keep * s;
+    const float b = decay * c;
+    return a + b;                                  // no contraction: -ffp-contract=off
+}
+
+// Observer steps of up to two states on the same step amax c, in place.
+__device__ void observer_steps(float c, const ObserverArgs& o, int n)
+{
+    for (int i = 0; i < n; ++i)
+        *o.state[i] = observer_value(*o.state[i], c, o.mode[i], o.decay[i]);
+}
+
+// Where a quantizing pass takes its amax from: amax[0] (and amax[1] for the dual
+// pass), or (workspace calls) the partial maxima of the amax pass, which every
+// workgroup reduces itself, so no launch sits between the two passes.  From
+// the partials, the pass quantizes with the reduced amax c, or, with nobs
+// observers, with their new states observer(prior[i], c); prior holds the
+// states as the amax pass copied them, so workgroup 0 may store the new states
+// (and c in *store) while other workgroups have yet to start.
+struct AmaxIn {
+    const float* amax[2];
+    const uint32_t* partials;     // 16-byte aligned, at most NVFP4_MAX_PARTIALS
+    int count;
+    float* store;                 // may be null
+    ObserverArgs obs;
+    int nobs;
+    const float* prior;
+};
+
+// Each lane's share of the partials: kPartialsPerLane consecutive slots (slots
+// at or past count read as 0).  Vector loads, issued by every wave.
+constexpr int kPartialsPerLane = NVFP4_MAX_PARTIALS / 64;
+static_assert(NVFP4_MAX_PARTIALS % 256 == 0, "whole 16-byte loads of partials per lane");
+
+struct PartialLoads {
+    uint4 v[kPartialsPerLane / 4];
+    float prior[2];
+};
+
+__device__ __forceinline__ PartialLoads load_partials(const AmaxIn& src)
+{
+    PartialLoads p;
+    const int i = kPartialsPerLane * (int)(threadIdx.x & 63u);
+    const uint4* q = reinterpret_cast<const uint4*>(src.partials + i);
+#pragma unroll
+    for (int k = 0; k < kPartialsPerLane / 4; ++k)
+        p.v[k] = i < src.count ? q[k] : make_uint4(0u, 0u, 0u, 0u);
+    p.prior[0] = src.nobs > 0 ? src.prior[0] : 0.0f;
+    p.prior[1] = src.nobs > 1 ? src.prior[1] : 0.0f;
+    return p;
+}
+
+// The amaxes the pass quantizes with, from the loaded partials: a max over the
+// lane's valid slots, then across the wave (every wave computes it, so no
+// barrier is needed), then the observer steps.
+__device__ __forceinline__ void resolve_amax(const PartialLoads& p, const AmaxIn& src, float (&a)[2])
+{
+    const int i = kPartialsPerLane * (int)(threadIdx.x & 63u);
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < kPartialsPerLane / 4; ++k) {
+        const uint32_t w[4] = {p.v[k].x, p.v[k].y, p.v[k].z, p.v[k].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            m = i + 4 * k + e < src.count ? max(m, w[e]) : m;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    const float c = __uint_as_float(m << 16);
+    a[0] = src.nobs > 0 ? observer_value(p.prior[0], c, src.obs.mode[0], src.obs.decay[0]) : c;
+    a[1] = src.nobs > 1 ? observer_value(p.prior[1], c, src.obs.mode[1], src.obs.decay[1]) : c;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (src.store)
+            *src.store = c;
+        if (src.nobs > 0)
+            *src.obs.state[0] = a[0];
+        if (src.nobs > 1)
+            *src.obs.state[1] = a[1];
+    }
+}
+
+// The amax of a single-amax pass: issue the loads it needs (before the loads
+// of x), then finish it once they are in.  Without partials the pass reads
+// *src.amax[0] and behaves as before partials existed.
+template <bool Partials>
+struct AmaxOfPass {
+    PartialLoads p;
+    float direct;
+
+    __device__ __forceinline__ explicit AmaxOfPass(const AmaxIn& src)
+    {
+        if (Partials)
+            p = load_partials(src);
+        else
+            direct = *src.amax[0];
+    }
+    __device__ __forceinline__ float finish(const AmaxIn& src) const
+    {
+        if (!Partials)
+            return direct;
+        float a[2];
+        resolve_amax(p, src, a);
+        return a[0];
+    }
+};
+
 // Threads 0..127 tabulate the 128 scale bytes under gs (the other threads idle).
 __device__ __forceinline__ void build_table(float gs, uint32_t* tab)
 {
@@ -694,15 +828,19 @@ __device__ __forceinline__ void build_table(float gs, uint32_t* tab)
         build_entry(threadIdx.x, gs, tab + threadIdx.x * kEntryWords);
 }
 
+template <bool Partials>
 __global__ __launch_bounds__(kThreads) void k_fake_quant(const uint4* x, uint4* y,
-                                                         int64_t nhalves,
-                                                         const float* __restrict__ amax)
+                                                         int64_t nhalves, AmaxIn src)
 {
     __shared__ uint4 table[128 * kEntryWords / 4];
     uint32_t* tab = reinterpret_cast<uint32_t*>(table);
-    const float gs = global_scale_of(*amax);
-    quantize_pass<NVFP4_FQ_NT_LD != 0>(x, nhalves, [&] { build_table(gs, tab); },
-                                       [&](const uint32_t (&w)[4], int64_t j) {
+    const AmaxOfPass<Partials> am(src);
+    float gs = Partials ? 0.0f : global_scale_of(am.direct);
+    quantize_pass<NVFP4_FQ_NT_LD != 0, Partials>(x, nhalves, [&] {
+        if (Partials)
+            gs = global_scale_of(am.finish(src));
+        build_table(gs, tab);
+    }, [&](const uint32_t (&w)[4], int64_t j) {
         fake_quant_half<NVFP4_FQ_NT_ST != 0>(w, pair_max(w), tab, gs, y, j);
     });
 }
@@ -713,16 +851,27 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant(const uint4* x, uint4* 
 // one amax.  A lane reads its half block before writing either output, so
 // y0 == x or y1 == x (in place) is safe.
 static_assert(kThreads == 256, "the dual table build gives each amax 128 threads");
+template <bool Partials>
 __global__ __launch_bounds__(kThreads) void k_fake_quant_dual(const uint4* x, uint4* y0,
-                                                              uint4* y1, int64_t nhalves,
-                                                              const float* __restrict__ amax0,
-                                                              const float* __restrict__ amax1)
+                                                              uint4* y1, int64_t nhalves, AmaxIn src)
 {
     __shared__ uint4 table[2 * 128 * kEntryWords / 4];
     uint32_t* tab = reinterpret_cast<uint32_t*>(table);
-    const float gs0 = global_scale_of(*amax0);
-    const float gs1 = global_scale_of(*amax1);
-    quantize_pass<NVFP4_FQ_NT_LD != 0>(x, nhalves, [&] {
+    PartialLoads p;
+    float gs0 = 0.0f, gs1 = 0.0f;
+    if (Partials) {
+        p = load_partials(src);
+    } else {
+        gs0 = global_scale_of(*src.amax[0]);
+        gs1 = global_scale_of(*src.amax[1]);
+    }
+    quantize_pass<NVFP4_FQ_NT_LD != 0, Partials>(x, nhalves, [&] {
+        if (Partials) {
+            float a[2];
+            resolve_amax(p, src, a);
+            gs0 = global_scale_of(a[0]);
+            gs1 = global_scale_of(a[1]);
+        }
         const uint32_t half = threadIdx.x >> 7, s = threadIdx.x & 127u;
         build_entry(s, half ? gs1 : gs0, tab + (half * 128u + s) * kEntryWords);
     }, [&](const uint32_t (&w)[4], int64_t j) {
@@ -745,12 +894,16 @@ struct FqGroup {
     int32_t count;
 };
 
-__global__ __launch_bounds__(kThreads) void k_fake_quant_group(FqGroup g, const float* __restrict__ amax)
+template <bool Partials>
+__global__ __launch_bounds__(kThreads) void k_fake_quant_group(FqGroup g, AmaxIn src)
 {
     constexpr int64_t kChunk = (int64_t)kThreads * kUnroll;
     __shared__ uint4 table[128 * kEntryWords / 4];
     uint32_t* tab = reinterpret_cast<uint32_t*>(table);
-    const float gs = global_scale_of(*amax);
+    const AmaxOfPass<Partials> am(src);
+    float gs = Partials ? 0.0f : global_scale_of(am.direct);
+    if (Partials)
+        __builtin_amdgcn_sched_barrier(0);
     const int64_t total = g.chunk_end[g.count - 1];
     // chunks only grow along the loop, so the tensor cursor only moves forward
     int t = 0;
@@ -767,6 +920,8 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant_group(FqGroup g, const 
         seek(c);
         load_halves<NVFP4_FQ_NT_LD != 0>(g.x[t], (c - begin) * kChunk + threadIdx.x, g.nhalves[t], v);
     }
+    if (Partials)
+        gs = global_scale_of(am.finish(src));
     build_table(gs, tab);
     __syncthreads();
     for (; c < total; c += gridDim.x) {
@@ -790,20 +945,27 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant_group(FqGroup g, const 
 
 // Quantize-pack: lane j stores the eight codes of half j (one dword of the
 // packed codes); the even lane of a block also stores its scale byte.
+template <bool Partials>
 __global__ __launch_bounds__(kThreads) void k_quantize_pack(const uint4* __restrict__ x,
                                                             uint32_t* __restrict__ packed,
                                                             uint8_t* __restrict__ scales,
                                                             float* __restrict__ gs_out,
-                                                            int64_t nhalves,
-                                                            const float* __restrict__ amax)
+                                                            int64_t nhalves, AmaxIn src)
 {
     __shared__ uint4 table[128 * kEntryWords / 4];
     uint32_t* tab = reinterpret_cast<uint32_t*>(table);
-    const float gs = global_scale_of(*amax);
-    if (blockIdx.x == 0 && threadIdx.x == 0)
+    const AmaxOfPass<Partials> am(src);
+    float gs = Partials ? 0.0f : global_scale_of(am.direct);
+    if (!Partials && blockIdx.x == 0 && threadIdx.x == 0)
         *gs_out = gs;
-    quantize_pass<NVFP4_QP_NT_LD != 0>(x, nhalves, [&] { build_table(gs, tab); },
-                                       [&](const uint32_t (&w)[4], int64_t j) {
+    quantize_pass<NVFP4_QP_NT_LD != 0, Partials>(x, nhalves, [&] {
+        if (Partials) {
+            gs = global_scale_of(am.finish(src));
+            if (blockIdx.x == 0 && threadIdx.x == 0)
+                *gs_out = gs;
+        }
+        build_table(gs, tab);
+    }, [&](const uint32_t (&w)[4], int64_t j) {
         const uint32_t sb = scale_byte_of(pair_max(w), gs);
         store4<NVFP4_QP_NT_ST != 0>(packed + j, half_codes(w, tab + sb * kEntryWords));
         if (!(j & 1))
@@ -1398,32 +1560,6 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_linear_tiled(const uint16_t
     }
 }
 
-// Observer steps of up to two states on the same step amax *cur.
-struct ObserverArgs {
-    float* state[2];
-    int mode[2];
-    float decay[2];
-};
-
-__device__ void observer_steps(float c, const ObserverArgs& o, int n)
-{
-    for (int i = 0; i < n; ++i) {
-        const float s = *o.state[i];
-        float r;
-        if (s < 0.0f) {
-            r = c;                                 // first observation
-        } else if (o.mode[i] == NVFP4_OBS_STATIC_MINMAX) {
-            r = c > s ? c : s;
-        } else {
-            const float keep = 1.0f - o.decay[i];
-            const float a = keep * s;
-            const float b = o.decay[i] * c;
-            r = a + b;                             // no contraction: -ffp-contract=off
-        }
-        *o.state[i] = r;
-    }
-}
-
 __global__ void k_observer(const float* cur, ObserverArgs o, int n)
 {
     observer_steps(*cur, o, n);
@@ -1574,12 +1710,14 @@ int quant_wg_per_cu(int64_t nhalves, int large)
     return nhalves * 16 < NVFP4_MID_BYTES ? NVFP4_MID_WG_PER_CU : large;
 }
 
-// One fake-quant launch of a single tensor with a device amax.
-nvfp4_status enqueue_fake_quant(const void* x, void* y, int64_t cols, const Matrix& m, const float* a,
+// One fake-quant launch of a single tensor with its amax from src (partials
+// only for rows of whole blocks).
+nvfp4_status enqueue_fake_quant(const void* x, void* y, int64_t cols, const Matrix& m, const AmaxIn& src,
                                 hipStream_t s)
 {
     if (m.numel == 0)
         return NVFP4_OK;
+    const float* a = src.amax[0];                  // the ragged kernels take a direct amax
     if (m.ragged) {
         const RaggedShape g{cols, m.nbr, m.nblocks};
         k_fake_quant_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
@@ -1587,16 +1725,27 @@ nvfp4_status enqueue_fake_quant(const void* x, void* y, int64_t cols, const Matr
         return launched();
     }
     const int64_t nh = 2 * m.nblocks;
-    k_fake_quant<<<persistent_grid(nh, (int64_t)kThreads * kUnroll, quant_wg_per_cu(nh, NVFP4_FQ_WG_PER_CU)),
-                   kThreads, 0, s>>>(static_cast<const uint4*>(x), static_cast<uint4*>(y), nh, a);
+    const dim3 grid(persistent_grid(nh, (int64_t)kThreads * kUnroll, quant_wg_per_cu(nh, NVFP4_FQ_WG_PER_CU)));
+    if (src.partials)
+        k_fake_quant<true><<<grid, kThreads, 0, s>>>(static_cast<const uint4*>(x), static_cast<uint4*>(y), nh, src);
+    else
+        k_fake_quant<false><<<grid, kThreads, 0, s>>>(static_cast<const uint4*>(x), static_cast<uint4*>(y), nh, src);
     return launched();
+}
+
+// The same with a device amax.
+nvfp4_status enqueue_fake_quant(const void* x, void* y, int64_t cols, const Matrix& m, const float* a,
+                                hipStream_t s)
+{
+    return enqueue_fake_quant(x, y, cols, m, AmaxIn{{a, nullptr}}, s);
 }
 
 // One quantize-pack launch of a single tensor (also for an empty one: it still
 // writes the global scale).
 nvfp4_status enqueue_quantize_pack(const void* x, int64_t cols, const Matrix& m, uint8_t* packed, uint8_t* scales,
-                                   float* global_scale, const float* a, hipStream_t s)
+                                   float* global_scale, const AmaxIn& src, hipStream_t s)
 {
+    const float* a = src.amax[0];                  // the ragged kernel takes a direct amax
     if (m.ragged) {
         const RaggedShape g{cols, m.nbr, m.nblocks};
         k_quantize_pack_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
@@ -1604,35 +1753,71 @@ nvfp4_status enqueue_quantize_pack(const void* x, int64_t cols, const Matrix& m,
         return launched();
     }
     const int64_t nh = 2 * m.nblocks;
-    k_quantize_pack<<<persistent_grid(nh, (int64_t)kThreads * kUnroll, quant_wg_per_cu(nh, NVFP4_QP_WG_PER_CU)),
-                      kThreads, 0, s>>>(static_cast<const uint4*>(x), reinterpret_cast<uint32_t*>(packed), scales,
-                                        global_scale, nh, a);
+    const dim3 grid(persistent_grid(nh, (int64_t)kThreads * kUnroll, quant_wg_per_cu(nh, NVFP4_QP_WG_PER_CU)));
+    const uint4* xv = static_cast<const uint4*>(x);
+    uint32_t* pv = reinterpret_cast<uint32_t*>(packed);
+    if (src.partials)
+        k_quantize_pack<true><<<grid, kThreads, 0, s>>>(xv, pv, scales, global_scale, nh, src);
+    else
+        k_quantize_pack<false><<<grid, kThreads, 0, s>>>(xv, pv, scales, global_scale, nh, src);
     return launched();
+}
+
+nvfp4_status enqueue_quantize_pack(const void* x, int64_t cols, const Matrix& m, uint8_t* packed, uint8_t* scales,
+                                   float* global_scale, const float* a, hipStream_t s)
+{
+    return enqueue_quantize_pack(x, cols, m, packed, scales, global_scale, AmaxIn{{a, nullptr}}, s);
 }
 
 // The workspace of the calls that take one: the amax (when the caller asks
 // for none) at byte 0, the amax pass's partial maxima from byte kPartialsOffset.
 constexpr int64_t kPartialsOffset = 256;
-constexpr int kMaxPartials = (int)((NVFP4_WORKSPACE_BYTES - kPartialsOffset) / 4);
-static_assert(kMaxPartials >= 2 * 256, "the workspace holds a partial per amax workgroup");
+constexpr int kMaxPartials = NVFP4_MAX_PARTIALS;
+static_assert(kPartialsOffset + 4 * kMaxPartials <= NVFP4_WORKSPACE_BYTES, "partials fit the workspace");
+static_assert(kMaxPartials >= NVFP4_AMAX_WG_PER_CU * 256, "the workspace holds a partial per amax workgroup");
 
 // Enqueue the amax of up to NVFP4_AMAX_GROUP_MAX tensors through the workspace:
 // the amax pass in partials mode, then their reduction into *amax, followed by
 // nobs observer steps on it.  An all-empty group gets one workgroup, which stores
 // a zero partial.
-nvfp4_status enqueue_amax_ws(const void* const* xs, const int64_t* numels, int n, void* ws, float* amax,
-                             hipStream_t stream, const ObserverArgs& obs = ObserverArgs{}, int nobs = 0)
+// The amax pass alone, in partials mode: *src gets the partials and their count,
+// and, with nobs observers, their arguments and the states as the pass copies
+// them into the workspace (at byte kPriorOffset).
+constexpr int64_t kPriorOffset = 16;
+static_assert(kPriorOffset >= 4 && kPriorOffset + 8 <= kPartialsOffset, "workspace layout");
+
+nvfp4_status enqueue_amax_partials(const void* const* xs, const int64_t* numels, int n, void* ws,
+                                   hipStream_t stream, AmaxIn* src, const ObserverArgs& obs = ObserverArgs{},
+                                   int nobs = 0)
 {
     int64_t chunks;
-    const AmaxGroup g = amax_group(xs, numels, n, &chunks);
+    AmaxGroup g = amax_group(xs, numels, n, &chunks);
     unsigned grid = persistent_grid(chunks, 1, NVFP4_AMAX_WG_PER_CU);
     if (grid > (unsigned)kMaxPartials)
         grid = (unsigned)kMaxPartials;
     uint32_t* partials = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kPartialsOffset);
+    float* prior = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kPriorOffset);
+    for (int i = 0; i < nobs; ++i)
+        g.snap_from[i] = obs.state[i];
+    g.snap_to = prior;
+    g.nsnap = nobs;
     k_amax<true><<<grid, kThreads, 0, stream>>>(g, nullptr, partials);
-    if (launched() != NVFP4_OK)
+    *src = AmaxIn{};
+    src->partials = partials;
+    src->count = (int)grid;
+    src->obs = obs;
+    src->nobs = nobs;
+    src->prior = prior;
+    return launched();
+}
+
+nvfp4_status enqueue_amax_ws(const void* const* xs, const int64_t* numels, int n, void* ws, float* amax,
+                             hipStream_t stream, const ObserverArgs& obs = ObserverArgs{}, int nobs = 0)
+{
+    AmaxIn src{};
+    if (enqueue_amax_partials(xs, numels, n, ws, stream, &src) != NVFP4_OK)
         return NVFP4_ERR_HIP;
-    k_amax_finish<<<1, kThreads, 0, stream>>>(partials, (int)grid, amax, obs, nobs);
+    k_amax_finish<<<1, kThreads, 0, stream>>>(src.partials, src.count, amax, obs, nobs);
     return launched();
 }
 
@@ -1645,7 +1830,7 @@ struct FakeQuantBatch {
     FqGroup g{};
     int64_t chunks = 0;
 
-    nvfp4_status add(const void* x, void* y, int64_t nblocks, const float* a, hipStream_t s)
+    nvfp4_status add(const void* x, void* y, int64_t nblocks, const AmaxIn& src, hipStream_t s)
     {
         constexpr int64_t kChunk = (int64_t)kThreads * kUnroll;
         const int k = g.count;
@@ -1654,15 +1839,18 @@ struct FakeQuantBatch {
         g.nhalves[k] = 2 * nblocks;
         chunks += (2 * nblocks + kChunk - 1) / kChunk;
         g.chunk_end[k] = chunks;
-        return ++g.count == NVFP4_AMAX_GROUP_MAX ? flush(a, s) : NVFP4_OK;
+        return ++g.count == NVFP4_AMAX_GROUP_MAX ? flush(src, s) : NVFP4_OK;
     }
-    nvfp4_status flush(const float* a, hipStream_t s)
+    nvfp4_status flush(const AmaxIn& src, hipStream_t s)
     {
         if (g.count == 0)
             return NVFP4_OK;
         constexpr int64_t kChunk = (int64_t)kThreads * kUnroll;
-        k_fake_quant_group<<<persistent_grid(chunks, 1, quant_wg_per_cu(chunks * kChunk, NVFP4_FQ_WG_PER_CU)),
-                             kThreads, 0, s>>>(g, a);
+        const dim3 grid(persistent_grid(chunks, 1, quant_wg_per_cu(chunks * kChunk, NVFP4_FQ_WG_PER_CU)));
+        if (src.partials)
+            k_fake_quant_group<true><<<grid, kThreads, 0, s>>>(g, src);
+        else
+            k_fake_quant_group<false><<<grid, kThreads, 0, s>>>(g, src);
         g = FqGroup{};
         chunks = 0;
         return launched();
@@ -1819,10 +2007,11 @@ nvfp4_status check_group_members(const void* const* xs, void* const* ys, const i
     return NVFP4_OK;
 }
 
-// The fake-quant of every member with the device amax a: members whose rows are
-// whole blocks share group launches, ragged ones get a launch each.
+// The fake-quant of every member with the amax from src: members whose rows are
+// whole blocks share group launches, ragged ones get a launch each (which needs
+// a direct amax, src.amax[0]).
 nvfp4_status enqueue_group_fake_quant(const void* const* xs, void* const* ys, const int64_t* rows,
-                                      const int64_t* cols, int n, const float* a, hipStream_t s)
+                                      const int64_t* cols, int n, const AmaxIn& src, hipStream_t s)
 {
     FakeQuantBatch batch;
     for (int i = 0; i < n; ++i) {
@@ -1830,12 +2019,18 @@ nvfp4_status enqueue_group_fake_quant(const void* const* xs, void* const* ys, co
         check_matrix(rows[i], cols[i], &m);
         if (m.numel == 0)
             continue;
-        const nvfp4_status st = m.ragged ? enqueue_fake_quant(xs[i], ys[i], cols[i], m, a, s)
-                                         : batch.add(xs[i], ys[i], m.nblocks, a, s);
+        const nvfp4_status st = m.ragged ? enqueue_fake_quant(xs[i], ys[i], cols[i], m, src.amax[0], s)
+                                         : batch.add(xs[i], ys[i], m.nblocks, src, s);
         if (st != NVFP4_OK)
             return st;
     }
-    return batch.flush(a, s);
+    return batch.flush(src, s);
+}
+
+nvfp4_status enqueue_group_fake_quant(const void* const* xs, void* const* ys, const int64_t* rows,
+                                      const int64_t* cols, int n, const float* a, hipStream_t s)
+{
+    return enqueue_group_fake_quant(xs, ys, rows, cols, n, AmaxIn{{a, nullptr}}, s);
 }
 
 bool observer_args_ok(int mode, float decay)
@@ -1993,8 +2188,20 @@ nvfp4_status nvfp4_fake_quant_group_ws(const void* const* xs, void* const* ys, c
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     int64_t numels[NVFP4_AMAX_GROUP_MAX];
-    for (int i = 0; i < n; ++i)
+    bool whole_blocks = true, any = false;
+    for (int i = 0; i < n; ++i) {
         numels[i] = rows[i] * cols[i];
+        any = any || numels[i] > 0;
+        whole_blocks = whole_blocks && (numels[i] == 0 || cols[i] % 16 == 0);
+    }
+    if (any && whole_blocks) {
+        // one group launch, which reduces the partials itself and stores the amax
+        AmaxIn src;
+        if (enqueue_amax_partials(xs, numels, n, workspace, s, &src) != NVFP4_OK)
+            return NVFP4_ERR_HIP;
+        src.store = amax_out;
+        return enqueue_group_fake_quant(xs, ys, rows, cols, n, src, s);
+    }
     float* a = ws_amax(workspace, amax_out);
     if (enqueue_amax_ws(xs, numels, n, workspace, a, s) != NVFP4_OK)
         return NVFP4_ERR_HIP;
@@ -2035,9 +2242,10 @@ nvfp4_status nvfp4_fake_quant_dual(const void* x, int64_t rows, int64_t cols, co
         return st != NVFP4_OK ? st : enqueue_fake_quant(x, y1, cols, m, amax1, s);
     }
     const int64_t nh = 2 * m.nblocks;
-    k_fake_quant_dual<<<persistent_grid(nh, (int64_t)kThreads * kUnroll, quant_wg_per_cu(nh, NVFP4_FQ_WG_PER_CU)),
-                        kThreads, 0, s>>>(static_cast<const uint4*>(x), static_cast<uint4*>(y0),
-                                          static_cast<uint4*>(y1), nh, amax0, amax1);
+    k_fake_quant_dual<false><<<persistent_grid(nh, (int64_t)kThreads * kUnroll,
+                                               quant_wg_per_cu(nh, NVFP4_FQ_WG_PER_CU)),
+                               kThreads, 0, s>>>(static_cast<const uint4*>(x), static_cast<uint4*>(y0),
+                                                 static_cast<uint4*>(y1), nh, AmaxIn{{amax0, amax1}});
     return launched();
 }
 
@@ -2144,6 +2352,14 @@ nvfp4_status nvfp4_fake_quant_ws(const void* x, void* y, int64_t rows, int64_t c
     (void)hipGetLastError();
     if (m.numel == 0)
         return amax_out ? enqueue_reset(amax_out, s) : NVFP4_OK;
+    if (!m.ragged) {
+        // the pass reduces the partials itself and stores the amax
+        AmaxIn src;
+        if (enqueue_amax_partials(&x, &m.numel, 1, workspace, s, &src) != NVFP4_OK)
+            return NVFP4_ERR_HIP;
+        src.store = amax_out;
+        return enqueue_fake_quant(x, y, cols, m, src, s);
+    }
     float* a = ws_amax(workspace, amax_out);
     if (enqueue_amax_ws(&x, &m.numel, 1, workspace, a, s) != NVFP4_OK)
         return NVFP4_ERR_HIP;
@@ -2173,6 +2389,13 @@ nvfp4_status nvfp4_quantize_pack_ws(const void* x, int64_t rows, int64_t cols, f
         return NVFP4_ERR_OVERLAP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
+    if (!m.ragged) {
+        AmaxIn src;
+        if (enqueue_amax_partials(&x, &m.numel, 1, workspace, s, &src) != NVFP4_OK)
+            return NVFP4_ERR_HIP;
+        src.store = amax_out;
+        return enqueue_quantize_pack(x, cols, m, packed, scales, global_scale, src, s);
+    }
     float* a = ws_amax(workspace, amax_out);
     if (enqueue_amax_ws(&x, &m.numel, 1, workspace, a, s) != NVFP4_OK)
         return NVFP4_ERR_HIP;
@@ -2204,9 +2427,25 @@ nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols,
         return NVFP4_ERR_OVERLAP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
+    const ObserverArgs obs{{state0, state1}, {mode0, mode1}, {decay0, decay1}};
+    const int64_t nh = 2 * m.nblocks;
+    const unsigned grid = persistent_grid(nh, (int64_t)kThreads * kUnroll, quant_wg_per_cu(nh, NVFP4_FQ_WG_PER_CU));
+    if (m.numel > 0 && !m.ragged) {
+        // the amax pass (which also copies the states), then one pass that reduces
+        // the partials into *cur, steps the observers and fake-quantizes with the
+        // new states
+        AmaxIn src;
+        if (enqueue_amax_partials(&x, &m.numel, 1, workspace, s, &src, obs, two ? 2 : 1) != NVFP4_OK)
+            return NVFP4_ERR_HIP;
+        src.store = cur;
+        if (!two)
+            return enqueue_fake_quant(x, y0, cols, m, src, s);
+        k_fake_quant_dual<true><<<grid, kThreads, 0, s>>>(static_cast<const uint4*>(x), static_cast<uint4*>(y0),
+                                                          static_cast<uint4*>(y1), nh, src);
+        return launched();
+    }
     // the amax pass, then one workgroup reduces its partial maxima into *cur and
     // steps both observers on it
-    const ObserverArgs obs{{state0, state1}, {mode0, mode1}, {decay0, decay1}};
     if (enqueue_amax_ws(&x, &m.numel, 1, workspace, cur, s, obs, two ? 2 : 1) != NVFP4_OK)
         return NVFP4_ERR_HIP;
     if (m.numel == 0)
@@ -2219,10 +2458,8 @@ nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols,
         st = enqueue_fake_quant(x, swap ? y1 : y0, cols, m, swap ? state1 : state0, s);
         return st != NVFP4_OK ? st : enqueue_fake_quant(x, swap ? y0 : y1, cols, m, swap ? state0 : state1, s);
     }
-    const int64_t nh = 2 * m.nblocks;
-    k_fake_quant_dual<<<persistent_grid(nh, (int64_t)kThreads * kUnroll, quant_wg_per_cu(nh, NVFP4_FQ_WG_PER_CU)),
-                        kThreads, 0, s>>>(static_cast<const uint4*>(x), static_cast<uint4*>(y0),
-                                          static_cast<uint4*>(y1), nh, state0, state1);
+    k_fake_quant_dual<false><<<grid, kThreads, 0, s>>>(static_cast<const uint4*>(x), static_cast<uint4*>(y0),
+                                                       static_cast<uint4*>(y1), nh, AmaxIn{{state0, state1}});
     return launched();
 }
 

@@ -225,10 +225,13 @@ nvfp4_status nvfp4_observer_update(float* state, const float* cur, int mode, flo
 /*
  * Workspace calls.  nvfp4_fake_quant and nvfp4_quantize_pack without amax_in
  * clear the amax, run the amax pass (one atomic max per workgroup into the
- * amax), then the quantizing pass.  The calls below take a caller-owned
- * workspace instead: the amax pass leaves one partial maximum per workgroup
- * there and a one-workgroup launch reduces them, so no atomics contend at the
- * end of the pass (3-4 us on 32-64 MB tensors).  Same results, bit for bit.
+ * amax), then the quantizing pass: three launches.  The calls below take a
+ * caller-owned workspace instead: the amax pass leaves one partial maximum per
+ * workgroup there, and every workgroup of the quantizing pass reduces them
+ * itself (workgroup 0 stores the amax), so there is no clearing launch and no
+ * atomic: two launches, 3-6 us less on 32-112 MB tensors.  Same results, bit
+ * for bit.  (Rows whose length is not a multiple of 16 take one more launch,
+ * which reduces the partials before the quantizing pass.)
  *
  *   workspace  device memory of NVFP4_WORKSPACE_BYTES bytes, 256-byte aligned,
  *              owned by the caller.  Its contents on entry do not matter and are
@@ -288,8 +291,12 @@ nvfp4_status nvfp4_fake_quant_group_ws(const void* const* xs, void* const* ys, c
  *   mode_i, decay_i as for nvfp4_observer_update
  *   workspace       as for the workspace calls above (NVFP4_WORKSPACE_BYTES,
  *                   256-byte aligned, caller-owned, contents irrelevant)
- * Launches: the amax pass (partial maxima into the workspace), one workgroup
- * that reduces them into *cur and steps the observers, and the fake-quant pass.
+ * Launches: the amax pass (partial maxima into the workspace, and a copy of
+ * the states), then the fake-quant pass, whose every workgroup reduces the
+ * partials and steps the observers from the copied states (workgroup 0 stores
+ * *cur and the new states).  Rows whose length is not a multiple of 16, and
+ * rows == 0, take a one-workgroup launch for the reduction and the steps in
+ * between.
  * x, y0 and y1 may be NULL when rows == 0; the states still step on *cur = +0.
  * The amax is the local one: a data-parallel caller that all-reduces the step
  * amax before the observer update uses the separate calls instead.
