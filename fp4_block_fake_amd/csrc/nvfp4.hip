@@ -141,6 +141,19 @@ namespace {
 #ifndef NVFP4_AMAX_ALLOC_BYTES
 #define NVFP4_AMAX_ALLOC_BYTES (192LL << 20)  // bytes at the end of an amax pass read with allocating loads
 #endif
+// The same for the amax pass in front of a quantizing pass over a tensor below
+// NVFP4_MID_BYTES: quantize-pack (QP) and fake-quant (FQ: also the dual, group
+// and observe calls).  Measured on MI355X (warm loops, 0-256 MB swept): fake-
+// quant, which writes as many bytes as it reads, gains most from finding all of
+// x in the cache; quantize-pack was fastest with only the last 8-16 MB
+// allocated (64 MB tensor: 28.6 -> 25.8 us; 112 MB: 42.0 -> 40.6 us), its amax
+// pass then streaming like the rest.  Above NVFP4_MID_BYTES both keep 192 MB.
+#ifndef NVFP4_QP_AMAX_ALLOC_MID
+#define NVFP4_QP_AMAX_ALLOC_MID (16LL << 20)
+#endif
+#ifndef NVFP4_FQ_AMAX_ALLOC_MID
+#define NVFP4_FQ_AMAX_ALLOC_MID NVFP4_AMAX_ALLOC_BYTES
+#endif
 #ifndef NVFP4_FQ_NT_LD
 #define NVFP4_FQ_NT_LD 1
 #endif
@@ -1633,7 +1646,8 @@ nvfp4_status launched()
 
 // The amax pass's description of up to NVFP4_AMAX_GROUP_MAX tensors; *chunks
 // receives the number of chunks it walks.
-AmaxGroup amax_group(const void* const* xs, const int64_t* numels, int n, int64_t* chunks)
+AmaxGroup amax_group(const void* const* xs, const int64_t* numels, int n, int64_t* chunks,
+                     int64_t alloc_bytes = NVFP4_AMAX_ALLOC_BYTES)
 {
     AmaxGroup g{};
     constexpr int64_t kChunk = (int64_t)kThreads * kAmaxUnroll;
@@ -1647,10 +1661,10 @@ AmaxGroup amax_group(const void* const* xs, const int64_t* numels, int n, int64_
         c += (g.nvec[i] + kChunk - 1) / kChunk;
         g.chunk_end[i] = c;
     }
-    // Only the last NVFP4_AMAX_ALLOC_BYTES of the group are read with allocating
-    // loads: that is what the Infinity Cache still holds when the quantizing pass
-    // over the same tensor gets there; the rest streams past the caches.
-    const int64_t alloc_chunks = (int64_t)NVFP4_AMAX_ALLOC_BYTES / (kChunk * 16);
+    // Only the last alloc_bytes of the group are read with allocating loads: that
+    // is what the Infinity Cache still holds when the quantizing pass over the same
+    // tensor gets there; the rest streams past the caches.
+    const int64_t alloc_chunks = alloc_bytes / (kChunk * 16);
     g.alloc_from = c > alloc_chunks ? c - alloc_chunks : 0;
     *chunks = c;
     return g;
@@ -1658,10 +1672,10 @@ AmaxGroup amax_group(const void* const* xs, const int64_t* numels, int n, int64_
 
 // Enqueue max|x| of up to NVFP4_AMAX_GROUP_MAX tensors into *amax (atomic max).
 nvfp4_status enqueue_amax(const void* const* xs, const int64_t* numels, int n, float* amax,
-                          hipStream_t stream)
+                          hipStream_t stream, int64_t alloc_bytes = NVFP4_AMAX_ALLOC_BYTES)
 {
     int64_t chunks;
-    const AmaxGroup g = amax_group(xs, numels, n, &chunks);
+    const AmaxGroup g = amax_group(xs, numels, n, &chunks, alloc_bytes);
     k_amax<false><<<persistent_grid(chunks, 1, NVFP4_AMAX_WG_PER_CU), kThreads, 0, stream>>>(g, amax, nullptr);
     return launched();
 }
@@ -1696,18 +1710,26 @@ nvfp4_status enqueue_reset(float* amax, hipStream_t s)
     return launched();
 }
 
-nvfp4_status enqueue_amax_one(const void* x, int64_t numel, float* amax, hipStream_t stream)
+nvfp4_status enqueue_amax_one(const void* x, int64_t numel, float* amax, hipStream_t stream,
+                              int64_t alloc_bytes = NVFP4_AMAX_ALLOC_BYTES)
 {
     nvfp4_status st = enqueue_reset(amax, stream);
     if (st != NVFP4_OK || numel == 0)
         return st;
-    return enqueue_amax(&x, &numel, 1, amax, stream);
+    return enqueue_amax(&x, &numel, 1, amax, stream, alloc_bytes);
 }
 
 // Workgroups per CU of a quantizing pass over nhalves half blocks.
 int quant_wg_per_cu(int64_t nhalves, int large)
 {
     return nhalves * 16 < NVFP4_MID_BYTES ? NVFP4_MID_WG_PER_CU : large;
+}
+
+// Bytes at the end of the amax pass in front of a quantizing pass that are read
+// with allocating loads, for bytes of input (mid: the size below NVFP4_MID_BYTES).
+int64_t amax_alloc_bytes(int64_t bytes, int64_t mid)
+{
+    return bytes < NVFP4_MID_BYTES ? mid : NVFP4_AMAX_ALLOC_BYTES;
 }
 
 // One fake-quant launch of a single tensor with its amax from src (partials
@@ -1788,10 +1810,10 @@ static_assert(kPriorOffset >= 4 && kPriorOffset + 8 <= kPartialsOffset, "workspa
 
 nvfp4_status enqueue_amax_partials(const void* const* xs, const int64_t* numels, int n, void* ws,
                                    hipStream_t stream, AmaxIn* src, const ObserverArgs& obs = ObserverArgs{},
-                                   int nobs = 0)
+                                   int nobs = 0, int64_t alloc_bytes = NVFP4_AMAX_ALLOC_BYTES)
 {
     int64_t chunks;
-    AmaxGroup g = amax_group(xs, numels, n, &chunks);
+    AmaxGroup g = amax_group(xs, numels, n, &chunks, alloc_bytes);
     unsigned grid = persistent_grid(chunks, 1, NVFP4_AMAX_WG_PER_CU);
     if (grid > (unsigned)kMaxPartials)
         grid = (unsigned)kMaxPartials;
@@ -2116,7 +2138,7 @@ nvfp4_status nvfp4_fake_quant(const void* x, void* y, int64_t rows, int64_t cols
     (void)hipGetLastError();
     const float* a = amax_in;
     if (!a) {
-        st = enqueue_amax_one(x, n, amax_out, s);
+        st = enqueue_amax_one(x, n, amax_out, s, amax_alloc_bytes(2 * n, NVFP4_FQ_AMAX_ALLOC_MID));
         if (st != NVFP4_OK)
             return st;
         a = amax_out;
@@ -2196,8 +2218,12 @@ nvfp4_status nvfp4_fake_quant_group_ws(const void* const* xs, void* const* ys, c
     }
     if (any && whole_blocks) {
         // one group launch, which reduces the partials itself and stores the amax
+        int64_t total = 0;
+        for (int i = 0; i < n; ++i)
+            total += 2 * numels[i];
         AmaxIn src;
-        if (enqueue_amax_partials(xs, numels, n, workspace, s, &src) != NVFP4_OK)
+        if (enqueue_amax_partials(xs, numels, n, workspace, s, &src, ObserverArgs{}, 0,
+                                  amax_alloc_bytes(total, NVFP4_FQ_AMAX_ALLOC_MID)) != NVFP4_OK)
             return NVFP4_ERR_HIP;
         src.store = amax_out;
         return enqueue_group_fake_quant(xs, ys, rows, cols, n, src, s);
@@ -2278,7 +2304,7 @@ nvfp4_status nvfp4_quantize_pack(const void* x, int64_t rows, int64_t cols,
     (void)hipGetLastError();
     const float* a = amax_in;
     if (!a) {
-        st = enqueue_amax_one(x, n, amax_out, s);
+        st = enqueue_amax_one(x, n, amax_out, s, amax_alloc_bytes(2 * n, NVFP4_QP_AMAX_ALLOC_MID));
         if (st != NVFP4_OK)
             return st;
         a = amax_out;
@@ -2355,7 +2381,8 @@ nvfp4_status nvfp4_fake_quant_ws(const void* x, void* y, int64_t rows, int64_t c
     if (!m.ragged) {
         // the pass reduces the partials itself and stores the amax
         AmaxIn src;
-        if (enqueue_amax_partials(&x, &m.numel, 1, workspace, s, &src) != NVFP4_OK)
+        if (enqueue_amax_partials(&x, &m.numel, 1, workspace, s, &src, ObserverArgs{}, 0,
+                                  amax_alloc_bytes(2 * m.numel, NVFP4_FQ_AMAX_ALLOC_MID)) != NVFP4_OK)
             return NVFP4_ERR_HIP;
         src.store = amax_out;
         return enqueue_fake_quant(x, y, cols, m, src, s);
@@ -2391,7 +2418,8 @@ nvfp4_status nvfp4_quantize_pack_ws(const void* x, int64_t rows, int64_t cols, f
     (void)hipGetLastError();
     if (!m.ragged) {
         AmaxIn src;
-        if (enqueue_amax_partials(&x, &m.numel, 1, workspace, s, &src) != NVFP4_OK)
+        if (enqueue_amax_partials(&x, &m.numel, 1, workspace, s, &src, ObserverArgs{}, 0,
+                                  amax_alloc_bytes(2 * m.numel, NVFP4_QP_AMAX_ALLOC_MID)) != NVFP4_OK)
             return NVFP4_ERR_HIP;
         src.store = amax_out;
         return enqueue_quantize_pack(x, cols, m, packed, scales, global_scale, src, s);
@@ -2435,7 +2463,8 @@ nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols,
         // the partials into *cur, steps the observers and fake-quantizes with the
         // new states
         AmaxIn src;
-        if (enqueue_amax_partials(&x, &m.numel, 1, workspace, s, &src, obs, two ? 2 : 1) != NVFP4_OK)
+        if (enqueue_amax_partials(&x, &m.numel, 1, workspace, s, &src, obs, two ? 2 : 1,
+                                  amax_alloc_bytes(2 * m.numel, NVFP4_FQ_AMAX_ALLOC_MID)) != NVFP4_OK)
             return NVFP4_ERR_HIP;
         src.store = cur;
         if (!two)
