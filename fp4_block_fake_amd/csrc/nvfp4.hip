@@ -124,7 +124,7 @@ namespace {
 #define NVFP4_TILE_SMALL_M 128
 #endif
 #ifndef NVFP4_TILE_DEPTH
-#define NVFP4_TILE_DEPTH 4        // K steps of weight loads in flight per tiled-linear wave (even)
+#define NVFP4_TILE_DEPTH 6        // K steps of weight loads in flight per tiled-linear wave (even)
 #endif
 #ifndef NVFP4_DQ_WG_PER_CU
 #define NVFP4_DQ_WG_PER_CU 32

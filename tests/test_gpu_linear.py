@@ -94,11 +94,12 @@ def test_linear_within_the_rounding_bound(m, n, k, with_bias):
 # aligned (k % 64 == 32, up to 16 rows of x), one workgroup per CU for widths n = 4096 c
 # (c tiles of 16 weight rows per workgroup, c = 1, 3, 5, 8), several 16-row tiles of x,
 # and the tiled kernel from 65 rows of x (64- and 128-row tiles, 32- and 64-wide K steps,
-# ragged rows of x and a width that is not a multiple of the 128-row weight tile).
+# ragged rows of x, many x tiles, and a width that is not a multiple of the 128-row weight
+# tile).
 @pytest.mark.parametrize("m,n,k", [(5, 40, 288), (16, 130, 800), (4, 12288, 256), (2, 20480, 128),
                                    (64, 32768, 64), (33, 4096, 96), (48, 8192, 160),
                                    (129, 256, 1024), (300, 200, 2048), (1024, 520, 256), (128, 4096, 4096),
-                                   (128, 96, 192)])
+                                   (128, 96, 192), (600, 200, 512), (512, 130, 96), (1100, 1024, 2048)])
 def test_linear_launch_shapes(m, n, k):
     packed, scales, gs = weight(n, k, 11 * m + n + k)
     rng = np.random.default_rng(m * 5 + n + k)
@@ -112,8 +113,9 @@ def test_linear_launch_shapes(m, n, k):
 
 def test_c5_weight_as_a_layer():
     """The c5 weight (28672 x 8192) quantized on the device, then used as a linear layer
-    on 16 tokens (the register-decode kernel) and on 256 tokens (the tiled kernel), the
-    shapes the bench times; sampled output columns are checked against the oracle."""
+    on 16 tokens (the register-decode kernel) and on 256 and 1024 tokens (the tiled
+    kernel), shapes the bench times; sampled output columns are checked against the
+    oracle."""
     w = synth.c5_weight()
     say("linear on the c5 weight")
     packed, scales, gs = nv.nvfp4_quantize_pack(dev(w))
@@ -124,7 +126,7 @@ def test_c5_weight_as_a_layer():
     p_ref, s_ref, g_ref = oracle.quantize(w[cols], oracle.amax(w))
     assert_same(p_rows, p_ref, "c5 packed rows")
     assert_same(s_rows, s_ref, "c5 scale rows")
-    for m in (16, 256):
+    for m in (16, 256, 1024):
         x = synth.to_bf16_bits(rng.standard_normal((m, w.shape[1])).astype(np.float32))
         y = nv.nvfp4_linear(dev(x), packed, scales, gs)
         torch.cuda.synchronize()
