@@ -811,7 +811,7 @@ __device__ __forceinline__ void resolve_amax(const PartialLoads& p, const AmaxIn
 
 // The amax of a single-amax pass: issue the loads it needs (before the loads
 // of x), then finish it once they are in.  Without partials the pass reads
-// *src.amax[0] and behaves as before partials existed.
+// *src.amax[0] directly, and no fence orders that load against the loads of x.
 template <bool Partials>
 struct AmaxOfPass {
     PartialLoads p;
