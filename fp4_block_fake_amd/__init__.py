@@ -385,9 +385,12 @@ class FakeQuantSTE(torch.autograd.Function):
     estimator, verl QATLinear page section 2)."""
 
     @staticmethod
-    def forward(ctx, x, amax_in=None):
+    def forward(ctx, x, amax_in=None, workspace=None):
+        # without amax_in, a workspace (when given) saves the clearing launch
+        if amax_in is None and workspace is not None:
+            return nvfp4_fake_quant_ws(x.contiguous(), workspace=workspace)
         return nvfp4_fake_quant(x.contiguous(), amax_in=amax_in)
 
     @staticmethod
     def backward(ctx, grad_out):
-        return grad_out, None
+        return grad_out, None, None
