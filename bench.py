@@ -59,8 +59,15 @@ def log(*a):
 
 
 def kernel_source_hash():
-    with open(os.path.join(ROOT, "fp4_block_fake_amd", "csrc", "nvfp4.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """SHA-256 (first 16 hex digits) over the kernel sources, file names included."""
+    csrc = os.path.join(ROOT, "fp4_block_fake_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel, workload):

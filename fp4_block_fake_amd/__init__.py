@@ -1,7 +1,7 @@
 """Python binding of libnvfp4.so: NVFP4 two-level block quantization on MI355X.
 
 Argument marshalling only.  Every step of the computation runs in the HIP
-kernels of ``csrc/nvfp4.hip``; torch supplies device memory and the current
+kernels in ``csrc/``; torch supplies device memory and the current
 stream.  The functions carry the C ABI's names and semantics (see
 ``include/nvfp4.h``); outputs that are not passed in are allocated here with
 torch.  Importing this package fails when the library has not been built.

@@ -1,0 +1,433 @@
+// The linear layer over a packed NVFP4 weight: bf16 MFMA with the weight decoded
+// in registers (included by nvfp4.hip).
+
+#ifndef NVFP4_LINEAR_HPP
+#define NVFP4_LINEAR_HPP
+
+#include "device.hpp"
+
+namespace {
+
+// ---------------------------------------------------------------- linear over a packed weight
+//
+// y[m, n] = bf16( sum_k x[m, k] * w[n, k] + b[n] ), w = the bf16 weight that
+// dequant-unpack would write (VideoX-Fun page, the per-forward reconstruction:
+// the packed weight is dequantized to bf16 and the layer's linear runs on it).
+// Here the dequantization happens in registers, straight into the B operand of
+// bf16 MFMAs, so the bf16 weight never exists in memory: the weight costs 0.5625
+// bytes per element of HBM traffic instead of 2 (read) + 2 (write) + 2 (read).
+//
+// v_mfma_f32_16x16x32_bf16 operand layout (checked on MI355X): lane l holds
+// A[l % 16][8 (l / 16) .. + 8], B[8 (l / 16) .. + 8][l % 16], and accumulator
+// element i of lane l is D[4 (l / 16) + i][l % 16].  The sum over k may visit k
+// in any order, so in a KS-wide step lane group g = l / 16 takes the KS / 4
+// contiguous k from KS g / 4 for all KS / 32 MFMAs of the step (MFMA q uses the
+// q-th 8 of them), for A and B alike: per weight row, KS / 128 16-byte loads of
+// codes and one load of their KS / 64 scale bytes; per x row, KS / 32 16-byte
+// loads.
+//
+// A workgroup computes a tile of 16 MT rows of x by 16 NT rows of w; its W
+// waves split K (steps interleaved) and their partial sums meet in LDS, added in
+// wave order, so results do not depend on timing.  Rows past the end of x or w
+// read row 0 instead: accumulator element D[m][n] depends only on row m of x
+// and row n of w, and those rows are never stored, so every load stays
+// unconditional (no branch splits the load pipeline).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLinDepth = NVFP4_LIN_DEPTH;
+constexpr size_t kLinLdsBudget = 64 * 1024 - 128 * sizeof(float);   // beside the sd table
+
+// Eight codes (one dword) -> the B operand: their bf16 values decode * sd, as
+// dequant-unpack writes them.
+__device__ __forceinline__ bf16x8 decode_operand(uint32_t c, float sd)
+{
+    return __builtin_bit_cast(bf16x8, decode_half(c, sd));
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int i)
+{
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Dynamic LDS of the linear kernel: with SL, the scale rows of the workgroup's
+// weight tiles during the K loop; then the partial sums of waves 1..W-1.
+extern __shared__ __align__(16) uint8_t lin_lds[];
+
+template <int MT, int NT, int W, int KS, bool SL>
+__global__ __launch_bounds__(64 * W) void k_linear(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                     const uint32_t* __restrict__ packed,
+                                                     const uint8_t* __restrict__ scales,
+                                                     const float* __restrict__ gs_in, int64_t N,
+                                                     const uint16_t* __restrict__ bias,
+                                                     uint16_t* __restrict__ y)
+{
+    static_assert(KS == 128 || KS == 256, "step width");
+    constexpr int kQ = KS / 32;            // MFMAs per weight tile and step
+    constexpr int kCv = KS / 128;          // 16-byte code loads per row and step
+    __shared__ float sd_of[128];
+    f32x4 (*partial)[MT * NT][64] = reinterpret_cast<f32x4 (*)[MT * NT][64]>(lin_lds);
+    const float gs = *gs_in;
+    if (threadIdx.x < 128)
+        sd_of[threadIdx.x] = e4m3_decode(threadIdx.x) / gs;
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * NT, m0 = (int64_t)blockIdx.y * 16 * MT;
+    const int64_t cw = K / 8, sw = K / 16;           // code dwords and scale bytes per weight row
+    const bool scale_dword = KS == 256 && (sw & 3) == 0 && (SL || ((uintptr_t)scales & 3) == 0);
+    if (SL) {
+        // The workgroup's scale rows are contiguous: one coalesced copy into LDS
+        // (16-byte pieces when aligned, 2-byte otherwise; every row is an even
+        // number of bytes).
+        const int64_t rows = N - n0 < 16 * NT ? N - n0 : 16 * NT;
+        const uint8_t* src = scales + n0 * sw;
+        const int64_t bytes = rows * sw;
+        if (((uintptr_t)src & 15) == 0) {
+            for (int64_t i = threadIdx.x; i < bytes / 16; i += 64 * W)
+                reinterpret_cast<uint4*>(lin_lds)[i] = reinterpret_cast<const uint4*>(src)[i];
+            for (int64_t i = bytes / 16 * 16 + 2 * threadIdx.x; i < bytes; i += 2 * 64 * W)
+                *reinterpret_cast<uint16_t*>(lin_lds + i) = *reinterpret_cast<const uint16_t*>(src + i);
+        } else {
+            for (int64_t i = 2 * threadIdx.x; i < bytes; i += 2 * 64 * W)
+                *reinterpret_cast<uint16_t*>(lin_lds + i) = *reinterpret_cast<const uint16_t*>(src + i);
+        }
+    }
+    __syncthreads();
+
+    const uint32_t* wrow[NT];
+    const uint8_t* srow[NT];               // without SL: the scale row in HBM
+    uint32_t soff[NT];                     // with SL: the scale row's offset in LDS
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int64_t n = n0 + 16 * t + r;
+        wrow[t] = packed + (n < N ? n : 0) * cw;
+        srow[t] = scales + (n < N ? n : 0) * sw;
+        soff[t] = (uint32_t)((n < N ? 16 * t + r : 0) * sw);
+    }
+    // scale bytes [k / 16, k / 16 + bytes) of weight tile t (bytes = 1, 2 or 4)
+    auto scale_bytes = [&](int t, int64_t k, int bytes) -> uint32_t {
+        if (SL) {
+            const uint8_t* sp = lin_lds + soff[t] + k / 16;
+            if (bytes == 1)
+                return *sp;
+            if (bytes == 2 || !scale_dword)
+                return bytes == 2 ? *reinterpret_cast<const uint16_t*>(sp)
+                                  : (uint32_t)*reinterpret_cast<const uint16_t*>(sp) |
+                                    ((uint32_t)*reinterpret_cast<const uint16_t*>(sp + 2) << 16);
+            return *reinterpret_cast<const uint32_t*>(sp);
+        }
+        const uint8_t* sp = srow[t] + k / 16;
+        if (bytes == 1)
+            return *sp;
+        if (bytes == 2)
+            return *reinterpret_cast<const uint16_t*>(sp);
+        if (scale_dword)
+            return *reinterpret_cast<const uint32_t*>(sp);
+        return (uint32_t)*reinterpret_cast<const uint16_t*>(sp) |
+               ((uint32_t)*reinterpret_cast<const uint16_t*>(sp + 2) << 16);
+    };
+    const uint16_t* xrow[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int64_t m = m0 + 16 * i + r;
+        xrow[i] = x + (m < M ? m : 0) * K;
+    }
+
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // The weight operands of a step (codes and scale bytes, the HBM stream) are
+    // loaded kLinDepth steps ahead; x (from L2) one step ahead.
+    struct WOp {
+        uint4 c[NT][kCv];
+        uint32_t sc[NT];                   // KS / 64 scale bytes, lowest first
+    };
+    struct XOp {
+        uint4 a[MT][kQ];
+    };
+    auto load_w = [&](int64_t st, WOp& o) {
+        const int64_t k0 = st * KS + (KS / 4) * g;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int v = 0; v < kCv; ++v)
+                o.c[t][v] = *reinterpret_cast<const uint4*>(wrow[t] + k0 / 8 + 4 * v);
+            o.sc[t] = scale_bytes(t, k0, KS / 64);
+        }
+    };
+    auto load_x = [&](int64_t st, XOp& o) {
+        const int64_t k0 = st * KS + (KS / 4) * g;
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int q = 0; q < kQ; ++q)
+                o.a[i][q] = *reinterpret_cast<const uint4*>(xrow[i] + k0 + 8 * q);
+    };
+    auto mma_step = [&](const WOp& o, const XOp& xo) {
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const float sd = sd_of[(o.sc[t] >> (8 * (q / 2))) & 0x7Fu];
+                const bf16x8 b = decode_operand(dword_of(o.c[t][q / 4], q % 4), sd);
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xo.a[i][q]), b,
+                                                                        acc[i][t], 0, 0, 0);
+            }
+        }
+    };
+    // A wave's j-th step uses ring[j % D] and xbuf[j % 2]; D is even, so both
+    // indices are compile-time constants in the unrolled body.
+    static_assert(kLinDepth % 2 == 0, "the x double buffer alternates with the ring");
+    const int64_t steps = K / KS;
+    WOp ring[kLinDepth];
+    XOp xbuf[2];
+#pragma unroll
+    for (int d = 0; d < kLinDepth; ++d)
+        if (wave + d * W < steps)
+            load_w(wave + d * W, ring[d]);
+    if (wave < steps)
+        load_x(wave, xbuf[0]);
+    for (int64_t st = wave; st < steps; st += kLinDepth * W) {
+#pragma unroll
+        for (int d = 0; d < kLinDepth; ++d) {
+            const int64_t at = st + d * W;
+            if (at < steps) {
+                if (at + W < steps)
+                    load_x(at + W, xbuf[(d + 1) % 2]);
+                mma_step(ring[d], xbuf[d % 2]);
+                if (at + kLinDepth * W < steps)
+                    load_w(at + kLinDepth * W, ring[d]);
+            }
+        }
+    }
+    // K % KS: 32-wide steps shared out over the waves, in the plain layout
+    // (lane group g takes k in [8 g, 8 g + 8) of the step)
+    for (int64_t kt = steps * KS + 32 * wave; kt < K; kt += 32 * W) {
+        const int64_t k0 = kt + 8 * g;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const bf16x8 b = decode_operand(wrow[t][k0 / 8], sd_of[scale_bytes(t, k0, 1) & 0x7Fu]);
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const uint4 a = *reinterpret_cast<const uint4*>(xrow[i] + k0);
+                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, acc[i][t],
+                                                                    0, 0, 0);
+            }
+        }
+    }
+
+    // waves 1..W-1 hand their partial sums to wave 0, which adds them in order
+    // (through the LDS the scales used, once every wave is past the K loop)
+    if (SL)
+        __syncthreads();
+    if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                partial[wave - 1][i * NT + t][lane] = acc[i][t];
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            f32x4 v = acc[i][t];
+#pragma unroll
+            for (int w = 0; w < W - 1; ++w)
+                v += partial[w][i * NT + t][lane];
+            const int64_t n = n0 + 16 * t + r;
+            if (n >= N)
+                continue;
+            const float b = bias ? bf16_value(bias[n]) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t m = m0 + 16 * i + 4 * g + e;
+                if (m < M) {
+                    const f32x2 o = {v[e] + b, 0.0f};
+                    y[m * N + n] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(o, bf16x2)) & 0xFFFFu);
+                }
+            }
+        }
+    }
+}
+
+// The linear layer for many rows of x.  A workgroup covers 32 MW rows of x and
+// 32 NW kTileWaves weight rows.  The x tile of each K step goes through LDS
+// (double-buffered: the next step's tile is loaded while this one is used) and
+// is shared by the kTileWaves waves; each wave owns NW tiles of 32 weight rows
+// and decodes their codes straight into its B operands, so every weight is
+// decoded once per workgroup and used by MW MFMA tiles.  The waves split N, so
+// there are no partial sums to combine.  The tiles are 32 x 32 x 16 MFMAs, which
+// do twice the FLOPs per operand byte of 16 x 16 x 32 ones (half the LDS reads
+// of x per FLOP; measured 1.25x faster here).  Operand layouts (checked on
+// MI355X): lane l holds A[l % 32][8 (l / 32) .. +8] and B[8 (l / 32) .. +8][l % 32];
+// accumulator j of lane l is D[(j % 4) + 8 (j / 4) + 4 (l / 32)][l % 32].  Within a
+// K step, lane half h takes K indices [KS/2 h, KS/2 (h + 1)) in MFMA slices of 8,
+// for x and weights alike.
+constexpr int kTileWaves = NVFP4_TILE_WAVES;
+constexpr int kTileDepth = NVFP4_TILE_DEPTH;
+static_assert(kTileDepth % 2 == 0, "the x double buffer alternates with the weight ring");
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int MW, int NW, int KS>
+__global__ __launch_bounds__(64 * kTileWaves) void k_linear_tiled(const uint16_t* __restrict__ x, int64_t M,
+                                                                    int64_t K, const uint8_t* __restrict__ packed,
+                                                                    const uint8_t* __restrict__ scales,
+                                                                    const float* __restrict__ gs_in, int64_t N,
+                                                                    const uint16_t* __restrict__ bias,
+                                                                    uint16_t* __restrict__ y)
+{
+    static_assert(KS == 32 || KS == 64, "step width");
+    constexpr int kQ = KS / 16;                      // MFMA slices per step (and code dwords per lane)
+    constexpr int kRows = 32 * MW;
+    constexpr int kStride = KS + 8;
+    constexpr int kPieces = kRows * KS / 8;
+    constexpr int kPer = (kPieces + 64 * kTileWaves - 1) / (64 * kTileWaves);
+    __shared__ float sd_of[128];
+    uint16_t* xt = reinterpret_cast<uint16_t*>(lin_lds);     // [2][kRows][kStride]
+
+    const float gs = *gs_in;
+    if (threadIdx.x < 128)
+        sd_of[threadIdx.x] = e4m3_decode(threadIdx.x) / gs;
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int c = lane & 31, h = lane >> 5;
+    const int64_t m0 = (int64_t)blockIdx.x * kRows;
+    const int64_t n0 = ((int64_t)blockIdx.y * kTileWaves + wave) * 32 * NW;
+    const int64_t cb = K / 2, sb = K / 16;
+    const uint8_t* wrow[NW];
+    const uint8_t* srow[NW];
+#pragma unroll
+    for (int t = 0; t < NW; ++t) {
+        const int64_t n = n0 + 32 * t + c;
+        wrow[t] = packed + (n < N ? n : 0) * cb;
+        srow[t] = scales + (n < N ? n : 0) * sb;
+    }
+
+    auto load_x = [&](int64_t st, uint4 (&v)[kPer]) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int p = threadIdx.x + 64 * kTileWaves * j;
+            const int64_t m = m0 + p / (KS / 8);
+            v[j] = p < kPieces && m < M
+                       ? *reinterpret_cast<const uint4*>(x + m * K + st * KS + 8 * (p % (KS / 8)))
+                       : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto store_x = [&](int buf, const uint4 (&v)[kPer]) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int p = threadIdx.x + 64 * kTileWaves * j;
+            if (p < kPieces)
+                *reinterpret_cast<uint4*>(xt + (buf * kRows + p / (KS / 8)) * kStride + 8 * (p % (KS / 8))) = v[j];
+        }
+    };
+    // the lane's KS / 2 codes (kQ dwords) and their KS / 32 scale bytes, per weight tile
+    auto load_w = [&](int64_t st, uint32_t (&cw)[NW][kQ], uint32_t (&sc)[NW]) {
+        const int64_t k0 = st * KS + (KS / 2) * h;
+#pragma unroll
+        for (int t = 0; t < NW; ++t) {
+            if (KS == 64) {
+                const uint4 v = *reinterpret_cast<const uint4*>(wrow[t] + k0 / 2);
+                cw[t][0] = v.x;
+                cw[t][1] = v.y;
+                cw[t][kQ - 2] = v.z;
+                cw[t][kQ - 1] = v.w;
+                sc[t] = *reinterpret_cast<const uint16_t*>(srow[t] + k0 / 16);
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2*>(wrow[t] + k0 / 2);
+                cw[t][0] = v.x;
+                cw[t][kQ - 1] = v.y;
+                sc[t] = srow[t][k0 / 16];
+            }
+        }
+    };
+
+    f32x16 acc[MW][NW];
+#pragma unroll
+    for (int i = 0; i < MW; ++i)
+#pragma unroll
+        for (int t = 0; t < NW; ++t)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                acc[i][t][j] = 0.0f;
+    auto mma_step = [&](int buf, const uint32_t (&cw)[NW][kQ], const uint32_t (&sc)[NW]) {
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+            bf16x8 b[NW];
+#pragma unroll
+            for (int t = 0; t < NW; ++t)
+                b[t] = decode_operand(cw[t][q], sd_of[(sc[t] >> (8 * (q / 2))) & 0x7Fu]);
+#pragma unroll
+            for (int i = 0; i < MW; ++i) {
+                const uint4 a = *reinterpret_cast<const uint4*>(xt + (buf * kRows + 32 * i + c) * kStride +
+                                                                (KS / 2) * h + 8 * q);
+#pragma unroll
+                for (int t = 0; t < NW; ++t)
+                    acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b[t],
+                                                                        acc[i][t], 0, 0, 0);
+            }
+        }
+    };
+
+    const int64_t steps = K / KS;
+    uint4 xv[kPer];
+    uint32_t wc[kTileDepth][NW][kQ], wsb[kTileDepth][NW];
+#pragma unroll
+    for (int d = 0; d < kTileDepth; ++d)
+        if (d < steps)
+            load_w(d, wc[d], wsb[d]);
+    load_x(0, xv);
+    store_x(0, xv);
+    __syncthreads();
+    for (int64_t st0 = 0; st0 < steps; st0 += kTileDepth) {
+#pragma unroll
+        for (int d = 0; d < kTileDepth; ++d) {
+            const int64_t st = st0 + d;
+            if (st < steps) {
+                const bool more = st + 1 < steps;
+                if (more)
+                    load_x(st + 1, xv);
+                mma_step(d & 1, wc[d], wsb[d]);
+                if (st + kTileDepth < steps)
+                    load_w(st + kTileDepth, wc[d], wsb[d]);
+                if (more)
+                    store_x((d & 1) ^ 1, xv);
+                __syncthreads();
+            }
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+#pragma unroll
+        for (int t = 0; t < NW; ++t) {
+            const int64_t n = n0 + 32 * t + c;
+            if (n >= N)
+                continue;
+            const float b = bias ? bf16_value(bias[n]) : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int64_t m = m0 + 32 * i + (j % 4) + 8 * (j / 4) + 4 * h;
+                if (m < M) {
+                    const f32x2 o = {acc[i][t][j] + b, 0.0f};
+                    y[m * N + n] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(o, bf16x2)) & 0xFFFFu);
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+#endif  // NVFP4_LINEAR_HPP
