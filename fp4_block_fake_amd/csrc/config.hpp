@@ -40,6 +40,13 @@ namespace {
 #ifndef NVFP4_MID_BYTES
 #define NVFP4_MID_BYTES (256LL << 20)
 #endif
+// The two-output pass (dual fake-quant, observe step) below NVFP4_MID_BYTES.
+// Swept on the c4 activation observe step (one process): 6, 16, 24 or 32
+// workgroups per CU 41.0-41.4 us, 8 and 12 42.9-44.0 us; at 8 every workgroup
+// runs exactly two iterations in lockstep.
+#ifndef NVFP4_DUAL_MID_WG_PER_CU
+#define NVFP4_DUAL_MID_WG_PER_CU 16
+#endif
 #ifndef NVFP4_MID_WG_PER_CU
 #define NVFP4_MID_WG_PER_CU 8
 #endif

@@ -198,6 +198,12 @@ int quant_wg_per_cu(int64_t nhalves, int large)
     return nhalves * 16 < NVFP4_MID_BYTES ? NVFP4_MID_WG_PER_CU : large;
 }
 
+// Workgroups per CU of the two-output pass over nhalves half blocks.
+int dual_wg_per_cu(int64_t nhalves)
+{
+    return nhalves * 16 < NVFP4_MID_BYTES ? NVFP4_DUAL_MID_WG_PER_CU : NVFP4_FQ_WG_PER_CU;
+}
+
 // Bytes at the end of the amax pass in front of a quantizing pass that are read
 // with allocating loads, for bytes of input (mid: the size below NVFP4_MID_BYTES).
 int64_t amax_alloc_bytes(int64_t bytes, int64_t mid)
@@ -741,8 +747,7 @@ nvfp4_status nvfp4_fake_quant_dual(const void* x, int64_t rows, int64_t cols, co
         return st != NVFP4_OK ? st : enqueue_fake_quant(x, y1, cols, m, amax1, s);
     }
     const int64_t nh = 2 * m.nblocks;
-    k_fake_quant_dual<false><<<persistent_grid(nh, (int64_t)kThreads * kUnroll,
-                                               quant_wg_per_cu(nh, NVFP4_FQ_WG_PER_CU)),
+    k_fake_quant_dual<false><<<persistent_grid(nh, (int64_t)kThreads * kUnroll, dual_wg_per_cu(nh)),
                                kThreads, 0, s>>>(static_cast<const uint4*>(x), static_cast<uint4*>(y0),
                                                  static_cast<uint4*>(y1), nh, AmaxIn{{amax0, amax1}});
     return launched();
@@ -930,7 +935,8 @@ nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols,
     (void)hipGetLastError();
     const ObserverArgs obs{{state0, state1}, {mode0, mode1}, {decay0, decay1}};
     const int64_t nh = 2 * m.nblocks;
-    const unsigned grid = persistent_grid(nh, (int64_t)kThreads * kUnroll, quant_wg_per_cu(nh, NVFP4_FQ_WG_PER_CU));
+    const unsigned grid = persistent_grid(nh, (int64_t)kThreads * kUnroll,
+                                          two ? dual_wg_per_cu(nh) : quant_wg_per_cu(nh, NVFP4_FQ_WG_PER_CU));
     if (m.numel > 0 && !m.ragged) {
         // the amax pass (which also copies the states), then one pass that reduces
         // the partials into *cur, steps the observers and fake-quantizes with the
