@@ -33,22 +33,25 @@ namespace {
 #ifndef NVFP4_QP_WG_PER_CU
 #define NVFP4_QP_WG_PER_CU 64
 #endif
-// Tensors below NVFP4_MID_BYTES get at most NVFP4_MID_WG_PER_CU quantizing
-// workgroups per CU: each then covers several iterations (fewer table builds,
-// loads of the next iteration in flight), 2-4 us faster on 64-112 MB tensors
-// and slower on the 470 MB one.
+// Tensors below NVFP4_MID_BYTES get fewer quantizing workgroups per CU: each
+// then covers a few iterations (fewer table builds), 2-4 us faster on 64-112 MB
+// tensors and slower on the 470 MB one.  Swept per pass (one process, 5-24 per
+// CU): fake-quant was fastest at 7 (c4 activation 30.5 us against 31.3 at 8,
+// c4 weight 52.6 against 53.2), quantize-pack at 8 (c4 weight 40.9 against
+// 42.3 at 7); the two-output pass (dual fake-quant, observe step) at 6 or 16-32
+// (41.0-41.4 us against 42.9-44.0 at 8 and 12: at 8 every workgroup of the
+// c4 activation runs exactly two iterations in lockstep).
 #ifndef NVFP4_MID_BYTES
 #define NVFP4_MID_BYTES (256LL << 20)
 #endif
-// The two-output pass (dual fake-quant, observe step) below NVFP4_MID_BYTES.
-// Swept on the c4 activation observe step (one process): 6, 16, 24 or 32
-// workgroups per CU 41.0-41.4 us, 8 and 12 42.9-44.0 us; at 8 every workgroup
-// runs exactly two iterations in lockstep.
+#ifndef NVFP4_FQ_MID_WG_PER_CU
+#define NVFP4_FQ_MID_WG_PER_CU 7
+#endif
+#ifndef NVFP4_QP_MID_WG_PER_CU
+#define NVFP4_QP_MID_WG_PER_CU 8
+#endif
 #ifndef NVFP4_DUAL_MID_WG_PER_CU
 #define NVFP4_DUAL_MID_WG_PER_CU 16
-#endif
-#ifndef NVFP4_MID_WG_PER_CU
-#define NVFP4_MID_WG_PER_CU 8
 #endif
 // Partial maxima the workspace holds (one per amax workgroup), from byte 256.
 #define NVFP4_MAX_PARTIALS ((NVFP4_WORKSPACE_BYTES - 256) / 4)

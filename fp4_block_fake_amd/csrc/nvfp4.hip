@@ -193,15 +193,15 @@ nvfp4_status enqueue_amax_one(const void* x, int64_t numel, float* amax, hipStre
 }
 
 // Workgroups per CU of a quantizing pass over nhalves half blocks.
-int quant_wg_per_cu(int64_t nhalves, int large)
+int quant_wg_per_cu(int64_t nhalves, int mid, int large)
 {
-    return nhalves * 16 < NVFP4_MID_BYTES ? NVFP4_MID_WG_PER_CU : large;
+    return nhalves * 16 < NVFP4_MID_BYTES ? mid : large;
 }
 
 // Workgroups per CU of the two-output pass over nhalves half blocks.
 int dual_wg_per_cu(int64_t nhalves)
 {
-    return nhalves * 16 < NVFP4_MID_BYTES ? NVFP4_DUAL_MID_WG_PER_CU : NVFP4_FQ_WG_PER_CU;
+    return quant_wg_per_cu(nhalves, NVFP4_DUAL_MID_WG_PER_CU, NVFP4_FQ_WG_PER_CU);
 }
 
 // Bytes at the end of the amax pass in front of a quantizing pass that are read
@@ -226,7 +226,8 @@ nvfp4_status enqueue_fake_quant(const void* x, void* y, int64_t cols, const Matr
         return launched();
     }
     const int64_t nh = 2 * m.nblocks;
-    const dim3 grid(persistent_grid(nh, (int64_t)kThreads * kUnroll, quant_wg_per_cu(nh, NVFP4_FQ_WG_PER_CU)));
+    const dim3 grid(persistent_grid(nh, (int64_t)kThreads * kUnroll,
+                                    quant_wg_per_cu(nh, NVFP4_FQ_MID_WG_PER_CU, NVFP4_FQ_WG_PER_CU)));
     if (src.partials)
         k_fake_quant<true><<<grid, kThreads, 0, s>>>(static_cast<const uint4*>(x), static_cast<uint4*>(y), nh, src);
     else
@@ -254,7 +255,8 @@ nvfp4_status enqueue_quantize_pack(const void* x, int64_t cols, const Matrix& m,
         return launched();
     }
     const int64_t nh = 2 * m.nblocks;
-    const dim3 grid(persistent_grid(nh, (int64_t)kThreads * kUnroll, quant_wg_per_cu(nh, NVFP4_QP_WG_PER_CU)));
+    const dim3 grid(persistent_grid(nh, (int64_t)kThreads * kUnroll,
+                                    quant_wg_per_cu(nh, NVFP4_QP_MID_WG_PER_CU, NVFP4_QP_WG_PER_CU)));
     const uint4* xv = static_cast<const uint4*>(x);
     uint32_t* pv = reinterpret_cast<uint32_t*>(packed);
     if (src.partials)
@@ -347,7 +349,8 @@ struct FakeQuantBatch {
         if (g.count == 0)
             return NVFP4_OK;
         constexpr int64_t kChunk = (int64_t)kThreads * kUnroll;
-        const dim3 grid(persistent_grid(chunks, 1, quant_wg_per_cu(chunks * kChunk, NVFP4_FQ_WG_PER_CU)));
+        const dim3 grid(persistent_grid(chunks, 1, quant_wg_per_cu(chunks * kChunk, NVFP4_FQ_MID_WG_PER_CU,
+                                                                   NVFP4_FQ_WG_PER_CU)));
         if (src.partials)
             k_fake_quant_group<true><<<grid, kThreads, 0, s>>>(g, src);
         else
@@ -935,8 +938,9 @@ nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols,
     (void)hipGetLastError();
     const ObserverArgs obs{{state0, state1}, {mode0, mode1}, {decay0, decay1}};
     const int64_t nh = 2 * m.nblocks;
-    const unsigned grid = persistent_grid(nh, (int64_t)kThreads * kUnroll,
-                                          two ? dual_wg_per_cu(nh) : quant_wg_per_cu(nh, NVFP4_FQ_WG_PER_CU));
+    const int wg_per_cu = two ? dual_wg_per_cu(nh)
+                              : quant_wg_per_cu(nh, NVFP4_FQ_MID_WG_PER_CU, NVFP4_FQ_WG_PER_CU);
+    const unsigned grid = persistent_grid(nh, (int64_t)kThreads * kUnroll, wg_per_cu);
     if (m.numel > 0 && !m.ragged) {
         // the amax pass (which also copies the states), then one pass that reduces
         // the partials into *cur, steps the observers and fake-quantizes with the
