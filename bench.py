@@ -113,6 +113,38 @@ def cpu_baseline(x, rows):
     }
 
 
+def cpu_baseline_threads(x, rows, threads):
+    """The same oracle step over row shards on `threads` host threads (the oracle's C
+    calls release the GIL): the amax of the shards, reduced, then each shard quantized
+    with it.  Rows are independent, so the bytes equal the single-threaded run's."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    sample = np.ascontiguousarray(x[:rows])
+    n = sample.size
+    shards = [s for s in np.array_split(sample, threads) if s.size]
+    cols = sample.shape[1]
+    with ThreadPoolExecutor(threads) as pool:
+        t0 = time.perf_counter()
+        a = max(pool.map(oracle.amax, shards))
+        list(pool.map(lambda s: oracle.fake_quant(s, a), shards))
+        a = max(pool.map(oracle.amax, shards))
+        packs = list(pool.map(lambda s: oracle.quantize(s, a), shards))
+        list(pool.map(lambda p: oracle.dequantize(p[0], p[1], p[2], cols), packs))
+        dt = time.perf_counter() - t0
+    return {
+        "value": round(STEP_BYTES_PER_ELEM * n / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "first %d of %d rows (%d elements) in %d row shards, one step; %.2f s" % (
+            rows, x.shape[0], n, len(shards), dt),
+        "elements_per_s": round(n / dt, 1),
+    }
+
+
 def secondary(nv, synth, np, torch, dev, reps=20, only=None):
     """Per-call throughput on the other workloads (not part of the headline step).
 
@@ -506,6 +538,9 @@ def main():
     if args.cpu_rows > 0:
         log("cpu baseline: oracle on %d rows" % args.cpu_rows)
         result["cpu_baseline"] = cpu_baseline(x_host, min(args.cpu_rows, rows))
+        # the same oracle on the host's cores (at most 16: the machine's CPU share per GPU)
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        result["cpu_baseline_threads"] = cpu_baseline_threads(x_host, min(args.cpu_rows, rows), threads)
     print(json.dumps(result), flush=True)
 
 
