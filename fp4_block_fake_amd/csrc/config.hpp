@@ -88,6 +88,9 @@ namespace {
 #ifndef NVFP4_TILE_SMALL_M
 #define NVFP4_TILE_SMALL_M 128
 #endif
+#ifndef NVFP4_TILE_XCD_REMAP
+#define NVFP4_TILE_XCD_REMAP 1    // 1: the tiled linear groups each weight tile's x tiles on one XCD
+#endif
 #ifndef NVFP4_TILE_DEPTH
 #define NVFP4_TILE_DEPTH 6        // K steps of weight loads in flight per tiled-linear wave (even)
 #endif
