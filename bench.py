@@ -323,11 +323,23 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
                                                workspace=ws), 4.5625 * wc.numel())
         del yc, pc, scc
         # the c5 weight used as a linear layer (packed once), against unpack + torch's bf16
-        # GEMM and torch's bf16 GEMM on an already unpacked weight (context only)
+        # GEMM and torch's bf16 GEMM on an already unpacked weight (context only).  Calls
+        # on one weight find its 132 MB of codes and scales in the 256 MB Infinity Cache;
+        # the "rotated" figures cycle through three copies of it (396 MB), so every call
+        # reads its weight from HBM, as the layers of a model forward do.
         if only is None or only in "c5_weight_linear":
             packed, scales, gsc = nv.nvfp4_quantize_pack(wc)
             wdq = nv.nvfp4_dequant_unpack(packed, scales, gsc)
             del wc
+            copies = [(packed, scales), (packed.clone(), scales.clone()), (packed.clone(), scales.clone())]
+            turn = [0]
+
+            def rotated(f):
+                def call():
+                    p_, s_ = copies[turn[0] % 3]
+                    turn[0] += 1
+                    f(p_, s_)
+                return call
             gen = torch.Generator(device="cpu").manual_seed(7)
             for m in (1, 16, 64, 128, 256, 1024):
                 xm = torch.randn(m, k, generator=gen).to(torch.bfloat16).to(dev)
@@ -338,7 +350,16 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
                     lambda: torch.nn.functional.linear(xm, nv.nvfp4_dequant_unpack(packed, scales, gsc, y=wdq)),
                     1.0)["us"]
                 res["torch_bf16_gemm_us"] = timed(lambda: torch.nn.functional.linear(xm, wdq), 1.0)["us"]
+                if m <= 64:
+                    res["rotated_us"] = timed(rotated(lambda p_, s_: nv.nvfp4_linear(xm, p_, s_, gsc, y=ym)),
+                                              1.0)["us"]
+                    res["rotated_pct_of_hbm_peak"] = round(
+                        100 * (n * k * 0.5625 + 2.0 * m * (k + n)) / (res["rotated_us"] * 1e3) / HBM_PEAK_GBS, 1)
+                    res["unpack_plus_torch_gemm_rotated_us"] = timed(rotated(
+                        lambda p_, s_: torch.nn.functional.linear(xm, nv.nvfp4_dequant_unpack(p_, s_, gsc, y=wdq))),
+                        1.0)["us"]
                 out["c5_weight_linear_%dx8192_by_28672x8192" % m] = res
+            del copies
     return out
 
 

@@ -111,11 +111,49 @@ def test_linear_launch_shapes(m, n, k):
     check_bound(host(yt), x, packed, scales, gs, k, bias, "m=%d n=%d k=%d" % (m, n, k))
 
 
+# Up to 16 rows of x with wide K (1024 to 8192): every count of 16-row weight tiles per
+# workgroup (1-8 for widths n = 4096 c; 4, 2 and 1 otherwise, with a ragged last
+# workgroup), one to sixteen rows of x, 128- and 256-wide K steps over several rounds
+# of the eight waves.
+@pytest.mark.parametrize("m,n,k", [(1, 4096, 1024), (16, 12288, 2048), (5, 32768, 1024), (7, 16400, 1024),
+                                   (2, 8200, 2048), (16, 20480, 3072), (9, 24576, 1024), (1, 33, 1024),
+                                   (12, 8192, 8192), (3, 28672, 1024), (16, 16384, 1024)])
+def test_small_m_wide_k(m, n, k):
+    packed, scales, gs = weight(n, k, 13 * m + n + k)
+    rng = np.random.default_rng(m * 7 + n + 3 * k)
+    x = synth.to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    bias = synth.to_bf16_bits(rng.standard_normal(n).astype(np.float32))
+    say("linear small m, wide k: m=%d n=%d k=%d" % (m, n, k))
+    yt = nv.nvfp4_linear(dev(x), *to_dev_packed(packed, scales, gs), bias=dev(bias))
+    torch.cuda.synchronize()
+    check_bound(host(yt), x, packed, scales, gs, k, bias, "m=%d n=%d k=%d" % (m, n, k))
+
+
+@pytest.mark.parametrize("n,k", [(40, 1024), (12288, 3072)])
+def test_one_hot_rows_of_few_tokens_give_the_weight_exactly(n, k):
+    """Sixteen one-hot rows of x (columns spread over every K step, wave and lane group)
+    read back those columns of the decoded weight exactly."""
+    packed, scales, gs = weight(n, k, 3 * n + k)
+    rng = np.random.default_rng(n + k)
+    cols = np.concatenate([[0, k - 1], rng.choice(np.arange(1, k - 1), 14, replace=False)])
+    x = np.zeros((16, k), dtype=np.uint16)
+    x[np.arange(16), cols] = 0x3F80
+    say("linear one-hot, 16 rows, n=%d k=%d" % (n, k))
+    y = nv.nvfp4_linear(dev(x), *to_dev_packed(packed, scales, gs))
+    torch.cuda.synchronize()
+    got = oracle.bf16_array_to_f64(host(y))
+    want = oracle.bf16_array_to_f64(oracle.dequantize(packed, scales, gs, k)[:, cols].T)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, "one-hot rows: %d mismatches, first at %d: got %r want %r" % (
+        bad.size, bad[0], got.flat[bad[0]], want.flat[bad[0]])
+    assert (got != 0).sum() > got.size // 2
+
+
 def test_c5_weight_as_a_layer():
     """The c5 weight (28672 x 8192) quantized on the device, then used as a linear layer
-    on 16 tokens (the register-decode kernel) and on 256 and 1024 tokens (the tiled
-    kernel), shapes the bench times; sampled output columns are checked against the
-    oracle."""
+    on 1, 16 and 64 tokens (the register-decode kernel) and 256 and 1024 tokens (the
+    tiled kernel), shapes the bench times; sampled output columns are checked against
+    the oracle."""
     w = synth.c5_weight()
     say("linear on the c5 weight")
     packed, scales, gs = nv.nvfp4_quantize_pack(dev(w))
@@ -126,7 +164,7 @@ def test_c5_weight_as_a_layer():
     p_ref, s_ref, g_ref = oracle.quantize(w[cols], oracle.amax(w))
     assert_same(p_rows, p_ref, "c5 packed rows")
     assert_same(s_rows, s_ref, "c5 scale rows")
-    for m in (16, 256, 1024):
+    for m in (1, 16, 64, 256, 1024):
         x = synth.to_bf16_bits(rng.standard_normal((m, w.shape[1])).astype(np.float32))
         y = nv.nvfp4_linear(dev(x), packed, scales, gs)
         torch.cuda.synchronize()
