@@ -38,6 +38,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kLinDepth = NVFP4_LIN_DEPTH;
 constexpr size_t kLinLdsBudget = 64 * 1024 - 128 * sizeof(float);   // beside the sd table
 
+// 16-row tiles of x whose partial sums waves 1..W-1 of k_linear hand over per
+// round: all MT when they fit in kLinLdsBudget, else one per round.
+template <int MT, int NT, int W>
+constexpr int lin_partial_tiles()
+{
+    return (size_t)(W - 1) * MT * NT * 64 * sizeof(f32x4) <= kLinLdsBudget ? MT : 1;
+}
+
 // Eight codes (one dword) -> the B operand: their bf16 values decode * sd, as
 // dequant-unpack writes them.
 __device__ __forceinline__ bf16x8 decode_operand(uint32_t c, float sd)
@@ -66,7 +74,6 @@ __global__ __launch_bounds__(64 * W) void k_linear(const uint16_t* __restrict__ 
     constexpr int kQ = KS / 32;            // MFMAs per weight tile and step
     constexpr int kCv = KS / 128;          // 16-byte code loads per row and step
     __shared__ float sd_of[128];
-    f32x4 (*partial)[MT * NT][64] = reinterpret_cast<f32x4 (*)[MT * NT][64]>(lin_lds);
     const float gs = *gs_in;
     if (threadIdx.x < 128)
         sd_of[threadIdx.x] = e4m3_decode(threadIdx.x) / gs;
@@ -224,37 +231,46 @@ __global__ __launch_bounds__(64 * W) void k_linear(const uint16_t* __restrict__ 
     }
 
     // waves 1..W-1 hand their partial sums to wave 0, which adds them in order
-    // (through the LDS the scales used, once every wave is past the K loop)
-    if (SL)
+    // (through the LDS the scales used, once every wave is past the K loop); when
+    // they do not all fit at once, one 16-row tile of x per round
+    constexpr int kPer = lin_partial_tiles<MT, NT, W>();
+    static_assert((size_t)(W - 1) * kPer * NT * 64 * sizeof(f32x4) <= kLinLdsBudget, "one round fits in LDS");
+    f32x4 (*partial)[kPer * NT][64] = reinterpret_cast<f32x4 (*)[kPer * NT][64]>(lin_lds);
+#pragma unroll
+    for (int rd = 0; rd < MT / kPer; ++rd) {
+        if (SL || rd > 0)
+            __syncthreads();
+        if (wave > 0) {
+#pragma unroll
+            for (int i = 0; i < kPer; ++i)
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    partial[wave - 1][i * NT + t][lane] = acc[rd * kPer + i][t];
+        }
         __syncthreads();
-    if (wave > 0) {
+        if (wave != 0)
+            continue;
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+        for (int i = 0; i < kPer; ++i) {
+            const int ti = rd * kPer + i;
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                partial[wave - 1][i * NT + t][lane] = acc[i][t];
-    }
-    __syncthreads();
-    if (wave != 0)
-        return;
+            for (int t = 0; t < NT; ++t) {
+                f32x4 v = acc[ti][t];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
+                for (int w = 0; w < W - 1; ++w)
+                    v += partial[w][i * NT + t][lane];
+                const int64_t n = n0 + 16 * t + r;
+                if (n >= N)
+                    continue;
+                const float b = bias ? bf16_value(bias[n]) : 0.0f;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            f32x4 v = acc[i][t];
-#pragma unroll
-            for (int w = 0; w < W - 1; ++w)
-                v += partial[w][i * NT + t][lane];
-            const int64_t n = n0 + 16 * t + r;
-            if (n >= N)
-                continue;
-            const float b = bias ? bf16_value(bias[n]) : 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t m = m0 + 16 * i + 4 * g + e;
-                if (m < M) {
-                    const f32x2 o = {v[e] + b, 0.0f};
-                    y[m * N + n] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(o, bf16x2)) & 0xFFFFu);
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t m = m0 + 16 * ti + 4 * g + e;
+                    if (m < M) {
+                        const f32x2 o = {v[e] + b, 0.0f};
+                        y[m * N + n] =
+                            (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(o, bf16x2)) & 0xFFFFu);
+                    }
                 }
             }
         }

@@ -369,7 +369,7 @@ nvfp4_status enqueue_linear(const void* x, int64_t m, int64_t k, const uint8_t* 
                             hipStream_t s)
 {
     const dim3 grid((unsigned)((n + 16 * NT - 1) / (16 * NT)), (unsigned)((m + 16 * MT - 1) / (16 * MT)));
-    const size_t partial_bytes = (size_t)(W - 1) * MT * NT * 64 * sizeof(f32x4);
+    const size_t partial_bytes = (size_t)(W - 1) * lin_partial_tiles<MT, NT, W>() * NT * 64 * sizeof(f32x4);
     const size_t scale_bytes = (size_t)16 * NT * (k / 16);
     // the scale rows go to LDS when they fit in the 64 KB a workgroup may always use
     if (NVFP4_LIN_SCALES_LDS && scale_bytes <= kLinLdsBudget) {
@@ -388,8 +388,9 @@ nvfp4_status enqueue_linear(const void* x, int64_t m, int64_t k, const uint8_t* 
 // K step: 256 wide (fewer, wider loads) for one 16-row tile of x and at most
 // four weight tiles, else 128 wide (fewer registers).  The waves split K: 8 for
 // one 16-row tile of x (more loads in flight per CU; 33 vs 38 us for one row of
-// x on the c5 weight), else 4 (the partial sums of 8 waves of several x tiles do
-// not fit in LDS, and 16 waves spill registers).
+// x on the c5 weight), else 4 (8 waves of 2-4 x tiles spill registers, the
+// double-buffered x operands: 64 rows of x on the c5 weight took 211 us against
+// 59; 16 waves spill for one tile too).
 template <int MT, int NT>
 nvfp4_status enqueue_linear_w(const void* x, int64_t m, int64_t k, const uint8_t* packed,
                               const uint8_t* scales, const float* gs, int64_t n, const void* bias, void* y,
