@@ -320,6 +320,92 @@ def test_observer_ema_within_rounding_of_exact_recurrence():
     assert abs(s - exact) <= 10 * 3 * 2.0 ** -24 * exact
 
 
+# The EMA update of the verl QATLinear page, section 5 (_update_input_global_scale):
+# new = (1 - d) * old + d * cur on float32 buffers.  Evaluated as torch evaluates it on
+# float32 tensors, every operation rounds to float32 on its own: 1 - d, both products,
+# then the sum.  numpy float32 scalar arithmetic does exactly that (it never fuses).
+
+def ema_step_f32(state, cur, d):
+    """One update in numpy float32, each operation rounded separately (the -1 sentinel
+    start stores cur)."""
+    state, cur, d = np.float32(state), np.float32(cur), np.float32(d)
+    if state < 0:
+        return cur
+    keep = np.float32(np.float32(1.0) - d)
+    return np.float32(np.float32(keep * state) + np.float32(d * cur))
+
+
+def round_f32(q):
+    """An exact rational -> the nearest float32, ties to the even significand."""
+    from fractions import Fraction
+    f = np.float32(float(q))                          # within one float32 step of q
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    dist = [abs(Fraction(float(c)) - q) for c in cands]
+    best = min(dist)
+    near = [c for c, e in zip(cands, dist) if e == best]
+    return near[0] if len(near) == 1 else [c for c in near if not (int(c.view(np.uint32)) & 1)][0]
+
+
+def ema_lerp_f32(state, cur, d):
+    """A plausible mistake: the lerp form old + d * (cur - old), each step rounded."""
+    state, cur, d = np.float32(state), np.float32(cur), np.float32(d)
+    if state < 0:
+        return cur
+    return np.float32(state + np.float32(d * np.float32(cur - state)))
+
+
+def ema_fma_f32(state, cur, d):
+    """A plausible mistake: (1 - d) * old + (d * cur) as one fused multiply-add."""
+    from fractions import Fraction
+    state, cur, d = np.float32(state), np.float32(cur), np.float32(d)
+    if state < 0:
+        return cur
+    keep = np.float32(np.float32(1.0) - d)
+    return round_f32(Fraction(float(keep)) * Fraction(float(state)) + Fraction(float(np.float32(d * cur))))
+
+
+def ema_sequences():
+    """(decay, amax sequence) pairs: the c4 activations' ten step maxima, and seeded random
+    sequences over several decades, each starting from the -1 sentinel."""
+    c4 = np.float32([oracle.amax(synth.c4_activation(t)) for t in range(10)])
+    rng = np.random.default_rng(23)
+    seqs = [(0.01, c4)]
+    for d in (0.01, 0.25, 0.3, 0.5, 1.0):
+        for k in range(4):
+            seqs.append((d, np.exp(rng.uniform(-8, 12, 40)).astype(np.float32)))
+    return seqs
+
+
+def test_observer_ema_bit_exact_float32_recurrence():
+    """The oracle's EMA equals the float32 step-by-step recurrence bit for bit, and the
+    sequences are chosen so that the lerp and fused-multiply-add orders are told apart."""
+    lerp_differs = fma_differs = 0
+    for d, seq in ema_sequences():
+        df = float(np.float32(d))
+        s = -1.0
+        want = np.float32(-1.0)
+        for c in seq:
+            prev = want
+            s = oracle.observer(s, float(c), oracle.OBS_EMA, df)
+            want = ema_step_f32(prev, c, df)
+            assert np.float32(s).view(np.uint32) == want.view(np.uint32), (d, c)
+            lerp_differs += ema_lerp_f32(prev, c, df) != want
+            fma_differs += ema_fma_f32(prev, c, df) != want
+    assert lerp_differs > 10 and fma_differs > 10, (lerp_differs, fma_differs)
+
+
+def test_observer_ema_from_a_prior_state():
+    """A state carried over (not the sentinel) steps with the same float32 recurrence."""
+    rng = np.random.default_rng(29)
+    for d in (0.01, 0.3, 0.7):
+        s = np.float32(rng.uniform(1, 100))
+        for c in np.exp(rng.uniform(-3, 6, 25)).astype(np.float32):
+            got = np.float32(oracle.observer(float(s), float(c), oracle.OBS_EMA, float(np.float32(d))))
+            want = ema_step_f32(s, c, float(np.float32(d)))
+            assert got.view(np.uint32) == want.view(np.uint32)
+            s = want
+
+
 # ---------------------------------------------------------------- special cases
 
 def test_all_zero_tensor():
