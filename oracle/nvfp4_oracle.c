@@ -60,8 +60,6 @@
 
 /* E2M1 magnitudes; index = code & 7 ([VX] FLOAT4_MAGNITUDES, [KS]).                */
 static const float MAGNITUDE[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
-/* Mid-points between neighbouring magnitudes ([VX] FLOAT4_BOUNDARIES).             */
-static const float BOUNDARY[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
 
 static float f32_of_bits(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
 static uint32_t bits_of_f32(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
@@ -129,19 +127,22 @@ uint8_t nvo_e4m3_encode(float v)
 }
 
 /* ---- E2M1 rounding ([VX] _float4_round) --------------------------------------
- * bucketize(a, boundaries, right=True) counts the boundaries <= a, which rounds
- * a value sitting on a boundary upward; such a tie is then moved to the even
- * index.  Neighbouring indices differ in parity, so the lower side of boundary
- * i (index i) is even exactly when i is even.                                    */
+ * A non-negative value goes to the nearest of the eight magnitudes.  When it sits
+ * exactly half-way between two neighbours, the one with the even index wins (the
+ * even E2M1 mantissa bit).  Anything at or above the largest magnitude maps to it.
+ * The two neighbours are found by a walk up the sorted magnitudes; their
+ * mid-point has at most four significant bits, so it is exact in double.         */
 int nvo_e2m1_round(float a)
 {
-    int idx = 0;
-    for (int i = 0; i < 7; i++)
-        if (BOUNDARY[i] <= a)
-            idx++;
-    int lower = idx > 0 ? idx - 1 : 0;
-    int tie = (idx > 0) && (a == BOUNDARY[lower]);
-    return (tie && lower % 2 == 0) ? lower : idx;
+    if (!(a < MAGNITUDE[7]))
+        return 7;
+    int lo = 0;                          /* MAGNITUDE[lo] <= a < MAGNITUDE[lo + 1]  */
+    while (lo < 6 && MAGNITUDE[lo + 1] <= a)
+        lo++;
+    double mid = ((double)MAGNITUDE[lo] + (double)MAGNITUDE[lo + 1]) / 2.0;
+    if ((double)a < mid) return lo;
+    if ((double)a > mid) return lo + 1;
+    return (lo % 2 == 0) ? lo : lo + 1;
 }
 
 /* ---- step 1: per-tensor amax ([VX] quantize_weight_to_float4; [QAT] s.4) ----- */
