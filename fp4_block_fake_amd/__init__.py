@@ -95,19 +95,37 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _matrix(x: torch.Tensor, name: str):
-    if not x.is_cuda or x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+def _same_device(t: torch.Tensor, device, name: str) -> None:
+    if not t.is_cuda or (device is not None and t.device != device):
+        raise ValueError("%s must be a CUDA tensor on %s" % (name, device if device is not None else "the GPU"))
+
+
+def _matrix(x: torch.Tensor, name: str, device=None, shape=None):
+    """A contiguous 2-D bf16 tensor on `device` (and of `shape`, when given) -> its shape."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
         raise ValueError("%s must be a contiguous 2-D bfloat16 CUDA tensor" % name)
+    _same_device(x, device, name)
+    if shape is not None and tuple(x.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, not %s" % (name, tuple(shape), tuple(x.shape)))
     return x.shape
 
 
-def _scalar(device, t=None, fill=None):
+def _bytes(t: torch.Tensor, name: str, shape, device) -> None:
+    """A contiguous uint8 tensor of `shape` on `device`."""
+    if t.dtype != torch.uint8 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous uint8 tensor of shape %s" % (name, tuple(shape)))
+    _same_device(t, device, name)
+
+
+def _scalar(device, t=None, fill=None, name="scalar"):
     if t is None:
         t = torch.empty(1, dtype=torch.float32, device=device)
         if fill is not None:
             t.fill_(fill)
-    elif not t.is_cuda or t.dtype != torch.float32 or t.numel() != 1:
-        raise ValueError("scalars are 1-element float32 CUDA tensors")
+    elif t.dtype != torch.float32 or t.numel() != 1:
+        raise ValueError("%s must be a 1-element float32 CUDA tensor" % name)
+    else:
+        _same_device(t, device, name)
     return t
 
 
@@ -117,11 +135,12 @@ def nvfp4_amax(tensors, amax: torch.Tensor | None = None, accumulate: bool = Fal
         tensors = [tensors]
     if not tensors:
         raise ValueError("nvfp4_amax needs at least one tensor")
-    for t in tensors:
-        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise ValueError("amax inputs must be contiguous bfloat16 CUDA tensors")
     dev = tensors[0].device
-    amax = _scalar(dev, amax)
+    for i, t in enumerate(tensors):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("amax inputs must be contiguous bfloat16 CUDA tensors")
+        _same_device(t, dev, "tensors[%d]" % i)
+    amax = _scalar(dev, amax, name="amax")
     ptrs = (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
     ns = (ctypes.c_int64 * len(tensors))(*[t.numel() for t in tensors])
     _check(lib.nvfp4_amax(ptrs, ns, len(tensors), _ptr(amax), int(bool(accumulate)), _stream(dev)),
@@ -137,10 +156,12 @@ def nvfp4_fake_quant(x: torch.Tensor, y: torch.Tensor | None = None,
     rows, cols = _matrix(x, "x")
     if y is None:
         y = torch.empty_like(x)
-    _matrix(y, "y")
+    _matrix(y, "y", x.device, x.shape)
     if amax_in is not None:
-        _scalar(x.device, amax_in)
-    elif amax_out is None:
+        _scalar(x.device, amax_in, name="amax_in")
+    if amax_out is not None:
+        _scalar(x.device, amax_out, name="amax_out")
+    elif amax_in is None:
         amax_out = _scalar(x.device)
     _check(lib.nvfp4_fake_quant(_ptr(x), _ptr(y), rows, cols, _ptr(amax_in), _ptr(amax_out),
                                 _stream(x.device)), "nvfp4_fake_quant")
@@ -157,8 +178,8 @@ def _group_args(xs, ys, what):
     if len(ys) != len(xs):
         raise ValueError("ys must have one output per input")
     for i, (x, y) in enumerate(zip(xs, ys)):
-        if _matrix(y, "ys[%d]" % i) != x.shape or x.device != dev or y.device != dev:
-            raise ValueError("ys[%d] must match xs[%d] in shape and device" % (i, i))
+        _same_device(x, dev, "xs[%d]" % i)
+        _matrix(y, "ys[%d]" % i, dev, x.shape)
     n = len(xs)
     arrays = ((ctypes.c_void_p * n)(*[x.data_ptr() for x in xs]), (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys]),
               (ctypes.c_int64 * n)(*[r for r, _ in shapes]), (ctypes.c_int64 * n)(*[c for _, c in shapes]), n)
@@ -171,8 +192,10 @@ def nvfp4_fake_quant_group(xs, ys=None, amax_in: torch.Tensor | None = None,
     Without amax_in the amax over all of xs is computed first, into amax_out."""
     dev, ys, arrays = _group_args(xs, ys, "nvfp4_fake_quant_group")
     if amax_in is not None:
-        _scalar(dev, amax_in)
-    elif amax_out is None:
+        _scalar(dev, amax_in, name="amax_in")
+    if amax_out is not None:
+        _scalar(dev, amax_out, name="amax_out")
+    elif amax_in is None:
         amax_out = _scalar(dev)
     _check(lib.nvfp4_fake_quant_group(*arrays, _ptr(amax_in), _ptr(amax_out), _stream(dev)),
            "nvfp4_fake_quant_group")
@@ -185,7 +208,7 @@ def nvfp4_fake_quant_group_ws(xs, ys=None, amax_out: torch.Tensor | None = None,
     through a workspace."""
     dev, ys, arrays = _group_args(xs, ys, "nvfp4_fake_quant_group_ws")
     if amax_out is not None:
-        _scalar(dev, amax_out)
+        _scalar(dev, amax_out, name="amax_out")
     ws = _workspace(dev, workspace)
     _check(lib.nvfp4_fake_quant_group_ws(*arrays, _ptr(amax_out), _ptr(ws), _stream(dev)),
            "nvfp4_fake_quant_group_ws")
@@ -196,13 +219,12 @@ def nvfp4_fake_quant_dual(x: torch.Tensor, amax0: torch.Tensor, amax1: torch.Ten
                           y0: torch.Tensor | None = None, y1: torch.Tensor | None = None):
     """One read of x fake-quantized under two amaxes (two observers) -> (y0, y1)."""
     rows, cols = _matrix(x, "x")
-    _scalar(x.device, amax0)
-    _scalar(x.device, amax1)
+    _scalar(x.device, amax0, name="amax0")
+    _scalar(x.device, amax1, name="amax1")
     y0 = torch.empty_like(x) if y0 is None else y0
     y1 = torch.empty_like(x) if y1 is None else y1
     for name, y in (("y0", y0), ("y1", y1)):
-        if _matrix(y, name) != x.shape:
-            raise ValueError("%s must have the shape of x" % name)
+        _matrix(y, name, x.device, x.shape)
     _check(lib.nvfp4_fake_quant_dual(_ptr(x), rows, cols, _ptr(amax0), _ptr(y0), _ptr(amax1), _ptr(y1),
                                      _stream(x.device)), "nvfp4_fake_quant_dual")
     return y0, y1
@@ -226,12 +248,15 @@ def nvfp4_quantize_pack(x: torch.Tensor, amax_in: torch.Tensor | None = None,
         packed = torch.empty((rows, 8 * nbr), dtype=torch.uint8, device=dev)
     if scales is None:
         scales = torch.empty((rows, nbr), dtype=torch.uint8, device=dev)
-    global_scale = _scalar(dev, global_scale)
-    if amax_in is None and amax_out is None:
+    global_scale = _scalar(dev, global_scale, name="global_scale")
+    if amax_in is not None:
+        _scalar(dev, amax_in, name="amax_in")
+    if amax_out is not None:
+        _scalar(dev, amax_out, name="amax_out")
+    elif amax_in is None:
         amax_out = _scalar(dev)
-    for t, shape in ((packed, (rows, 8 * nbr)), (scales, (rows, nbr))):
-        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError("packed/scales must be contiguous uint8 CUDA tensors of shape %s" % (shape,))
+    _bytes(packed, "packed", (rows, 8 * nbr), dev)
+    _bytes(scales, "scales", (rows, nbr), dev)
     _check(lib.nvfp4_quantize_pack(_ptr(x), rows, cols, _ptr(amax_in), _ptr(amax_out), _ptr(packed),
                                    _ptr(scales), _ptr(global_scale), _stream(dev)),
            "nvfp4_quantize_pack")
@@ -250,12 +275,11 @@ def nvfp4_dequant_unpack(packed: torch.Tensor, scales: torch.Tensor, global_scal
         cols = 16 * nbr
     if blocks_per_row(cols) != nbr:
         raise ValueError("cols=%d does not match %d packed blocks per row" % (cols, nbr))
-    if tuple(scales.shape) != (rows, nbr) or scales.dtype != torch.uint8 or not scales.is_contiguous():
-        raise ValueError("scales must be contiguous uint8 [%d, %d]" % (rows, nbr))
-    _scalar(packed.device, global_scale)
+    _bytes(scales, "scales", (rows, nbr), packed.device)
+    _scalar(packed.device, global_scale, name="global_scale")
     if y is None:
         y = torch.empty((rows, cols), dtype=torch.bfloat16, device=packed.device)
-    _matrix(y, "y")
+    _matrix(y, "y", packed.device, (rows, cols))
     _check(lib.nvfp4_dequant_unpack(_ptr(packed), _ptr(scales), _ptr(global_scale), rows, cols,
                                     _ptr(y), _stream(packed.device)), "nvfp4_dequant_unpack")
     return y
@@ -267,21 +291,21 @@ def nvfp4_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
     """x bf16 [M, K] times the packed weight [N, K] (transposed), plus bias -> bf16 [M, N].
     packed / scales / global_scale as nvfp4_quantize_pack returns them; K % 32 == 0."""
     m, k = _matrix(x, "x")
-    if packed.dtype != torch.uint8 or packed.dim() != 2 or not packed.is_cuda or not packed.is_contiguous():
+    if packed.dtype != torch.uint8 or packed.dim() != 2 or not packed.is_contiguous():
         raise ValueError("packed must be a contiguous 2-D uint8 CUDA tensor")
+    _same_device(packed, x.device, "packed")
     n = packed.shape[0]
     if packed.shape[1] * 2 != k:
         raise ValueError("packed holds %d codes per row, x has %d columns" % (packed.shape[1] * 2, k))
-    if tuple(scales.shape) != (n, k // 16) or scales.dtype != torch.uint8 or not scales.is_contiguous():
-        raise ValueError("scales must be contiguous uint8 [%d, %d]" % (n, k // 16))
-    _scalar(x.device, global_scale)
-    if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (n,) or
-                             not bias.is_contiguous() or not bias.is_cuda):
-        raise ValueError("bias must be a contiguous bfloat16 CUDA tensor of %d elements" % n)
+    _bytes(scales, "scales", (n, k // 16), x.device)
+    _scalar(x.device, global_scale, name="global_scale")
+    if bias is not None:
+        if bias.dtype != torch.bfloat16 or tuple(bias.shape) != (n,) or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous bfloat16 CUDA tensor of %d elements" % n)
+        _same_device(bias, x.device, "bias")
     if y is None:
         y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
-    if _matrix(y, "y") != (m, n):
-        raise ValueError("y must be [%d, %d]" % (m, n))
+    _matrix(y, "y", x.device, (m, n))
     _check(lib.nvfp4_linear(_ptr(x), m, k, _ptr(packed), _ptr(scales), _ptr(global_scale), n, _ptr(bias),
                             _ptr(y), _stream(x.device)), "nvfp4_linear")
     return y
@@ -290,8 +314,8 @@ def nvfp4_linear(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
 def nvfp4_observer_update(state: torch.Tensor, cur: torch.Tensor, mode: int = OBS_STATIC_MINMAX,
                           decay: float = 0.01) -> torch.Tensor:
     """One observer step on device scalars, in place on ``state`` (initialise it to -1)."""
-    _scalar(state.device, state)
-    _scalar(state.device, cur)
+    _scalar(state.device, state, name="state")
+    _scalar(state.device, cur, name="cur")
     _check(lib.nvfp4_observer_update(_ptr(state), _ptr(cur), int(mode), float(decay),
                                      _stream(state.device)), "nvfp4_observer_update")
     return state
@@ -307,16 +331,16 @@ def nvfp4_observe_fake_quant(x: torch.Tensor, state0: torch.Tensor, mode0: int =
     workspace: as for the *_ws calls (a fresh one when not given)."""
     rows, cols = _matrix(x, "x")
     dev = x.device
-    _scalar(dev, state0)
+    _scalar(dev, state0, name="state0")
     if state1 is not None:
-        _scalar(dev, state1)
-    cur = _scalar(dev, cur)
+        _scalar(dev, state1, name="state1")
+    cur = _scalar(dev, cur, name="cur")
     y0 = torch.empty_like(x) if y0 is None else y0
     if state1 is not None and y1 is None:
         y1 = torch.empty_like(x)
     for name, y in (("y0", y0), ("y1", y1)):
-        if y is not None and _matrix(y, name) != x.shape:
-            raise ValueError("%s must have the shape of x" % name)
+        if y is not None:
+            _matrix(y, name, dev, x.shape)
     ws = _workspace(dev, workspace)
     _check(lib.nvfp4_observe_fake_quant(_ptr(x), rows, cols, _ptr(cur), _ptr(state0), int(mode0),
                                         float(decay0), _ptr(y0), _ptr(state1), int(mode1), float(decay1),
@@ -333,9 +357,10 @@ def new_workspace(device) -> torch.Tensor:
 def _workspace(device, ws):
     if ws is None:
         return new_workspace(device)
-    if not ws.is_cuda or ws.dtype != torch.uint8 or ws.numel() < WORKSPACE_BYTES or not ws.is_contiguous():
+    if ws.dtype != torch.uint8 or ws.numel() < WORKSPACE_BYTES or not ws.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 CUDA tensor of at least %d bytes"
                          % WORKSPACE_BYTES)
+    _same_device(ws, device, "workspace")
     return ws
 
 
@@ -346,10 +371,9 @@ def nvfp4_fake_quant_ws(x: torch.Tensor, y: torch.Tensor | None = None,
     rows, cols = _matrix(x, "x")
     if y is None:
         y = torch.empty_like(x)
-    if _matrix(y, "y") != x.shape:
-        raise ValueError("y must have the shape of x")
+    _matrix(y, "y", x.device, x.shape)
     if amax_out is not None:
-        _scalar(x.device, amax_out)
+        _scalar(x.device, amax_out, name="amax_out")
     ws = _workspace(x.device, workspace)
     _check(lib.nvfp4_fake_quant_ws(_ptr(x), _ptr(y), rows, cols, _ptr(amax_out), _ptr(ws),
                                    _stream(x.device)), "nvfp4_fake_quant_ws")
@@ -368,12 +392,11 @@ def nvfp4_quantize_pack_ws(x: torch.Tensor, amax_out: torch.Tensor | None = None
         packed = torch.empty((rows, 8 * nbr), dtype=torch.uint8, device=dev)
     if scales is None:
         scales = torch.empty((rows, nbr), dtype=torch.uint8, device=dev)
-    global_scale = _scalar(dev, global_scale)
+    global_scale = _scalar(dev, global_scale, name="global_scale")
     if amax_out is not None:
-        _scalar(dev, amax_out)
-    for t, shape in ((packed, (rows, 8 * nbr)), (scales, (rows, nbr))):
-        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError("packed/scales must be contiguous uint8 CUDA tensors of shape %s" % (shape,))
+        _scalar(dev, amax_out, name="amax_out")
+    _bytes(packed, "packed", (rows, 8 * nbr), dev)
+    _bytes(scales, "scales", (rows, nbr), dev)
     ws = _workspace(dev, workspace)
     _check(lib.nvfp4_quantize_pack_ws(_ptr(x), rows, cols, _ptr(amax_out), _ptr(packed), _ptr(scales),
                                       _ptr(global_scale), _ptr(ws), _stream(dev)), "nvfp4_quantize_pack_ws")

@@ -62,6 +62,8 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 #include "nvfp4.h"
 #include "kernels.hpp"
 #include "linear.hpp"
@@ -101,12 +103,28 @@ nvfp4_status check_matrix(int64_t rows, int64_t cols, Matrix* m)
 
 constexpr int kRaggedWgPerCu = 32;
 
+// Devices whose properties the library caches.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device, queried once per device.
+int compute_units()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return 256;
+    int cus = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        g_cu_count[dev].store(cus, std::memory_order_relaxed);
+    }
+    return cus;
+}
+
 unsigned persistent_grid(int64_t items, int64_t items_per_wg, int wg_per_cu)
 {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
+    const int cus = compute_units();
     const int64_t need = (items + items_per_wg - 1) / items_per_wg;
     const int64_t cap = (int64_t)cus * wg_per_cu;
     return (unsigned)(need < 1 ? 1 : (need < cap ? need : cap));
