@@ -1,6 +1,11 @@
 """Helpers shared by the GPU parity tests (imported only by modules that need a GPU)."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
+
+import oracle
 
 DEV = torch.device("cuda:0")
 
@@ -33,6 +38,46 @@ def assert_same(got, want, what):
         what, bad.size, bad[0], got.reshape(-1)[bad[0]], want.reshape(-1)[bad[0]])
 
 
-def sample_rows(rows, seed, k=62):
-    rng = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, k, replace=False)]))
+# ---------------------------------------------------------------- the oracle on many host threads
+#
+# Whole-tensor comparisons at the configurations' full sizes run the unchanged oracle
+# calls over row shards on the host's cores (at most 16, a GPU machine's share): blocks
+# never cross rows, so each shard's bytes are the rows of the whole tensor's result,
+# and the amax is the maximum of the shards' maxima, which is exact.  The oracle's C
+# calls release the GIL.
+
+ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _row_shards(x):
+    x = np.ascontiguousarray(x)
+    return [s for s in np.array_split(x, min(ORACLE_THREADS, max(1, x.shape[0]))) if s.shape[0]]
+
+
+def _map(fn, items):
+    with ThreadPoolExecutor(ORACLE_THREADS) as pool:
+        return list(pool.map(fn, items))
+
+
+def oracle_amax(x):
+    return max(_map(oracle.amax, _row_shards(x)))
+
+
+def oracle_fake_quant(x, amax_value=None):
+    if amax_value is None:
+        amax_value = oracle_amax(x)
+    return np.concatenate(_map(lambda s: oracle.fake_quant(s, amax_value), _row_shards(x)))
+
+
+def oracle_quantize(x, amax_value=None):
+    """-> (packed, scales, gs), as oracle.quantize."""
+    if amax_value is None:
+        amax_value = oracle_amax(x)
+    parts = _map(lambda s: oracle.quantize(s, amax_value), _row_shards(x))
+    return (np.concatenate([p for p, _, _ in parts]), np.concatenate([q for _, q, _ in parts]), parts[0][2])
+
+
+def oracle_dequantize(packed, scales, gs, cols):
+    rows = np.array_split(np.arange(packed.shape[0]), min(ORACLE_THREADS, max(1, packed.shape[0])))
+    return np.concatenate(_map(lambda r: oracle.dequantize(packed[r[0]:r[-1] + 1], scales[r[0]:r[-1] + 1], gs, cols),
+                               [r for r in rows if r.size]))
