@@ -19,7 +19,7 @@ __all__ = [
     "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
     "nvfp4_strerror", "FakeQuantSTE", "blocks_per_row", "nvfp4_observe_fake_quant",
     "WORKSPACE_BYTES", "new_workspace", "nvfp4_fake_quant_ws", "nvfp4_quantize_pack_ws",
-    "nvfp4_fake_quant_group_ws",
+    "nvfp4_fake_quant_group_ws", "nvfp4_fake_quant_noalloc",
 ]
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
@@ -31,7 +31,7 @@ WORKSPACE_BYTES = 2304        # NVFP4_WORKSPACE_BYTES
 _EXPORTS = ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
             "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
             "nvfp4_observe_fake_quant", "nvfp4_fake_quant_ws", "nvfp4_quantize_pack_ws",
-            "nvfp4_fake_quant_group_ws", "nvfp4_strerror")
+            "nvfp4_fake_quant_group_ws", "nvfp4_fake_quant_noalloc", "nvfp4_strerror")
 
 
 class NVFP4Error(RuntimeError):
@@ -59,6 +59,7 @@ def _load() -> ctypes.CDLL:
     so.nvfp4_fake_quant_ws.argtypes = [P, P, I64, I64, P, P, P]
     so.nvfp4_quantize_pack_ws.argtypes = [P, I64, I64, P, P, P, P, P, P]
     so.nvfp4_fake_quant_group_ws.argtypes = [P, P, P, P, I, P, P, P]
+    so.nvfp4_fake_quant_noalloc.argtypes = [P, P, I64, I64, P, P]
     so.nvfp4_strerror.argtypes = [I]
     so.nvfp4_strerror.restype = ctypes.c_char_p
     for name in _EXPORTS:
@@ -377,6 +378,22 @@ def nvfp4_fake_quant_ws(x: torch.Tensor, y: torch.Tensor | None = None,
     ws = _workspace(x.device, workspace)
     _check(lib.nvfp4_fake_quant_ws(_ptr(x), _ptr(y), rows, cols, _ptr(amax_out), _ptr(ws),
                                    _stream(x.device)), "nvfp4_fake_quant_ws")
+    return y
+
+
+def nvfp4_fake_quant_noalloc(x: torch.Tensor, y: torch.Tensor | None = None,
+                             amax_out: torch.Tensor | None = None) -> torch.Tensor:
+    """nvfp4_fake_quant_ws on the library's own per-GPU scratch instead of a workspace:
+    the call allocates nothing (pass y to allocate nothing here either).  Calls on one
+    GPU must not overlap in time."""
+    rows, cols = _matrix(x, "x")
+    if y is None:
+        y = torch.empty_like(x)
+    _matrix(y, "y", x.device, x.shape)
+    if amax_out is not None:
+        _scalar(x.device, amax_out, name="amax_out")
+    _check(lib.nvfp4_fake_quant_noalloc(_ptr(x), _ptr(y), rows, cols, _ptr(amax_out), _stream(x.device)),
+           "nvfp4_fake_quant_noalloc")
     return y
 
 

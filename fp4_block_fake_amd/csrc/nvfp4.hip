@@ -63,6 +63,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "nvfp4.h"
 #include "kernels.hpp"
@@ -103,7 +104,7 @@ nvfp4_status check_matrix(int64_t rows, int64_t cols, Matrix* m)
 
 constexpr int kRaggedWgPerCu = 32;
 
-// Devices whose properties the library caches.
+// Devices whose properties (CU count, scratch address) the library caches.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
 
@@ -563,6 +564,99 @@ bool observer_args_ok(int mode, float decay)
     return mode != NVFP4_OBS_EMA || (decay > 0.0f && decay <= 1.0f);
 }
 
+
+// Shapes, pointers and alignment of the fused fake-quant through a workspace
+// (the workspace itself is checked by the caller).
+nvfp4_status check_fake_quant_ws(const void* x, const void* y, int64_t rows, int64_t cols, const float* amax_out,
+                                 Matrix* m)
+{
+    const nvfp4_status st = check_matrix(rows, cols, m);
+    if (st != NVFP4_OK)
+        return st;
+    if (m->numel > 0 && (!x || !y))
+        return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(y, 16) || (amax_out && !aligned(amax_out, 4)))
+        return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+// The fused fake-quant through the workspace ws: the amax pass into partial
+// maxima, then the fake-quant pass, which reduces them itself (rows of whole
+// blocks), or the partials reduced by one workgroup first (ragged rows).  The
+// partials are written by the amax pass before anything reads them, and the
+// pass reads exactly as many as it wrote, so nothing in ws needs clearing.
+nvfp4_status enqueue_fake_quant_ws(const void* x, void* y, int64_t cols, const Matrix& m, float* amax_out,
+                                   void* ws, hipStream_t s)
+{
+    if (m.numel == 0)
+        return amax_out ? enqueue_reset(amax_out, s) : NVFP4_OK;
+    if (!m.ragged) {
+        AmaxIn src;
+        if (enqueue_amax_partials(&x, &m.numel, 1, ws, s, &src, ObserverArgs{}, 0,
+                                  amax_alloc_bytes(2 * m.numel, NVFP4_FQ_AMAX_ALLOC_MID)) != NVFP4_OK)
+            return NVFP4_ERR_HIP;
+        src.store = amax_out;
+        return enqueue_fake_quant(x, y, cols, m, src, s);
+    }
+    float* a = ws_amax(ws, amax_out);
+    if (enqueue_amax_ws(&x, &m.numel, 1, ws, a, s) != NVFP4_OK)
+        return NVFP4_ERR_HIP;
+    return enqueue_fake_quant(x, y, cols, m, a, s);
+}
+
+// ---------------------------------------------------------------- library-owned scratch
+//
+// nvfp4_fake_quant_noalloc runs the workspace form of the fused fake-quant on
+// the `scratch` array below instead of a caller's workspace, so it needs no
+// memory from its caller or from an allocator.  Each GPU the library runs on
+// holds its own copy of the array, at its own address, until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per GPU (with that GPU current) and only
+// that address is ever passed to a kernel.  Every call on one GPU shares the
+// array, so calls that overlap in time on one GPU race.
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[NVFP4_WORKSPACE_BYTES];
+
+namespace {
+
+static_assert(kPartialsOffset + 4 * (int64_t)kMaxPartials <= (int64_t)sizeof(scratch),
+              "the scratch holds the amax pass's partial maxima for any tensor size");
+
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_lock;
+
+// The device address of `scratch` on the GPU of `stream`, looked up on the
+// first call there.
+nvfp4_status scratch_address(hipStream_t stream, void** out)
+{
+    int dev = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess)
+        return NVFP4_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices)
+        return NVFP4_ERR_ARG;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_lock);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            int cur = -1;
+            if (hipGetDevice(&cur) != hipSuccess)
+                return NVFP4_ERR_HIP;
+            if (cur != dev && hipSetDevice(dev) != hipSuccess)
+                return NVFP4_ERR_HIP;
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (cur != dev)
+                (void)hipSetDevice(cur);
+            if (e != hipSuccess || !p)
+                return NVFP4_ERR_HIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return NVFP4_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- C ABI
@@ -862,12 +956,12 @@ nvfp4_status nvfp4_fake_quant_ws(const void* x, void* y, int64_t rows, int64_t c
                                  void* workspace, void* stream)
 {
     Matrix m;
-    const nvfp4_status st = check_matrix(rows, cols, &m);
+    nvfp4_status st = check_fake_quant_ws(x, y, rows, cols, amax_out, &m);
     if (st != NVFP4_OK)
         return st;
-    if ((m.numel > 0 && (!x || !y)) || !workspace)
+    if (!workspace)
         return NVFP4_ERR_NULL;
-    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256) || (amax_out && !aligned(amax_out, 4)))
+    if (!aligned(workspace, 256))
         return NVFP4_ERR_ALIGN;
     const uint64_t bytes = 2 * (uint64_t)m.numel;
     const Region in[1] = {{x, bytes}};
@@ -876,21 +970,27 @@ nvfp4_status nvfp4_fake_quant_ws(const void* x, void* y, int64_t rows, int64_t c
         return NVFP4_ERR_OVERLAP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (m.numel == 0)
-        return amax_out ? enqueue_reset(amax_out, s) : NVFP4_OK;
-    if (!m.ragged) {
-        // the pass reduces the partials itself and stores the amax
-        AmaxIn src;
-        if (enqueue_amax_partials(&x, &m.numel, 1, workspace, s, &src, ObserverArgs{}, 0,
-                                  amax_alloc_bytes(2 * m.numel, NVFP4_FQ_AMAX_ALLOC_MID)) != NVFP4_OK)
-            return NVFP4_ERR_HIP;
-        src.store = amax_out;
-        return enqueue_fake_quant(x, y, cols, m, src, s);
-    }
-    float* a = ws_amax(workspace, amax_out);
-    if (enqueue_amax_ws(&x, &m.numel, 1, workspace, a, s) != NVFP4_OK)
-        return NVFP4_ERR_HIP;
-    return enqueue_fake_quant(x, y, cols, m, a, s);
+    return enqueue_fake_quant_ws(x, y, cols, m, amax_out, workspace, s);
+}
+
+nvfp4_status nvfp4_fake_quant_noalloc(const void* x, void* y, int64_t rows, int64_t cols, float* amax_out,
+                                      void* stream)
+{
+    Matrix m;
+    nvfp4_status st = check_fake_quant_ws(x, y, rows, cols, amax_out, &m);
+    if (st != NVFP4_OK)
+        return st;
+    const uint64_t bytes = 2 * (uint64_t)m.numel;
+    const Region in[1] = {{x, bytes}};
+    const Region out[2] = {{y, bytes}, {amax_out, amax_out ? 4u : 0u}};
+    if (check_regions(in, 1, out, 2, true) != NVFP4_OK)
+        return NVFP4_ERR_OVERLAP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    void* ws = nullptr;
+    if ((st = scratch_address(s, &ws)) != NVFP4_OK)
+        return st;
+    return enqueue_fake_quant_ws(x, y, cols, m, amax_out, ws, s);
 }
 
 nvfp4_status nvfp4_quantize_pack_ws(const void* x, int64_t rows, int64_t cols, float* amax_out,

@@ -308,6 +308,30 @@ nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols,
                                       float* state1, int mode1, float decay1, void* y1,
                                       void* workspace, void* stream);
 
+/*
+ * nvfp4_fake_quant_noalloc -- nvfp4_fake_quant_ws without a workspace argument,
+ * for callers that cannot allocate device memory at all (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same y and
+ * amax_out as nvfp4_fake_quant_ws, bit for bit; x, y and amax_out as there.
+ *
+ * The workspace is a library-owned device array of NVFP4_WORKSPACE_BYTES bytes:
+ * one per GPU, created with the library's code on that GPU and held until the
+ * process ends.  Its device address is looked up on the first call on each GPU
+ * (the GPU of `stream`); the call itself never allocates or frees memory.  The
+ * array's contents carry over from call to call and nothing in it needs to
+ * start at zero.  Its size does not grow with the tensor (the amax pass leaves
+ * at most 512 partial maxima there), so every shape nvfp4_fake_quant_ws accepts
+ * is accepted here; no other size limit applies.
+ * Every call on one GPU shares that GPU's array: calls on one GPU whose work
+ * overlaps in time (two streams, or host threads with their own streams) race
+ * and give undefined results.  Order them on one stream, or use the _ws call
+ * with a workspace each.
+ * Errors: SHAPE, NULL, ALIGN, OVERLAP, ARG (more than 64 GPUs), HIP (including
+ * a failed address lookup).
+ */
+nvfp4_status nvfp4_fake_quant_noalloc(const void* x, void* y, int64_t rows, int64_t cols, float* amax_out,
+                                      void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* nvfp4_strerror(int status);
 

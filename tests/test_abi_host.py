@@ -34,7 +34,7 @@ def test_header_declares_every_call():
     for n in ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
               "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
               "nvfp4_observe_fake_quant", "nvfp4_fake_quant_ws", "nvfp4_quantize_pack_ws",
-              "nvfp4_fake_quant_group_ws", "nvfp4_strerror"):
+              "nvfp4_fake_quant_group_ws", "nvfp4_fake_quant_noalloc", "nvfp4_strerror"):
         assert n in names
 
 
@@ -68,6 +68,7 @@ int main(void)
     bad |= nvfp4_fake_quant_ws(0, 0, 4, 16, 0, 0, 0) != NVFP4_ERR_NULL;
     bad |= nvfp4_quantize_pack_ws(0, 4, 0, 0, 0, 0, 0, 0, 0) != NVFP4_ERR_SHAPE;
     bad |= nvfp4_fake_quant_group_ws(0, 0, 0, 0, 1, 0, 0, 0) != NVFP4_ERR_NULL;
+    bad |= nvfp4_fake_quant_noalloc(0, 0, 4, 16, 0, 0) != NVFP4_ERR_NULL;
     bad |= NVFP4_WORKSPACE_BYTES < 2304;
     bad |= strcmp(nvfp4_strerror(NVFP4_OK), "ok") != 0;
     printf("%s\n", bad ? "FAIL" : "OK");
@@ -329,6 +330,28 @@ def test_fake_quant_ws_validation():
     assert call(amax=w + 4) == ERR_OVERLAP                      # amax inside the workspace
     assert call(ws=x) == ERR_OVERLAP
     assert call(ws=y - 256) == ERR_OVERLAP                      # the workspace runs into y
+
+
+def test_fake_quant_noalloc_validation():
+    """Every check runs before the scratch lookup, so none of these touches HIP."""
+    f = nv.lib.nvfp4_fake_quant_noalloc
+    G = 1 << 30
+    x, y, a = A, A + G, A + 2 * G
+
+    def call(x=x, y=y, rows=4, cols=16, amax=a):
+        return f(P(x), P(y), rows, cols, P(amax), None)
+
+    assert call(cols=0) == ERR_SHAPE
+    assert call(rows=-1) == ERR_SHAPE
+    assert call(rows=1 << 62, cols=1 << 20) == ERR_SHAPE
+    assert call(x=None) == ERR_NULL
+    assert call(y=None) == ERR_NULL
+    assert call(x=x + 8) == ERR_ALIGN
+    assert call(y=y + 2) == ERR_ALIGN
+    assert call(amax=a + 2) == ERR_ALIGN
+    assert call(y=x + 16) == ERR_OVERLAP
+    assert call(amax=x + 64) == ERR_OVERLAP
+    assert call(amax=y + 4) == ERR_OVERLAP
 
 
 def test_quantize_pack_ws_validation():
