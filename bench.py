@@ -58,12 +58,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+PROBE_SOURCE = "stream_probe.hip"     # the benchmark's own stream probes, not a library kernel
+
+
 def kernel_source_hash():
-    """SHA-256 (first 16 hex digits) over the kernel sources, file names included."""
+    """SHA-256 (first 16 hex digits) over the library's kernel sources, file names included."""
     csrc = os.path.join(ROOT, "fp4_block_fake_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
+        if name.endswith((".hip", ".hpp")) and name != PROBE_SOURCE:
             h.update(name.encode())
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(f.read())
@@ -71,7 +74,10 @@ def kernel_source_hash():
 
 
 def read_traffic(kernel, workload):
-    """HBM bytes per launch measured by rocprofv3 counters, if taken on the current source."""
+    """Bytes per launch that crossed the L2's memory-side interface (rocprofv3 FETCH_SIZE +
+    WRITE_SIZE, scaled by a copy of known size), if taken on the current source.  These
+    requests go on to the Infinity Cache, so its hits count too: an upper bound on HBM
+    bytes, not a DRAM-only figure (no per-kernel counter on gfx950 separates the two)."""
     path = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (kernel, workload))
     if not os.path.exists(path):
         return None
@@ -84,7 +90,7 @@ def read_traffic(kernel, workload):
     if kv.get("source_sha256_16") != kernel_source_hash():
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["bytes_past_l2_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -110,6 +116,7 @@ def cpu_baseline(x, rows):
         "sample": "first %d of %d rows (%d elements), one step: amax+fake-quant, "
                   "amax+quantize-pack, dequant-unpack; %.1f s single-threaded" % (rows, x.shape[0], n, dt),
         "elements_per_s": round(n / dt, 1),
+        "host": host_info(),
     }
 
 
@@ -142,7 +149,29 @@ def cpu_baseline_threads(x, rows, threads):
         "sample": "first %d of %d rows (%d elements) in %d row shards, one step; %.2f s" % (
             rows, x.shape[0], n, len(shards), dt),
         "elements_per_s": round(n / dt, 1),
+        "host": host_info(),
     }
+
+
+def cold_times(torch, stream, flush, fn, reps):
+    """GPU times of single calls of fn, each started with no data of its own in the caches:
+    a 1 GiB read (outside the events) evicts the Infinity Cache and the L2s first.  The
+    events and the calls are enqueued behind the flush without waiting for it, so the
+    host's submission of fn overlaps the flush and is not counted as GPU time."""
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        flush.sum()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    return sorted(ts)
+
+
+def median(ts):
+    return ts[len(ts) // 2]
 
 
 def secondary(nv, synth, np, torch, dev, reps=20, only=None):
@@ -153,7 +182,7 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
     stream = torch.cuda.current_stream(dev)
     out = {}
 
-    def timed(fn, nbytes):
+    def timed(fn, nbytes, elems=None):
         # warm up for at least 10 ms of calls, so each line is timed after the clock
         # transient that a change of load starts
         t_end = time.perf_counter() + 0.010
@@ -171,33 +200,28 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / reps * 1e3
-        return {"us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
-                "pct_of_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+        r = {"us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+             "pct_of_hbm_peak": round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+        if elems:
+            r["elements_per_s"] = round(elems / (us * 1e-6), 1)
+        return r
 
     flush = torch.ones((1 << 30) // 4, dtype=torch.int32, device=dev)
 
     def cold_us(fn, reps=9):
-        """Median time of single calls, each after a 1 GiB read has evicted the
-        Infinity Cache and the L2s (outside the events)."""
-        ts = []
-        for _ in range(reps):
-            flush.sum()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
-        return round(sorted(ts)[len(ts) // 2], 2)
+        """Median GPU time of single calls, each after a 1 GiB read has evicted the
+        Infinity Cache and the L2s."""
+        return round(median(cold_times(torch, stream, flush, fn, reps)), 2)
 
-    def line(name, fn, nbytes, cold=False):
+    def line(name, fn, nbytes, cold=False, elems=None):
         if only is None or only in name:
-            out[name] = timed(fn, nbytes)
+            out[name] = timed(fn, nbytes, elems)
             if cold:
                 c = cold_us(fn)
                 out[name]["cold_us"] = c
                 out[name]["cold_pct_of_hbm_peak"] = round(100 * nbytes / (c * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)
+                if elems:
+                    out[name]["cold_elements_per_s"] = round(elems / (c * 1e-6), 1)
 
     def group(prefix):
         return only is None or only.startswith(prefix) or prefix.startswith(only)
@@ -206,6 +230,44 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
     ws = nv.new_workspace(dev)
+
+    if group("c1_"):
+        # c1: one small weight, fused amax + fake-quant (launch-bound: no bandwidth target)
+        x = to_dev(synth.c1_weight())
+        n1 = x.numel()
+        y = torch.empty_like(x)
+        a = torch.empty(1, dtype=torch.float32, device=dev)
+        line("c1_fused_amax_fake_quant_256x1024", lambda: nv.nvfp4_fake_quant(x, y=y, amax_out=a), 6.0 * n1,
+             cold=True, elems=n1)
+        line("c1_fused_amax_fake_quant_ws", lambda: nv.nvfp4_fake_quant_ws(x, y=y, amax_out=a, workspace=ws),
+             6.0 * n1, cold=True, elems=n1)
+        line("c1_fused_amax_fake_quant_noalloc", lambda: nv.nvfp4_fake_quant_noalloc(x, y=y, amax_out=a),
+             6.0 * n1, cold=True, elems=n1)
+        del x, y
+
+    if group("c2_"):
+        # c2: 4096 x 4096 with outliers and exact ties; a power-of-two global scale, so
+        # 14 of the 126 scale bytes take the integer-threshold code path
+        x = to_dev(synth.c2_weight())
+        n2 = x.numel()
+        y = torch.empty_like(x)
+        a = torch.empty(1, dtype=torch.float32, device=dev)
+        p2 = torch.empty((x.shape[0], x.shape[1] // 2), dtype=torch.uint8, device=dev)
+        s2 = torch.empty((x.shape[0], x.shape[1] // 16), dtype=torch.uint8, device=dev)
+        g2 = torch.empty(1, dtype=torch.float32, device=dev)
+        line("c2_fused_amax_fake_quant_4096x4096", lambda: nv.nvfp4_fake_quant(x, y=y, amax_out=a), 6.0 * n2,
+             cold=True, elems=n2)
+        line("c2_fused_amax_fake_quant_ws", lambda: nv.nvfp4_fake_quant_ws(x, y=y, amax_out=a, workspace=ws),
+             6.0 * n2, cold=True, elems=n2)
+        line("c2_fused_amax_quantize_pack",
+             lambda: nv.nvfp4_quantize_pack(x, amax_out=a, packed=p2, scales=s2, global_scale=g2), 4.5625 * n2,
+             cold=True, elems=n2)
+        line("c2_fused_amax_quantize_pack_ws",
+             lambda: nv.nvfp4_quantize_pack_ws(x, amax_out=a, packed=p2, scales=s2, global_scale=g2,
+                                               workspace=ws), 4.5625 * n2, cold=True, elems=n2)
+        line("c2_dequant_unpack", lambda: nv.nvfp4_dequant_unpack(p2, s2, g2, y=y), 2.5625 * n2, cold=True,
+             elems=n2)
+        del x, y, p2, s2
 
     if group("c3_"):
         # c3: shared amax of fused QKV siblings in one launch, then a fake-quant of each
@@ -218,11 +280,12 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
             nv.nvfp4_amax(sibs, amax=shared)
             for t, y in zip(sibs, ys):
                 nv.nvfp4_fake_quant(t, y=y, amax_in=shared)
-        line("c3_qkv_shared_amax_fake_quant", c3, 6.0 * n3)
+        line("c3_qkv_shared_amax_fake_quant", c3, 6.0 * n3, cold=True, elems=n3)
         line("c3_qkv_group_fake_quant_one_launch",
-             lambda: nv.nvfp4_fake_quant_group(sibs, ys=ys, amax_out=shared), 6.0 * n3)
+             lambda: nv.nvfp4_fake_quant_group(sibs, ys=ys, amax_out=shared), 6.0 * n3, cold=True, elems=n3)
         line("c3_qkv_group_fake_quant_ws",
-             lambda: nv.nvfp4_fake_quant_group_ws(sibs, ys=ys, amax_out=shared, workspace=ws), 6.0 * n3)
+             lambda: nv.nvfp4_fake_quant_group_ws(sibs, ys=ys, amax_out=shared, workspace=ws), 6.0 * n3,
+             cold=True, elems=n3)
         del sibs, ys
 
     if group("c4_activation"):
@@ -240,7 +303,7 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
             nv.nvfp4_observer_update(st_e, cur, nv.OBS_EMA, 0.01)
             nv.nvfp4_fake_quant(x, y=y1, amax_in=st_s)
             nv.nvfp4_fake_quant(x, y=y2, amax_in=st_e)
-        line("c4_activation_step_8192x4096", c4act, 10.0 * n4)
+        line("c4_activation_step_8192x4096", c4act, 10.0 * n4, cold=True, elems=n4)
 
         def c4act_dual():
             nv.nvfp4_amax(x, amax=cur)
@@ -248,27 +311,29 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
             nv.nvfp4_observer_update(st_e, cur, nv.OBS_EMA, 0.01)
             nv.nvfp4_fake_quant_dual(x, st_s, st_e, y0=y1, y1=y2)
         # same outputs from one read of x: 8 bytes per element of traffic instead of 10
-        line("c4_activation_step_dual_fake_quant", c4act_dual, 8.0 * n4)
+        line("c4_activation_step_dual_fake_quant", c4act_dual, 8.0 * n4, cold=True, elems=n4)
         # the same step as one call: 3 launches (amax to partial maxima, their reduction
         # with both observer steps, dual fake-quant) instead of 5
         line("c4_activation_step_observe_fake_quant",
              lambda: nv.nvfp4_observe_fake_quant(x, st_s, nv.OBS_STATIC_MINMAX, 0.0, st_e, nv.OBS_EMA, 0.01,
-                                                 y0=y1, y1=y2, cur=cur, workspace=ws), 8.0 * n4)
-        line("c4_activation_cached_fake_quant", lambda: nv.nvfp4_fake_quant(x, y=y1, amax_in=st_s), 4.0 * n4)
+                                                 y0=y1, y1=y2, cur=cur, workspace=ws), 8.0 * n4,
+             cold=True, elems=n4)
+        line("c4_activation_cached_fake_quant", lambda: nv.nvfp4_fake_quant(x, y=y1, amax_in=st_s), 4.0 * n4,
+             cold=True, elems=n4)
         line("c4_activation_fused_amax_fake_quant", lambda: nv.nvfp4_fake_quant(x, y=y1, amax_out=cur), 6.0 * n4,
-             cold=True)
+             cold=True, elems=n4)
         pa = torch.empty((x.shape[0], x.shape[1] // 2), dtype=torch.uint8, device=dev)
         sa = torch.empty((x.shape[0], x.shape[1] // 16), dtype=torch.uint8, device=dev)
         ga = torch.empty(1, dtype=torch.float32, device=dev)
         line("c4_activation_fused_amax_quantize_pack",
              lambda: nv.nvfp4_quantize_pack(x, amax_out=cur, packed=pa, scales=sa, global_scale=ga), 4.5625 * n4,
-             cold=True)
+             cold=True, elems=n4)
         # the fused calls through a workspace: no clearing launch, no atomics
         line("c4_activation_fused_amax_fake_quant_ws",
-             lambda: nv.nvfp4_fake_quant_ws(x, y=y1, amax_out=cur, workspace=ws), 6.0 * n4, cold=True)
+             lambda: nv.nvfp4_fake_quant_ws(x, y=y1, amax_out=cur, workspace=ws), 6.0 * n4, cold=True, elems=n4)
         line("c4_activation_fused_amax_quantize_pack_ws",
              lambda: nv.nvfp4_quantize_pack_ws(x, amax_out=cur, packed=pa, scales=sa, global_scale=ga,
-                                               workspace=ws), 4.5625 * n4, cold=True)
+                                               workspace=ws), 4.5625 * n4, cold=True, elems=n4)
         del pa, sa, x, y1, y2
 
     if group("c4_weight"):
@@ -280,15 +345,15 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
         sc = torch.empty((w.shape[0], w.shape[1] // 16), dtype=torch.uint8, device=dev)
         gsw = torch.empty(1, dtype=torch.float32, device=dev)
         line("c4_weight_fused_amax_fake_quant_14336x4096",
-             lambda: nv.nvfp4_fake_quant(w, y=yw, amax_out=aw), 6.0 * nw, cold=True)
+             lambda: nv.nvfp4_fake_quant(w, y=yw, amax_out=aw), 6.0 * nw, cold=True, elems=nw)
         line("c4_weight_fused_amax_quantize_pack_14336x4096",
              lambda: nv.nvfp4_quantize_pack(w, amax_out=aw, packed=pk, scales=sc, global_scale=gsw), 4.5625 * nw,
-             cold=True)
+             cold=True, elems=nw)
         line("c4_weight_fused_amax_fake_quant_ws",
-             lambda: nv.nvfp4_fake_quant_ws(w, y=yw, amax_out=aw, workspace=ws), 6.0 * nw, cold=True)
+             lambda: nv.nvfp4_fake_quant_ws(w, y=yw, amax_out=aw, workspace=ws), 6.0 * nw, cold=True, elems=nw)
         line("c4_weight_fused_amax_quantize_pack_ws",
              lambda: nv.nvfp4_quantize_pack_ws(w, amax_out=aw, packed=pk, scales=sc, global_scale=gsw,
-                                               workspace=ws), 4.5625 * nw, cold=True)
+                                               workspace=ws), 4.5625 * nw, cold=True, elems=nw)
         del w, yw, pk, sc
 
     if group("c5_"):
@@ -302,13 +367,14 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
         psh = torch.empty((sh.shape[0], k // 2), dtype=torch.uint8, device=dev)
         ssh = torch.empty((sh.shape[0], k // 16), dtype=torch.uint8, device=dev)
         gsh = torch.empty(1, dtype=torch.float32, device=dev)
+        ns = sh.numel()
         line("c5_row_shard_3584x8192_cached_fake_quant",
-             lambda: nv.nvfp4_fake_quant(sh, y=ysh, amax_in=amax_all), 4.0 * sh.numel())
+             lambda: nv.nvfp4_fake_quant(sh, y=ysh, amax_in=amax_all), 4.0 * ns, cold=True, elems=ns)
         line("c5_row_shard_3584x8192_cached_quantize_pack",
              lambda: nv.nvfp4_quantize_pack(sh, amax_in=amax_all, packed=psh, scales=ssh, global_scale=gsh),
-             2.5625 * sh.numel())
+             2.5625 * ns, cold=True, elems=ns)
         line("c5_row_shard_3584x8192_dequant_unpack",
-             lambda: nv.nvfp4_dequant_unpack(psh, ssh, gsh, y=ysh), 2.5625 * sh.numel())
+             lambda: nv.nvfp4_dequant_unpack(psh, ssh, gsh, y=ysh), 2.5625 * ns, cold=True, elems=ns)
         del sh, ysh, psh, ssh
         # the fused calls on the c5 weight through the workspace (the step uses the
         # three-launch form, whose quantizing kernel the roofline times alone)
@@ -317,10 +383,11 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
         scc = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
         ac, gc = torch.empty(1, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.float32, device=dev)
         line("c5_weight_fused_amax_fake_quant_ws",
-             lambda: nv.nvfp4_fake_quant_ws(wc, y=yc, amax_out=ac, workspace=ws), 6.0 * wc.numel())
+             lambda: nv.nvfp4_fake_quant_ws(wc, y=yc, amax_out=ac, workspace=ws), 6.0 * wc.numel(), cold=True,
+             elems=wc.numel())
         line("c5_weight_fused_amax_quantize_pack_ws",
              lambda: nv.nvfp4_quantize_pack_ws(wc, amax_out=ac, packed=pc, scales=scc, global_scale=gc,
-                                               workspace=ws), 4.5625 * wc.numel())
+                                               workspace=ws), 4.5625 * wc.numel(), cold=True, elems=wc.numel())
         del yc, pc, scc
         # the c5 weight used as a linear layer (packed once), against unpack + torch's bf16
         # GEMM and torch's bf16 GEMM on an already unpacked weight (context only).  Calls
@@ -363,6 +430,168 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
     return out
 
 
+def stream_ceilings(torch, stream, flush, x, y, n):
+    """Read-only, write-only and copy streams over the c5 tensor (2n bytes each way) by
+    the probe kernels of libnvfp4_probe.so: the best of a few launch shapes, warm (a loop)
+    and cold (median of single runs after the flush)."""
+    import ctypes
+    path = os.path.join(ROOT, "fp4_block_fake_amd", "libnvfp4_probe.so")
+    lib = ctypes.CDLL(path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.nvfp4_probe_read.argtypes = [P, I64, P, I, P]
+    lib.nvfp4_probe_write.argtypes = [P, I64, I, P]
+    lib.nvfp4_probe_copy.argtypes = [P, P, I64, I, P]
+    sink = torch.zeros(256, dtype=torch.int32, device=x.device)
+    sp = P(stream.cuda_stream)
+    nbytes = 2 * n
+    kinds = {
+        "read": (lambda w: lib.nvfp4_probe_read(P(x.data_ptr()), nbytes, P(sink.data_ptr()), w, sp), nbytes),
+        "write": (lambda w: lib.nvfp4_probe_write(P(y.data_ptr()), nbytes, w, sp), nbytes),
+        "copy": (lambda w: lib.nvfp4_probe_copy(P(x.data_ptr()), P(y.data_ptr()), nbytes, w, sp), 2 * nbytes),
+    }
+    out = {}
+    for kind, (call, moved) in kinds.items():
+        best = None
+        for w in (2, 8, 32, 64):
+            for _ in range(20):
+                assert call(w) == 0
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                call(w)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            warm = e0.elapsed_time(e1) / 20 * 1e3
+            cold = median(cold_times(torch, stream, flush, lambda: call(w), 5))
+            if best is None or cold < best[2]:
+                best = (w, warm, cold)
+        w, warm, cold = best
+        out[kind] = {"wg_per_cu": w, "warm_us": round(warm, 2), "cold_us": round(cold, 2),
+                     "warm_gbs": round(moved / (warm * 1e-6) / 1e9, 1),
+                     "cold_gbs": round(moved / (cold * 1e-6) / 1e9, 1)}
+    return out
+
+
+def host_info():
+    """The host's CPUs as the CPU-baseline figures ran on them."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0)), "cpu_model": model,
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
+class OracleRunner:
+    """The oracle's calls on `threads` host threads over row shards (1: the plain calls).
+    Rows are independent and the amax of shards reduces exactly, so the bytes do not depend
+    on the thread count; the oracle's C calls release the GIL."""
+
+    def __init__(self, threads):
+        from concurrent.futures import ThreadPoolExecutor
+
+        import numpy as np
+
+        import oracle
+        self.o, self.np, self.threads = oracle, np, threads
+        self.pool = ThreadPoolExecutor(threads) if threads > 1 else None
+
+    def _map(self, fn, items):
+        return list(self.pool.map(fn, items)) if self.pool else [fn(i) for i in items]
+
+    def _shards(self, x):
+        if not self.pool:
+            return [x]
+        return [s for s in self.np.array_split(x, self.threads) if s.shape[0]]
+
+    def amax(self, *xs):
+        if not self.pool:
+            return self.o.amax_group(list(xs)) if len(xs) > 1 else self.o.amax(xs[0])
+        return max(max(self._map(self.o.amax, self._shards(x))) for x in xs)
+
+    def fake_quant(self, x, a):
+        self._map(lambda s: self.o.fake_quant(s, a), self._shards(x))
+
+    def quantize(self, x, a):
+        return self._map(lambda s: self.o.quantize(s, a), self._shards(x))
+
+    def dequantize(self, parts, cols):
+        self._map(lambda p: self.o.dequantize(p[0], p[1], p[2], cols), parts)
+
+
+def cpu_table(synth):
+    """The oracle timed per configuration on the host: each configuration's op sequence
+    (BASELINE's CPU plan), on 1 thread and on all usable host threads (at most 16),
+    median of 3 runs for c4 and c5 and of 10 for the others; generation is not timed."""
+    import numpy as np
+
+    import oracle
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    acts = [synth.c4_activation(t) for t in range(10)]
+    w4 = synth.c4_weight()
+
+    def c1(r, x=synth.c1_weight()):
+        r.fake_quant(x, r.amax(x))
+
+    def c2(r, x=synth.c2_weight()):
+        r.fake_quant(x, r.amax(x))
+        r.dequantize(r.quantize(x, r.amax(x)), x.shape[1])
+
+    def c3(r, sibs=synth.c3_siblings()):
+        a = r.amax(*sibs)
+        for t in sibs:
+            r.fake_quant(t, a)
+
+    def c4(r):
+        st = em = -1.0
+        for x in acts:
+            a = r.amax(x)
+            st = oracle.observer(st, a, oracle.OBS_STATIC_MINMAX)
+            em = oracle.observer(em, a, oracle.OBS_EMA, float(np.float32(0.01)))
+            r.fake_quant(x, st)
+            r.fake_quant(x, em)
+        r.fake_quant(w4, r.amax(w4))
+
+    x5 = synth.c5_weight()
+
+    def c5(r):
+        r.dequantize(r.quantize(x5, r.amax(x5)), x5.shape[1])
+        r.fake_quant(x5, r.amax(x5))
+
+    n1, n2, n3 = 256 * 1024, 4096 * 4096, sum(t.size for t in synth.c3_siblings())
+    n4a, n4w, n5 = acts[0].size, w4.size, x5.size
+    configs = {   # name: (run, elements, algorithmic bytes, repetitions)
+        "c1": (c1, n1, 6.0 * n1, 10),
+        "c2": (c2, n2, STEP_BYTES_PER_ELEM * n2, 10),
+        "c3": (c3, n3, 6.0 * n3, 10),
+        "c4": (c4, 10 * n4a + n4w, 10 * 10.0 * n4a + 6.0 * n4w, 3),
+        "c5": (c5, n5, STEP_BYTES_PER_ELEM * n5, 3),
+    }
+    out = {"host": host_info(), "threads": threads}
+    for name, (run, elems, nbytes, reps) in configs.items():
+        row = {"elements": elems, "bytes": nbytes, "reps": reps}
+        for t in (1, threads):
+            r = OracleRunner(t)
+            ts = []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                run(r)
+                ts.append(time.perf_counter() - t0)
+            ts.sort()
+            med = ts[len(ts) // 2]
+            row["threads_%d" % t] = {"median_s": round(med, 4), "gbs": round(nbytes / med / 1e9, 4),
+                                     "elements_per_s": round(elems / med, 1)}
+            log("cpu table %s, %d thread(s): median %.3f s" % (name, t, med))
+        out[name] = row
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -376,6 +605,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=28672,
                     help="rows of the oracle's CPU sample (default: the whole c5 weight, ~13 s; 0: skip)")
     ap.add_argument("--no-secondary", action="store_true", help="skip the c3/c4 per-call lines")
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="time the CPU oracle per configuration (1 thread and all host threads; no GPU) "
+                         "and print that JSON instead of the bench line")
     ap.add_argument("--secondary-only", metavar="NAME", default=None,
                     help="diagnostic mode: skip the step and run only the secondary lines whose name "
                          "contains NAME (prints their JSON, not the bench line); for profiling")
@@ -385,6 +617,11 @@ def main():
         print("bench.py measures one GPU only; this build has no multi-GPU path. Sharded "
               "tensors would need one 4-byte max all-reduce of the amax per tensor.", file=sys.stderr)
         sys.exit(2)
+
+    if args.cpu_table:
+        import synth
+        print(json.dumps({"cpu_table": cpu_table(synth)}), flush=True)
+        return
 
     import numpy as np
     import torch
@@ -482,34 +719,19 @@ def main():
     achieved = dom_bytes / (fq_ms * 1e-3) / 1e9
     traffic = read_traffic(KERNEL_NAMES[dom], "c5")
 
-    # a plain copy of the same tensor, as the practical HBM ceiling on this machine
-    for _ in range(3):
-        y.copy_(x)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(10):
-        y.copy_(x)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 4.0 * n * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-
-    # Cold steps: before each, outside its events, 1 GiB is read to evict the
-    # Infinity Cache (256 MB) and the L2s, so the step starts with none of its data
-    # cached (a read leaves clean lines, so no write-back overlaps the step).
+    # Cold figures: before each run, 1 GiB is read to evict the Infinity Cache (256 MB)
+    # and the L2s (a read leaves clean lines, so no write-back overlaps what follows);
+    # the events and calls queue behind it, so host submission is not timed.
     flush = torch.ones((1 << 30) // 4, dtype=torch.int32, device=dev)
-    cold_ms = []
-    for k in range(max(5, args.steps // 10)):
-        flush.sum()
-        torch.cuda.synchronize()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        step()
-        c1.record(stream)
-        torch.cuda.synchronize()
-        cold_ms.append(c0.elapsed_time(c1))
+    cold_runs = max(5, args.steps // 10)
+    cold_med = median(cold_times(torch, stream, flush, step, cold_runs)) * 1e-3
+    # the dominant kernel alone, cold: k_fake_quant with the amax given reads all of x
+    # from HBM (none of it in the Infinity Cache) and writes y
+    hbm_only_us = median(cold_times(torch, stream, flush, lambda: nv.nvfp4_fake_quant(x, y=y, amax_in=a1), 9))
+    # the box's stream ceilings, from probe kernels with the kernels' access pattern and
+    # none of their arithmetic (best launch shape of a few; median of cold runs)
+    streams = stream_ceilings(torch, stream, flush, x, y, n)
     del flush
-    cold_ms.sort()
-    cold_med = cold_ms[len(cold_ms) // 2]
 
     value = STEP_BYTES_PER_ELEM * n / (ms_per_step * 1e-3) / 1e9
     result = {
@@ -535,10 +757,10 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "elements_per_s": round(n / (ms_per_step * 1e-3), 1),
         "ops": op_report,
-        "copy_gbs": round(copy_gbs, 1),
+        "stream_ceilings": streams,
         "cold_step": {"ms": round(cold_med, 4),
                       "gbs": round(STEP_BYTES_PER_ELEM * n / (cold_med * 1e-3) / 1e9, 1),
-                      "runs": len(cold_ms),
+                      "runs": cold_runs,
                       "note": "median step after reading 1 GiB (caches evicted); value is the warm rate"},
         "roofline": {
             "kernel": KERNEL_NAMES[dom],
@@ -548,8 +770,16 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "traffic_note": "FETCH_SIZE + WRITE_SIZE: bytes past the L2, Infinity-Cache hits included",
             "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_us": round(fq_ms * 1e3, 2),
+            "note": "in the step the amax pass before it leaves the last 192 MB of x in the "
+                    "Infinity Cache; hbm_only is the same kernel alone with nothing cached",
+            "hbm_only": {"us": round(hbm_only_us, 2),
+                         "achieved": round(dom_bytes / (hbm_only_us * 1e-6) / 1e9, 1),
+                         "frac": round(dom_bytes / (hbm_only_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "frac_of_copy_stream": round(dom_bytes / (hbm_only_us * 1e-6) / 1e9
+                                                      / streams["copy"]["cold_gbs"], 4)},
         },
         "cpu_baseline": None,
     }

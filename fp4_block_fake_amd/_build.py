@@ -1,4 +1,5 @@
-"""Compile libnvfp4.so in-tree with hipcc for gfx950.
+"""Compile libnvfp4.so (and libnvfp4_probe.so, the benchmark's HBM stream probes)
+in-tree with hipcc for gfx950.
 
 Kept free of package imports so it can run before the library exists:
 ``python fp4_block_fake_amd/_build.py``.
@@ -11,6 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "nvfp4.hip")
 LIB = os.path.join(PKG, "libnvfp4.so")
+PROBE_SRC = os.path.join(PKG, "csrc", "stream_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libnvfp4_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -23,13 +26,18 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
+def _compile(src: str, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, src]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    _compile(SRC, LIB, verbose)
+    _compile(PROBE_SRC, PROBE_LIB, verbose)
     return LIB
 
 

@@ -45,7 +45,7 @@ def fake_root(tmp_path, monkeypatch):
 
 def write_traffic(root, src_hash, hbm="12345"):
     (root / "profiles" / "traffic_k_x_w.txt").write_text(
-        "# comment: ignored\nsource_sha256_16: %s\nhbm_bytes_per_launch: %s\n" % (src_hash, hbm))
+        "# comment: ignored\nsource_sha256_16: %s\nbytes_past_l2_per_launch: %s\n" % (src_hash, hbm))
 
 
 def test_source_hash_covers_every_kernel_source(fake_root):
@@ -68,3 +68,25 @@ def test_traffic_only_for_the_source_it_was_measured_on(fake_root):
     write_traffic(fake_root, bench.kernel_source_hash(), hbm="n/a")
     assert bench.read_traffic("k_x", "w") is None                 # unreadable figure
 
+
+
+def test_oracle_runner_threads_give_the_single_threaded_bytes():
+    """The CPU-baseline runner shards rows over threads; amax and codes must not change."""
+    import numpy as np
+
+    import synth
+    x = synth.c5_weight(rows=40)
+    one, four = bench.OracleRunner(1), bench.OracleRunner(4)
+    assert one.amax(x) == four.amax(x)
+    a = one.amax(x)
+    p1, p4 = one.quantize(x, a), four.quantize(x, a)
+    assert len(p1) == 1 and len(p4) == 4
+    assert np.array_equal(p1[0][0], np.concatenate([p[0] for p in p4]))
+    assert np.array_equal(p1[0][1], np.concatenate([p[1] for p in p4]))
+    sibs = [s[:32] for s in synth.c3_siblings()]
+    assert one.amax(*sibs) == four.amax(*sibs)
+
+
+def test_host_info_names_the_cpus():
+    info = bench.host_info()
+    assert info["nproc"] >= 1 and info["usable_cpus"] >= 1
