@@ -61,6 +61,9 @@ def _load():
             "nvo_e4m3_decode_array": (None, [P, P, I64]),
             "nvo_e2m1_round_array": (None, [P, P, I64]),
             "nvo_f32_to_bf16_array": (None, [P, P, I64]),
+            "nvo_mx_quantize": (None, [P, I64, I64, P, P]),
+            "nvo_mx_dequantize": (None, [P, P, I64, I64, P]),
+            "nvo_mx_fake_quant": (ctypes.c_int, [P, P, I64, I64]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -182,6 +185,41 @@ def fake_quant(x: np.ndarray, amax_value: float | None = None) -> np.ndarray:
     rc = _load().nvo_fake_quant(_ptr(x), _ptr(y), rows, cols, amax_value)
     if rc != 0:
         raise MemoryError("oracle fake_quant: allocation failed")
+    return y
+
+
+# ---- the MXFP4 variant (block 32, one binary32 scale per block, no global scale) ---
+
+MX_BLOCK = 32
+
+
+def mx_quantize(x: np.ndarray):
+    """bf16 [rows, cols] -> (packed uint8 [rows, padded/2], scales float32 [rows, padded/32]),
+    padded = cols rounded up to a multiple of 32."""
+    x = _c(x, np.uint16)
+    rows, cols = x.shape
+    padded = -(-cols // MX_BLOCK) * MX_BLOCK
+    packed = np.empty((rows, padded // 2), np.uint8)
+    scales = np.empty((rows, padded // MX_BLOCK), np.float32)
+    _load().nvo_mx_quantize(_ptr(x), rows, cols, _ptr(packed), _ptr(scales))
+    return packed, scales
+
+
+def mx_dequantize(packed: np.ndarray, scales: np.ndarray, cols: int) -> np.ndarray:
+    packed = _c(packed, np.uint8)
+    scales = _c(scales, np.float32)
+    rows = packed.shape[0]
+    y = np.empty((rows, cols), np.uint16)
+    _load().nvo_mx_dequantize(_ptr(packed), _ptr(scales), rows, cols, _ptr(y))
+    return y
+
+
+def mx_fake_quant(x: np.ndarray) -> np.ndarray:
+    x = _c(x, np.uint16)
+    rows, cols = x.shape
+    y = np.empty((rows, cols), np.uint16)
+    if _load().nvo_mx_fake_quant(_ptr(x), _ptr(y), rows, cols) != 0:
+        raise MemoryError("oracle mx_fake_quant: allocation failed")
     return y
 
 

@@ -36,7 +36,12 @@
  *   R5  the observer state -1 means "no observation yet": the first update
  *       stores the current amax for both observer kinds;
  *   R6  a row whose length is not a multiple of 16 is zero-padded to the next
- *       multiple ([VX] quantize_weight_to_float4), and the unpack drops the pad.
+ *       multiple ([VX] quantize_weight_to_float4), and the unpack drops the pad;
+ *   R7  the MXFP4 variant ([VX] module constants: "block 32 with an fp32 scale")
+ *       is NVFP4's block step with 32-element blocks, the block scale kept in
+ *       binary32 as block_amax / 6 (no per-tensor factor, no E4M3 rounding),
+ *       the same clamp before it divides the elements, and the same element
+ *       rounding, sign rule and output product.
  *
  * Parity pins (tests/test_oracle_pins.py): E2M1 grid and ties against the
  * pages' printed values and a brute-force nearest-value search; E4M3 encode and
@@ -277,6 +282,81 @@ int nvo_fake_quant(const uint16_t* x, uint16_t* y, int64_t rows, int64_t cols, f
     float gs;
     nvo_quantize(x, rows, cols, amax, packed, scales, &gs);
     nvo_dequantize(packed, scales, gs, rows, cols, y);
+    free(packed);
+    free(scales);
+    return 0;
+}
+
+/* ---- MXFP4 variant (reading R7; [VX] module constants) ------------------------
+ * Blocks of 32 consecutive elements of one row, a row zero-padded to a multiple
+ * of 32.  Each block keeps one binary32 scale s = block_amax / 6 (a zero block
+ * has s = 0); elements are divided by max(s, 1e-12), rounded onto the E2M1 grid
+ * and signed exactly as in nvo_quantize; the unpack multiplies the signed
+ * magnitude by s and rounds to bf16.  Outputs: packed [rows, padded / 2] bytes
+ * (even column in the low nibble), scales [rows, padded / 32] binary32.          */
+#define MX_BLOCK 32
+
+void nvo_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* packed, float* scales)
+{
+    int64_t padded = (cols + MX_BLOCK - 1) / MX_BLOCK * MX_BLOCK;
+    int64_t nblk = padded / MX_BLOCK;
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t j = 0; j < nblk; j++) {
+            float val[MX_BLOCK];
+            for (int i = 0; i < MX_BLOCK; i++) {
+                int64_t c = j * MX_BLOCK + i;
+                val[i] = c < cols ? nvo_bf16_to_f32(x[r * cols + c]) : 0.0f;
+            }
+            float block_amax = 0.0f;
+            for (int i = 0; i < MX_BLOCK; i++)
+                if (fabsf(val[i]) > block_amax)
+                    block_amax = fabsf(val[i]);
+            float scale = block_amax / E2M1_MAX;
+            scales[r * nblk + j] = scale;
+            float divisor = scale < SCALE_EPS ? SCALE_EPS : scale;
+            uint8_t code[MX_BLOCK];
+            for (int i = 0; i < MX_BLOCK; i++) {
+                float scaled = val[i] / divisor;
+                if (scaled > E2M1_MAX) scaled = E2M1_MAX;
+                if (scaled < -E2M1_MAX) scaled = -E2M1_MAX;
+                int idx = nvo_e2m1_round(fabsf(scaled));
+                code[i] = (uint8_t)(scaled < 0.0f ? idx + 8 : idx);
+            }
+            for (int i = 0; i < MX_BLOCK / 2; i++)
+                packed[r * (padded / 2) + j * (MX_BLOCK / 2) + i] =
+                    (uint8_t)(code[2 * i] | (code[2 * i + 1] << 4));
+        }
+    }
+}
+
+void nvo_mx_dequantize(const uint8_t* packed, const float* scales, int64_t rows, int64_t cols, uint16_t* y)
+{
+    int64_t padded = (cols + MX_BLOCK - 1) / MX_BLOCK * MX_BLOCK;
+    int64_t nblk = padded / MX_BLOCK;
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t c = 0; c < cols; c++) {
+            uint8_t byte = packed[r * (padded / 2) + c / 2];
+            int code = (c % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+            float lut = (code & 8) ? -MAGNITUDE[code & 7] : MAGNITUDE[code & 7];
+            y[r * cols + c] = nvo_f32_to_bf16(lut * scales[r * nblk + c / MX_BLOCK]);
+        }
+    }
+}
+
+/* MXFP4 fake-quant: quantize, then dequantize (as nvo_fake_quant). */
+int nvo_mx_fake_quant(const uint16_t* x, uint16_t* y, int64_t rows, int64_t cols)
+{
+    int64_t padded = (cols + MX_BLOCK - 1) / MX_BLOCK * MX_BLOCK;
+    size_t np = (size_t)(rows * (padded / 2)), ns = (size_t)(rows * (padded / MX_BLOCK));
+    uint8_t* packed = (uint8_t*)malloc(np ? np : 1);
+    float* scales = (float*)malloc((ns ? ns : 1) * sizeof(float));
+    if (!packed || !scales) {
+        free(packed);
+        free(scales);
+        return -1;
+    }
+    nvo_mx_quantize(x, rows, cols, packed, scales);
+    nvo_mx_dequantize(packed, scales, rows, cols, y);
     free(packed);
     free(scales);
     return 0;
