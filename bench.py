@@ -356,6 +356,23 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
                                                workspace=ws), 4.5625 * nw, cold=True, elems=nw)
         del w, yw, pk, sc
 
+    if group("mx_"):
+        # the MXFP4 variant (32-element blocks, binary32 block scales, no amax pass): one
+        # launch per call; bytes per element 2 + 2 (fake-quant), 2 + 0.5 + 4 / 32 (pack)
+        for tag, arr in (("c4_weight_14336x4096", synth.c4_weight()), ("c5_weight_28672x8192", synth.c5_weight())):
+            xm = to_dev(arr)
+            del arr
+            nm = xm.numel()
+            ym = torch.empty_like(xm)
+            pm = torch.empty((xm.shape[0], xm.shape[1] // 2), dtype=torch.uint8, device=dev)
+            sm = torch.empty((xm.shape[0], xm.shape[1] // 32), dtype=torch.float32, device=dev)
+            line("mx_%s_fake_quant" % tag, lambda: nv.nvfp4_mx_fake_quant(xm, y=ym), 4.0 * nm, cold=True, elems=nm)
+            line("mx_%s_quantize_pack" % tag, lambda: nv.nvfp4_mx_quantize_pack(xm, packed=pm, scales=sm),
+                 2.625 * nm, cold=True, elems=nm)
+            line("mx_%s_dequant_unpack" % tag, lambda: nv.nvfp4_mx_dequant_unpack(pm, sm, y=ym), 2.625 * nm,
+                 cold=True, elems=nm)
+            del xm, ym, pm, sm
+
     if group("c5_"):
         wc = to_dev(synth.c5_weight())
         n, k = wc.shape

@@ -20,6 +20,7 @@ __all__ = [
     "nvfp4_strerror", "FakeQuantSTE", "blocks_per_row", "nvfp4_observe_fake_quant",
     "WORKSPACE_BYTES", "new_workspace", "nvfp4_fake_quant_ws", "nvfp4_quantize_pack_ws",
     "nvfp4_fake_quant_group_ws", "nvfp4_fake_quant_noalloc",
+    "MX_BLOCK", "mx_blocks_per_row", "nvfp4_mx_fake_quant", "nvfp4_mx_quantize_pack", "nvfp4_mx_dequant_unpack",
 ]
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
@@ -27,11 +28,13 @@ library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp
 OBS_STATIC_MINMAX = 0
 OBS_EMA = 1
 WORKSPACE_BYTES = 2304        # NVFP4_WORKSPACE_BYTES
+MX_BLOCK = 32                 # NVFP4_MX_BLOCK
 
 _EXPORTS = ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
             "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
             "nvfp4_observe_fake_quant", "nvfp4_fake_quant_ws", "nvfp4_quantize_pack_ws",
-            "nvfp4_fake_quant_group_ws", "nvfp4_fake_quant_noalloc", "nvfp4_strerror")
+            "nvfp4_fake_quant_group_ws", "nvfp4_fake_quant_noalloc", "nvfp4_mx_fake_quant",
+            "nvfp4_mx_quantize_pack", "nvfp4_mx_dequant_unpack", "nvfp4_strerror")
 
 
 class NVFP4Error(RuntimeError):
@@ -60,6 +63,9 @@ def _load() -> ctypes.CDLL:
     so.nvfp4_quantize_pack_ws.argtypes = [P, I64, I64, P, P, P, P, P, P]
     so.nvfp4_fake_quant_group_ws.argtypes = [P, P, P, P, I, P, P, P]
     so.nvfp4_fake_quant_noalloc.argtypes = [P, P, I64, I64, P, P]
+    so.nvfp4_mx_fake_quant.argtypes = [P, P, I64, I64, P]
+    so.nvfp4_mx_quantize_pack.argtypes = [P, I64, I64, P, P, P]
+    so.nvfp4_mx_dequant_unpack.argtypes = [P, P, I64, I64, P, P]
     so.nvfp4_strerror.argtypes = [I]
     so.nvfp4_strerror.restype = ctypes.c_char_p
     for name in _EXPORTS:
@@ -418,6 +424,66 @@ def nvfp4_quantize_pack_ws(x: torch.Tensor, amax_out: torch.Tensor | None = None
     _check(lib.nvfp4_quantize_pack_ws(_ptr(x), rows, cols, _ptr(amax_out), _ptr(packed), _ptr(scales),
                                       _ptr(global_scale), _ptr(ws), _stream(dev)), "nvfp4_quantize_pack_ws")
     return packed, scales, global_scale
+
+
+# ---- the MXFP4 variant: 32-element blocks, one binary32 scale each, no global scale
+
+def mx_blocks_per_row(cols: int) -> int:
+    """32-element blocks per row; a ragged row is zero-padded to a whole block."""
+    return -(-cols // MX_BLOCK)
+
+
+def nvfp4_mx_fake_quant(x: torch.Tensor, y: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 [R, C] -> MXFP4 fake-quantized bf16 [R, C] (y may be x)."""
+    rows, cols = _matrix(x, "x")
+    if y is None:
+        y = torch.empty_like(x)
+    _matrix(y, "y", x.device, x.shape)
+    _check(lib.nvfp4_mx_fake_quant(_ptr(x), _ptr(y), rows, cols, _stream(x.device)), "nvfp4_mx_fake_quant")
+    return y
+
+
+def nvfp4_mx_quantize_pack(x: torch.Tensor, packed: torch.Tensor | None = None,
+                           scales: torch.Tensor | None = None):
+    """bf16 [R, C] -> (packed uint8 [R, 16*nbr], float32 block scales [R, nbr]), nbr = ceil(C / 32)."""
+    rows, cols = _matrix(x, "x")
+    dev = x.device
+    nbr = mx_blocks_per_row(cols)
+    if packed is None:
+        packed = torch.empty((rows, 16 * nbr), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, nbr), dtype=torch.float32, device=dev)
+    _bytes(packed, "packed", (rows, 16 * nbr), dev)
+    if scales.dtype != torch.float32 or tuple(scales.shape) != (rows, nbr) or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous float32 tensor of shape %s" % ((rows, nbr),))
+    _same_device(scales, dev, "scales")
+    _check(lib.nvfp4_mx_quantize_pack(_ptr(x), rows, cols, _ptr(packed), _ptr(scales), _stream(dev)),
+           "nvfp4_mx_quantize_pack")
+    return packed, scales
+
+
+def nvfp4_mx_dequant_unpack(packed: torch.Tensor, scales: torch.Tensor, y: torch.Tensor | None = None,
+                            cols: int | None = None) -> torch.Tensor:
+    """(packed [R, 16*nbr], float32 scales [R, nbr]) -> bf16 [R, cols]; cols defaults to 32*nbr."""
+    if packed.dtype != torch.uint8 or packed.dim() != 2 or not packed.is_contiguous():
+        raise ValueError("packed must be a contiguous 2-D uint8 CUDA tensor")
+    _same_device(packed, None, "packed")
+    if packed.shape[1] % 16:
+        raise ValueError("packed rows hold 16 bytes per 32-element block")
+    rows, nbr = packed.shape[0], packed.shape[1] // 16
+    if cols is None:
+        cols = MX_BLOCK * nbr
+    if mx_blocks_per_row(cols) != nbr:
+        raise ValueError("cols=%d does not match %d packed blocks per row" % (cols, nbr))
+    if scales.dtype != torch.float32 or tuple(scales.shape) != (rows, nbr) or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous float32 tensor of shape %s" % ((rows, nbr),))
+    _same_device(scales, packed.device, "scales")
+    if y is None:
+        y = torch.empty((rows, cols), dtype=torch.bfloat16, device=packed.device)
+    _matrix(y, "y", packed.device, (rows, cols))
+    _check(lib.nvfp4_mx_dequant_unpack(_ptr(packed), _ptr(scales), rows, cols, _ptr(y), _stream(packed.device)),
+           "nvfp4_mx_dequant_unpack")
+    return y
 
 
 class FakeQuantSTE(torch.autograd.Function):

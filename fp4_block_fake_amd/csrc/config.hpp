@@ -97,6 +97,9 @@ namespace {
 #ifndef NVFP4_DQ_WG_PER_CU
 #define NVFP4_DQ_WG_PER_CU 32
 #endif
+#ifndef NVFP4_MX_WG_PER_CU
+#define NVFP4_MX_WG_PER_CU 32     // workgroups per CU of the MXFP4 passes (one pass each, no table)
+#endif
 // 1: the quantizing passes walk the tensor from its end, so they start on the
 // data the amax pass read last (measured no better than forward on MI355X).
 #ifndef NVFP4_REVERSE

@@ -56,6 +56,7 @@
 // kernels.hpp  amax, fake-quant (single, dual, group), quantize-pack,
 //              dequant-unpack, the ragged-row kernels, the observer steps
 // linear.hpp   the linear layer over a packed weight (MFMA)
+// mx.hpp       the MXFP4 variant (32-element blocks, binary32 block scales)
 // nvfp4.hip    host helpers (launch shapes, argument checks) and the C ABI
 
 #include <hip/hip_runtime.h>
@@ -68,6 +69,7 @@
 #include "nvfp4.h"
 #include "kernels.hpp"
 #include "linear.hpp"
+#include "mx.hpp"
 
 namespace {
 
@@ -614,6 +616,21 @@ nvfp4_status enqueue_fake_quant_ws(const void* x, void* y, int64_t cols, const M
 // device address is looked up once per GPU (with that GPU current) and only
 // that address is ever passed to a kernel.  Every call on one GPU shares the
 // array, so calls that overlap in time on one GPU race.
+// Shape of an MXFP4 call: blocks of 32 per row, whole-block rows or not.
+nvfp4_status check_mx_matrix(int64_t rows, int64_t cols, Matrix* m)
+{
+    if (rows < 0 || cols < 1)
+        return NVFP4_ERR_SHAPE;
+    const int64_t nbr = (cols + kMxBlock - 1) / kMxBlock;
+    if (rows > 0 && nbr > (INT64_MAX / 128) / rows)
+        return NVFP4_ERR_SHAPE;
+    m->numel = rows * cols;
+    m->nbr = nbr;
+    m->nblocks = rows * nbr;
+    m->ragged = cols % kMxBlock != 0;
+    return NVFP4_OK;
+}
+
 }  // namespace
 
 static __device__ __align__(256) uint8_t scratch[NVFP4_WORKSPACE_BYTES];
@@ -1127,6 +1144,96 @@ nvfp4_status nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* pa
     if (m <= NVFP4_TILE_SMALL_M)
         return enqueue_linear_tiled<NVFP4_TILE_MW_SMALL, kNW>(x, m, k, packed, scales, global_scale, n, bias, y, s);
     return enqueue_linear_tiled<NVFP4_TILE_MW, kNW>(x, m, k, packed, scales, global_scale, n, bias, y, s);
+}
+
+nvfp4_status nvfp4_mx_fake_quant(const void* x, void* y, int64_t rows, int64_t cols, void* stream)
+{
+    Matrix m;
+    const nvfp4_status st = check_mx_matrix(rows, cols, &m);
+    if (st != NVFP4_OK)
+        return st;
+    if (m.numel > 0 && (!x || !y))
+        return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(y, 16))
+        return NVFP4_ERR_ALIGN;
+    const uint64_t bytes = 2 * (uint64_t)m.numel;
+    if (x != y && overlap(x, bytes, y, bytes))
+        return NVFP4_ERR_OVERLAP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (m.numel == 0)
+        return NVFP4_OK;
+    if (m.ragged) {
+        k_mx_fake_quant_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
+            static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), RaggedShape{cols, m.nbr, m.nblocks});
+        return launched();
+    }
+    const int64_t nq = 4 * m.nblocks;
+    k_mx_fake_quant<<<persistent_grid(nq, (int64_t)kThreads * kUnroll, NVFP4_MX_WG_PER_CU), kThreads, 0, s>>>(
+        static_cast<const uint4*>(x), static_cast<uint4*>(y), nq);
+    return launched();
+}
+
+nvfp4_status nvfp4_mx_quantize_pack(const void* x, int64_t rows, int64_t cols, uint8_t* packed, float* scales,
+                                    void* stream)
+{
+    Matrix m;
+    const nvfp4_status st = check_mx_matrix(rows, cols, &m);
+    if (st != NVFP4_OK)
+        return st;
+    if (m.numel > 0 && (!x || !packed || !scales))
+        return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 4))
+        return NVFP4_ERR_ALIGN;
+    const Region in[1] = {{x, 2 * (uint64_t)m.numel}};
+    const Region out[2] = {{packed, 16 * (uint64_t)m.nblocks}, {scales, 4 * (uint64_t)m.nblocks}};
+    if (check_regions(in, 1, out, 2, false) != NVFP4_OK)
+        return NVFP4_ERR_OVERLAP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (m.numel == 0)
+        return NVFP4_OK;
+    if (m.ragged) {
+        k_mx_quantize_pack_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
+            static_cast<const uint16_t*>(x), reinterpret_cast<uint4*>(packed), scales,
+            RaggedShape{cols, m.nbr, m.nblocks});
+        return launched();
+    }
+    const int64_t nq = 4 * m.nblocks;
+    k_mx_quantize_pack<<<persistent_grid(nq, (int64_t)kThreads * kUnroll, NVFP4_MX_WG_PER_CU), kThreads, 0, s>>>(
+        static_cast<const uint4*>(x), reinterpret_cast<uint32_t*>(packed), scales, nq);
+    return launched();
+}
+
+nvfp4_status nvfp4_mx_dequant_unpack(const uint8_t* packed, const float* scales, int64_t rows, int64_t cols,
+                                     void* y, void* stream)
+{
+    Matrix m;
+    const nvfp4_status st = check_mx_matrix(rows, cols, &m);
+    if (st != NVFP4_OK)
+        return st;
+    if (m.numel == 0)
+        return NVFP4_OK;
+    if (!packed || !scales || !y)
+        return NVFP4_ERR_NULL;
+    if (!aligned(packed, 16) || !aligned(scales, 4) || !aligned(y, 16))
+        return NVFP4_ERR_ALIGN;
+    const Region in[2] = {{packed, 16 * (uint64_t)m.nblocks}, {scales, 4 * (uint64_t)m.nblocks}};
+    const Region out[1] = {{y, 2 * (uint64_t)m.numel}};
+    if (check_regions(in, 2, out, 1, false) != NVFP4_OK)
+        return NVFP4_ERR_OVERLAP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (m.ragged) {
+        k_mx_dequant_unpack_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
+            reinterpret_cast<const uint4*>(packed), scales, static_cast<uint16_t*>(y),
+            RaggedShape{cols, m.nbr, m.nblocks});
+        return launched();
+    }
+    const int64_t nq = 4 * m.nblocks;
+    k_mx_dequant_unpack<<<persistent_grid(nq, (int64_t)kThreads * kDqUnroll, NVFP4_MX_WG_PER_CU), kThreads, 0,
+                          s>>>(reinterpret_cast<const uint32_t*>(packed), scales, static_cast<uint4*>(y), nq);
+    return launched();
 }
 
 }  // extern "C"

@@ -309,6 +309,50 @@ nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols,
                                       void* workspace, void* stream);
 
 /*
+ * MXFP4 variant (VideoX-Fun page, module constants: the comment naming block 32
+ * with an fp32 scale as the MXFP4 flavour).  Taken literally: blocks of
+ * NVFP4_MX_BLOCK = 32 consecutive elements of one row (a row is zero-padded to
+ * whole blocks), one binary32 scale per block and no per-tensor factor:
+ *   s    = block_amax / 6                      (binary32, stored as is; 0 for a zero block)
+ *   q    = x / max(s, 1e-12);  idx = E2M1 round-to-nearest-even of min(|q|, 6)
+ *   code = idx | 8 * (q < 0)
+ *   fake-quant / unpack output = bf16_RNE(LUT[code] * s)
+ * (The OCP MXFP4 format stores a power-of-two E8M0 scale; the page's flavour keeps
+ * the scale in fp32, and that is what these calls do.)  No amax pass: one launch
+ * per call.  nbr = ceil(cols / 32) blocks per row.
+ */
+#define NVFP4_MX_BLOCK 32
+
+/*
+ * nvfp4_mx_fake_quant -- bf16 [rows, cols] -> bf16 [rows, cols] MXFP4 fake-quant.
+ *   x, y  device bf16, 16-byte aligned; y == x (exact in-place) is allowed.
+ * Errors: SHAPE, NULL, ALIGN, OVERLAP, HIP.
+ */
+nvfp4_status nvfp4_mx_fake_quant(const void* x, void* y, int64_t rows, int64_t cols, void* stream);
+
+/*
+ * nvfp4_mx_quantize_pack -- bf16 [rows, cols] -> packed MXFP4.
+ *   packed  device uint8 [rows, 16 * nbr], 16-byte aligned: byte i of a row holds
+ *           the code of (padded) column 2i in its low nibble and of 2i + 1 in its
+ *           high nibble; padding columns get code 0
+ *   scales  device float [rows, nbr], 4-byte aligned: the binary32 block scales
+ * Outputs must not overlap x or each other.
+ * Errors: SHAPE, NULL, ALIGN, OVERLAP, HIP.
+ */
+nvfp4_status nvfp4_mx_quantize_pack(const void* x, int64_t rows, int64_t cols, uint8_t* packed, float* scales,
+                                    void* stream);
+
+/*
+ * nvfp4_mx_dequant_unpack -- packed MXFP4 -> bf16 [rows, cols] (LUT[code] * s,
+ * rounded to bf16).  Layouts as nvfp4_mx_quantize_pack writes them; packed
+ * 16-byte aligned, scales 4-byte aligned, y 16-byte aligned and not overlapping
+ * the inputs.
+ * Errors: SHAPE, NULL, ALIGN, OVERLAP, HIP.
+ */
+nvfp4_status nvfp4_mx_dequant_unpack(const uint8_t* packed, const float* scales, int64_t rows, int64_t cols,
+                                     void* y, void* stream);
+
+/*
  * nvfp4_fake_quant_noalloc -- nvfp4_fake_quant_ws without a workspace argument,
  * for callers that cannot allocate device memory at all (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation).  Same y and

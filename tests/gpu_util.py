@@ -81,3 +81,13 @@ def oracle_dequantize(packed, scales, gs, cols):
     rows = np.array_split(np.arange(packed.shape[0]), min(ORACLE_THREADS, max(1, packed.shape[0])))
     return np.concatenate(_map(lambda r: oracle.dequantize(packed[r[0]:r[-1] + 1], scales[r[0]:r[-1] + 1], gs, cols),
                                [r for r in rows if r.size]))
+
+
+def oracle_mx_fake_quant(x):
+    return np.concatenate(_map(oracle.mx_fake_quant, _row_shards(x)))
+
+
+def oracle_mx_quantize(x):
+    """-> (packed, scales), as oracle.mx_quantize."""
+    parts = _map(oracle.mx_quantize, _row_shards(x))
+    return np.concatenate([p for p, _ in parts]), np.concatenate([s for _, s in parts])

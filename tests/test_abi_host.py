@@ -34,7 +34,8 @@ def test_header_declares_every_call():
     for n in ("nvfp4_amax", "nvfp4_fake_quant", "nvfp4_fake_quant_group", "nvfp4_fake_quant_dual",
               "nvfp4_quantize_pack", "nvfp4_dequant_unpack", "nvfp4_linear", "nvfp4_observer_update",
               "nvfp4_observe_fake_quant", "nvfp4_fake_quant_ws", "nvfp4_quantize_pack_ws",
-              "nvfp4_fake_quant_group_ws", "nvfp4_fake_quant_noalloc", "nvfp4_strerror"):
+              "nvfp4_fake_quant_group_ws", "nvfp4_fake_quant_noalloc", "nvfp4_mx_fake_quant",
+              "nvfp4_mx_quantize_pack", "nvfp4_mx_dequant_unpack", "nvfp4_strerror"):
         assert n in names
 
 
@@ -69,6 +70,10 @@ int main(void)
     bad |= nvfp4_quantize_pack_ws(0, 4, 0, 0, 0, 0, 0, 0, 0) != NVFP4_ERR_SHAPE;
     bad |= nvfp4_fake_quant_group_ws(0, 0, 0, 0, 1, 0, 0, 0) != NVFP4_ERR_NULL;
     bad |= nvfp4_fake_quant_noalloc(0, 0, 4, 16, 0, 0) != NVFP4_ERR_NULL;
+    bad |= nvfp4_mx_fake_quant(0, 0, 4, 0, 0) != NVFP4_ERR_SHAPE;
+    bad |= nvfp4_mx_quantize_pack(0, 4, 32, 0, 0, 0) != NVFP4_ERR_NULL;
+    bad |= nvfp4_mx_dequant_unpack(0, 0, 4, 32, 0, 0) != NVFP4_ERR_NULL;
+    bad |= NVFP4_MX_BLOCK != 32;
     bad |= NVFP4_WORKSPACE_BYTES < 2304;
     bad |= strcmp(nvfp4_strerror(NVFP4_OK), "ok") != 0;
     printf("%s\n", bad ? "FAIL" : "OK");
@@ -352,6 +357,28 @@ def test_fake_quant_noalloc_validation():
     assert call(y=x + 16) == ERR_OVERLAP
     assert call(amax=x + 64) == ERR_OVERLAP
     assert call(amax=y + 4) == ERR_OVERLAP
+
+
+def test_mx_validation():
+    G = 1 << 30
+    x, y, p, sc = A, A + G, A + 2 * G, A + 3 * G
+    fq = nv.lib.nvfp4_mx_fake_quant
+    assert fq(P(x), P(y), 4, 0, None) == ERR_SHAPE
+    assert fq(P(x), P(y), -1, 32, None) == ERR_SHAPE
+    assert fq(None, P(y), 4, 32, None) == ERR_NULL
+    assert fq(P(x + 8), P(y), 4, 32, None) == ERR_ALIGN
+    assert fq(P(x), P(x + 16), 4, 32, None) == ERR_OVERLAP
+    qp = nv.lib.nvfp4_mx_quantize_pack
+    assert qp(P(x), 4, 32, None, P(sc), None) == ERR_NULL
+    assert qp(P(x), 4, 32, P(p + 8), P(sc), None) == ERR_ALIGN       # packed 16-byte aligned
+    assert qp(P(x), 4, 32, P(p), P(sc + 2), None) == ERR_ALIGN
+    assert qp(P(x), 4, 32, P(x + 64), P(sc), None) == ERR_OVERLAP
+    assert qp(P(x), 4, 32, P(p), P(p + 16), None) == ERR_OVERLAP     # scales inside the codes
+    dq = nv.lib.nvfp4_mx_dequant_unpack
+    assert dq(P(p), None, 4, 32, P(y), None) == ERR_NULL
+    assert dq(P(p), P(sc), 4, 32, P(y + 2), None) == ERR_ALIGN
+    assert dq(P(p), P(sc), 4, 32, P(p), None) == ERR_OVERLAP
+    assert dq(P(p), P(sc), 0, 32, None, None) == OK                  # empty: nothing to do
 
 
 def test_quantize_pack_ws_validation():
