@@ -206,7 +206,9 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
             r["elements_per_s"] = round(elems / (us * 1e-6), 1)
         return r
 
-    flush = torch.ones((1 << 30) // 4, dtype=torch.int32, device=dev)
+    # float32, so that sum() is one read-only reduction over 1 GiB (an int32 tensor would
+    # first be widened to int64, a 2 GB write stream that then overlaps the timed call)
+    flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
 
     def cold_us(fn, reps=9):
         """Median GPU time of single calls, each after a 1 GiB read has evicted the
@@ -425,7 +427,7 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
                     f(p_, s_)
                 return call
             gen = torch.Generator(device="cpu").manual_seed(7)
-            for m in (1, 16, 64, 128, 256, 1024):
+            for m in (1, 16, 64, 128, 256, 512, 1024, 2048):
                 xm = torch.randn(m, k, generator=gen).to(torch.bfloat16).to(dev)
                 ym = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
                 res = timed(lambda: nv.nvfp4_linear(xm, packed, scales, gsc, y=ym),
@@ -739,7 +741,7 @@ def main():
     # Cold figures: before each run, 1 GiB is read to evict the Infinity Cache (256 MB)
     # and the L2s (a read leaves clean lines, so no write-back overlaps what follows);
     # the events and calls queue behind it, so host submission is not timed.
-    flush = torch.ones((1 << 30) // 4, dtype=torch.int32, device=dev)
+    flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)     # sum(): a pure read
     cold_runs = max(5, args.steps // 10)
     cold_med = median(cold_times(torch, stream, flush, step, cold_runs)) * 1e-3
     # the dominant kernel alone, cold: k_fake_quant with the amax given reads all of x

@@ -91,6 +91,15 @@ namespace {
 #ifndef NVFP4_TILE_XCD_REMAP
 #define NVFP4_TILE_XCD_REMAP 1    // 1: the tiled linear groups each weight tile's x tiles on one XCD
 #endif
+#ifndef NVFP4_LIN_LDS_M
+#define NVFP4_LIN_LDS_M 384       // rows of x from which the linear layer decodes weight tiles into LDS
+#endif
+#ifndef NVFP4_LIN_LDS_WAVES
+#define NVFP4_LIN_LDS_WAVES 8     // waves per workgroup of the LDS-staged linear kernel (4 or 8)
+#endif
+#ifndef NVFP4_LIN_LDS_REMAP
+#define NVFP4_LIN_LDS_REMAP 1     // 1: the LDS-staged linear kernel orders its tiles by XCD
+#endif
 #ifndef NVFP4_TILE_DEPTH
 #define NVFP4_TILE_DEPTH 6        // K steps of weight loads in flight per tiled-linear wave (even)
 #endif

@@ -4,6 +4,8 @@
 #ifndef NVFP4_LINEAR_HPP
 #define NVFP4_LINEAR_HPP
 
+#include <type_traits>
+
 #include "device.hpp"
 
 namespace {
@@ -449,6 +451,209 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_linear_tiled(const uint16_t
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int64_t m = m0 + 32 * i + (j % 4) + 8 * (j / 4) + 4 * h;
+                if (m < M) {
+                    const f32x2 o = {acc[i][t][j] + b, 0.0f};
+                    y[m * N + n] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(o, bf16x2)) & 0xFFFFu);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- linear, weight tiles decoded into LDS
+//
+// For many rows of x (the layer is compute-bound there), the weight is decoded
+// once per workgroup and K step into LDS as bf16, and both MFMA operands are read
+// from LDS, so each weight element is decoded once per kLdsM rows of x instead of
+// once per 32-row x tile of a wave.  A workgroup of W waves computes a tile of
+// kLdsM = 256 rows of x by 32 W weight rows; wave w owns x rows 64 (w % 4) .. +64
+// against weight rows 128 (w / 4) .. +128 (2 x 4 tiles of
+// v_mfma_f32_32x32x16_bf16, operand and accumulator layouts as in
+// k_linear_tiled).  Per 64-wide K step, each thread stages 2048 / W 16-byte
+// pieces of x and decodes the 32 weight codes (16 bytes, two block scales) of
+// one half row into 64 bytes of bf16: the same decode as dequant-unpack, so the
+// weight is bit for bit the tensor dequant-unpack writes.  LDS holds two stages
+// of both tiles (the next stage is written while this one is read); x loads
+// run two steps ahead in registers, code loads four.  The next stage's decode
+// and LDS writes sit between this stage's MFMA slices so that the VALU work
+// overlaps the matrix cores.  With 8 waves a wave needs under 256 VGPRs, so two
+// waves share each SIMD.  Rows of x past M read row M - 1 and weight rows past
+// N read row 0: an output element depends only on its own rows, and those are
+// never stored.
+constexpr int kLdsM = 256;
+constexpr int kLdsK = 64;
+constexpr int kLdsStride = kLdsK + 8;          // bf16 per LDS row (padding against bank conflicts)
+constexpr int kLdsXDepth = 2;                  // register stages of x loads in flight
+constexpr int kLdsWDepth = 4;                  // register stages of code loads in flight
+
+template <int W>
+constexpr int lds_n() { return 32 * W; }       // weight rows per workgroup
+template <int W>
+constexpr size_t lds_bytes() { return (size_t)2 * (kLdsM + lds_n<W>()) * kLdsStride * 2; }
+
+template <int W>
+__global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                       const uint8_t* __restrict__ packed,
+                                                       const uint8_t* __restrict__ scales,
+                                                       const float* __restrict__ gs_in, int64_t N,
+                                                       const uint16_t* __restrict__ bias, uint16_t* __restrict__ y)
+{
+    static_assert(W == 4 || W == 8, "4 or 8 waves");
+    constexpr int kT = 64 * W;                 // threads
+    constexpr int kN = lds_n<W>();             // weight rows per workgroup
+    constexpr int kXP = kLdsM * (kLdsK / 8) / kT;   // 16-byte pieces of x per thread and step
+    static_assert(kXP % 4 == 0 && 2 * kN == kT, "staging shares");
+    __shared__ float sd_of[128];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(lin_lds);          // [2][kLdsM][kLdsStride]
+    uint16_t* ws = xs + 2 * kLdsM * kLdsStride;                     // [2][kN][kLdsStride]
+    const float gs = *gs_in;
+    if (threadIdx.x < 128)
+        sd_of[threadIdx.x] = e4m3_decode(threadIdx.x) / gs;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int c = lane & 31, h = lane >> 5;
+    const int wm = wave % 4, wn = wave / 4;
+    // XCD-aware order: workgroups go to the 8 XCDs round-robin by id; XCD k takes a
+    // contiguous run of weight tiles, x tile by x tile, so the workgroups running on
+    // one XCD at a time share their x tile's K slabs in that XCD's L2.
+    uint32_t bx = blockIdx.x, by = blockIdx.y;
+    if (NVFP4_LIN_LDS_REMAP && gridDim.y % 8 == 0) {
+        const uint32_t w = blockIdx.x + blockIdx.y * gridDim.x;
+        const uint32_t l = w / 8, per = gridDim.y / 8;               // weight tiles per XCD
+        bx = l / per;
+        by = (w % 8) * per + l % per;
+    }
+    const int64_t m0 = (int64_t)bx * kLdsM, n0 = (int64_t)by * kN;
+
+    // this thread's share of the staging: x rows m0 + tid / 8 + (kT / 8) j (j < kXP)
+    // at columns 8 (tid % 8) of the step; weight row n0 + tid / 2, the codes of
+    // columns 32 (tid % 2) .. + 32 of the step
+    const uint16_t* xrow[kXP];
+#pragma unroll
+    for (int j = 0; j < kXP; ++j) {
+        const int64_t m = m0 + tid / 8 + (kT / 8) * j;
+        xrow[j] = m < M ? x + m * K + 8 * (tid % 8) : nullptr;
+    }
+    const int wr = tid >> 1, wh = tid & 1;
+    const int64_t wrn = n0 + wr < N ? n0 + wr : 0;
+    const uint8_t* wrow = packed + wrn * (K / 2) + 16 * wh;
+    const uint8_t* srow = scales + wrn * (K / 16) + 2 * wh;
+
+    auto load_x = [&](int64_t st, uint4 (&v)[kXP]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kXP; ++j)
+            v[j] = xrow[j] ? *reinterpret_cast<const uint4*>(xrow[j] + st * kLdsK) : make_uint4(0u, 0u, 0u, 0u);
+    };
+    auto load_w = [&](int64_t st, uint4& cw, uint32_t& sc) __attribute__((always_inline)) {
+        cw = *reinterpret_cast<const uint4*>(wrow + st * (kLdsK / 2));
+        sc = *reinterpret_cast<const uint16_t*>(srow + st * (kLdsK / 16));
+    };
+    // piece q (0..3) of the staging of one step into buffer buf: a quarter of the
+    // thread's x pieces and one decoded dword of its codes (eight weights)
+    auto stage = [&](int buf, int q, const uint4 (&xv)[kXP], const uint4& cw, uint32_t sc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jj = 0; jj < kXP / 4; ++jj) {
+            const int j = (kXP / 4) * q + jj;
+            *reinterpret_cast<uint4*>(xs + (buf * kLdsM + tid / 8 + (kT / 8) * j) * kLdsStride + 8 * (tid % 8)) =
+                xv[j];
+        }
+        const float sd = sd_of[(sc >> (8 * (q / 2))) & 0x7Fu];
+        *reinterpret_cast<uint4*>(ws + (buf * kN + wr) * kLdsStride + 32 * wh + 8 * q) =
+            decode_half(dword_of(cw, q), sd);
+    };
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                acc[i][t][j] = 0.0f;
+    // slice q (16 of the step's 64 K) of this stage's MFMAs from buffer buf
+    auto mma_slice = [&](int buf, int q) __attribute__((always_inline)) {
+        bf16x8 a[2], b[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            a[i] = *reinterpret_cast<const bf16x8*>(xs + (buf * kLdsM + 64 * wm + 32 * i + c) * kLdsStride +
+                                                    16 * q + 8 * h);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            b[t] = *reinterpret_cast<const bf16x8*>(ws + (buf * kN + 128 * wn + 32 * t + c) * kLdsStride +
+                                                    16 * q + 8 * h);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[t], acc[i][t], 0, 0, 0);
+    };
+
+    const int64_t steps = K / kLdsK;
+    uint4 xr[kLdsXDepth][kXP];
+    uint4 cr[kLdsWDepth];
+    uint32_t sr[kLdsWDepth];
+#pragma unroll
+    for (int d = 0; d < kLdsWDepth; ++d)
+        if (d < steps)
+            load_w(d, cr[d], sr[d]);
+#pragma unroll
+    for (int d = 0; d < kLdsXDepth; ++d)
+        if (d < steps)
+            load_x(d, xr[d]);
+    __syncthreads();                                          // sd_of
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        stage(0, q, xr[0], cr[0], sr[0]);
+    if (kLdsXDepth < steps)
+        load_x(kLdsXDepth, xr[0]);
+    if (kLdsWDepth < steps)
+        load_w(kLdsWDepth, cr[0], sr[0]);
+    __syncthreads();
+    static_assert(kLdsWDepth == 4 && kLdsXDepth == 2, "ring indices repeat every four steps");
+    // step st0 + D of a group of four: the ring slots are compile-time constants, so
+    // the rings stay in registers
+    auto step = [&](int64_t st0, auto dc) __attribute__((always_inline)) {
+        constexpr int D = decltype(dc)::value;
+        constexpr int cur = D & 1, nxt = cur ^ 1, xn = (D + 1) % kLdsXDepth, wnx = (D + 1) % kLdsWDepth;
+        const int64_t st = st0 + D;
+        if (st >= steps)
+            return;
+        const bool more = st + 1 < steps;
+        // slice q of this stage's MFMAs, then piece q of the next stage's staging
+        auto slice = [&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            mma_slice(cur, q);
+            if (more)
+                stage(nxt, q, xr[xn], cr[wnx], sr[wnx]);
+        };
+        slice(std::integral_constant<int, 0>{});
+        slice(std::integral_constant<int, 1>{});
+        slice(std::integral_constant<int, 2>{});
+        slice(std::integral_constant<int, 3>{});
+        if (st + 1 + kLdsXDepth < steps)
+            load_x(st + 1 + kLdsXDepth, xr[xn]);
+        if (st + 1 + kLdsWDepth < steps)
+            load_w(st + 1 + kLdsWDepth, cr[wnx], sr[wnx]);
+        __syncthreads();
+    };
+    for (int64_t st0 = 0; st0 < steps; st0 += kLdsWDepth) {
+        step(st0, std::integral_constant<int, 0>{});
+        step(st0, std::integral_constant<int, 1>{});
+        step(st0, std::integral_constant<int, 2>{});
+        step(st0, std::integral_constant<int, 3>{});
+    }
+
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int64_t n = n0 + 128 * wn + 32 * t + c;
+            if (n >= N)
+                continue;
+            const float b = bias ? bf16_value(bias[n]) : 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int64_t m = m0 + 64 * wm + 32 * i + (j % 4) + 8 * (j / 4) + 4 * h;
                 if (m < M) {
                     const f32x2 o = {acc[i][t][j] + b, 0.0f};
                     y[m * N + n] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(o, bf16x2)) & 0xFFFFu);
