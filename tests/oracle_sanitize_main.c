@@ -10,7 +10,9 @@
  * Input file: a sequence of cases, each int64 rows, int64 cols, then rows*cols bf16
  * bit patterns; then int64 nf and nf float32 values for the element-wise forms.
  * Output file, per case: float amax, float gs, packed [rows, 8*nbr], scales [rows, nbr],
- * dequantized bf16 [rows, cols], fake-quant bf16 [rows, cols]; then the group amax of all
+ * dequantized bf16 [rows, cols], fake-quant bf16 [rows, cols], and the MXFP4 variant's
+ * packed [rows, 16*mbr], float scales [rows, mbr], dequantized and fake-quant bf16
+ * (mbr = ceil(cols / 32)); then the group amax of all
  * cases; then for the nf floats: E4M3 codes, E2M1 codes of |v|, bf16 roundings; then
  * the 256 E4M3 decodes; then the observer on each of the first min(nf, 64) floats.
  */
@@ -32,6 +34,9 @@ void nvo_e4m3_encode_array(const float* v, uint8_t* out, int64_t n);
 void nvo_e4m3_decode_array(const uint8_t* b, float* out, int64_t n);
 void nvo_e2m1_round_array(const float* a, uint8_t* out, int64_t n);
 void nvo_f32_to_bf16_array(const float* f, uint16_t* out, int64_t n);
+void nvo_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* packed, float* scales);
+void nvo_mx_dequantize(const uint8_t* packed, const float* scales, int64_t rows, int64_t cols, uint16_t* y);
+int nvo_mx_fake_quant(const uint16_t* x, uint16_t* y, int64_t rows, int64_t cols);
 
 #define MAX_CASES 64
 
@@ -96,6 +101,19 @@ int main(int argc, char** argv)
         put(out, scales, (size_t)(rows * nbr));
         put(out, dq, (size_t)n * 2);
         put(out, fq, (size_t)n * 2);
+        int64_t mbr = (cols + 31) / 32;
+        uint8_t* mpacked = (uint8_t*)exact((size_t)(rows * 16 * mbr));
+        float* mscales = (float*)exact((size_t)(rows * mbr) * 4);
+        nvo_mx_quantize(x, rows, cols, mpacked, mscales);
+        nvo_mx_dequantize(mpacked, mscales, rows, cols, dq);
+        if (nvo_mx_fake_quant(x, fq, rows, cols) != 0)
+            return 3;
+        put(out, mpacked, (size_t)(rows * 16 * mbr));
+        put(out, mscales, (size_t)(rows * mbr) * 4);
+        put(out, dq, (size_t)n * 2);
+        put(out, fq, (size_t)n * 2);
+        free(mpacked);
+        free(mscales);
         free(packed);
         free(scales);
         free(dq);

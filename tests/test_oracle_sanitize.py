@@ -3,7 +3,8 @@
 tests/oracle_sanitize_main.c links the oracle's C source with both sanitizers, gives
 every buffer exactly the size the oracle's contract states, and runs amax, quantize,
 dequantize, fake-quant, the group amax, the observer and the element-wise forms over
-ragged, empty and special-value tensors.  Any out-of-bounds access, use after free,
+ragged, empty and special-value tensors, and the MXFP4 variant's quantize, dequantize and
+fake-quant on the same tensors.  Any out-of-bounds access, use after free,
 leak, signed overflow, bad shift or out-of-range float-to-int conversion aborts the
 run.  Its outputs must also equal the normal (-O2) build's, byte for byte: the
 sanitized build is compiled at -O1, so this also checks that the oracle's results do
@@ -26,7 +27,8 @@ MAIN_SRC = os.path.join(HERE, "oracle_sanitize_main.c")
 SANITIZERS = "-fsanitize=address,undefined,float-cast-overflow"
 
 # ragged rows, single elements, empty, a wide row, several blocks per row
-SHAPES = [(0, 16), (1, 1), (1, 16), (3, 20), (7, 1), (5, 33), (17, 144), (2, 48), (4, 16), (9, 31)]
+SHAPES = [(0, 16), (1, 1), (1, 16), (3, 20), (7, 1), (5, 33), (17, 144), (2, 48), (4, 16), (9, 31), (3, 64),
+          (2, 65)]
 
 
 def special_tensor(shape, rng):
@@ -62,6 +64,10 @@ def expected(cases, fl):
         out += p.tobytes() + s.tobytes()
         out += oracle.dequantize(p, s, g, cols).tobytes()
         out += oracle.fake_quant(x, a).tobytes()
+        mp, ms = oracle.mx_quantize(x)
+        out += mp.tobytes() + ms.tobytes()
+        out += oracle.mx_dequantize(mp, ms, cols).tobytes()
+        out += oracle.mx_fake_quant(x).tobytes()
     out += struct.pack("<f", oracle.amax_group(cases))
     mag = np.abs(fl)
     out += oracle.e4m3_encode_array(fl).tobytes()
