@@ -219,6 +219,17 @@ int quant_wg_per_cu(int64_t nhalves, int mid, int large)
     return nhalves * 16 < NVFP4_MID_BYTES ? mid : large;
 }
 
+// Ragged rows of even length take the half-block kernels (32-bit half indices).
+bool even_rows(int64_t cols, const Matrix& m)
+{
+    return m.ragged && cols % 2 == 0 && m.nblocks < ((int64_t)1 << 31);
+}
+
+EvenRows even_rows_of(const void* x, int64_t cols, const Matrix& m)
+{
+    return EvenRows{static_cast<const uint32_t*>(x), cols, (uint32_t)(2 * m.nbr), 2 * m.nblocks};
+}
+
 // Workgroups per CU of the two-output pass over nhalves half blocks.
 int dual_wg_per_cu(int64_t nhalves)
 {
@@ -239,7 +250,17 @@ nvfp4_status enqueue_fake_quant(const void* x, void* y, int64_t cols, const Matr
 {
     if (m.numel == 0)
         return NVFP4_OK;
-    const float* a = src.amax[0];                  // the ragged kernels take a direct amax
+    const float* a = src.amax[0];                  // the odd-length ragged kernels take a direct amax
+    if (even_rows(cols, m)) {
+        const EvenRows g = even_rows_of(x, cols, m);
+        const dim3 grid(persistent_grid(g.nhalves, (int64_t)kThreads * kUnroll,
+                                        quant_wg_per_cu(g.nhalves, NVFP4_FQ_MID_WG_PER_CU, NVFP4_FQ_WG_PER_CU)));
+        if (src.partials)
+            k_fake_quant_even<true><<<grid, kThreads, 0, s>>>(g, static_cast<uint32_t*>(y), src);
+        else
+            k_fake_quant_even<false><<<grid, kThreads, 0, s>>>(g, static_cast<uint32_t*>(y), src);
+        return launched();
+    }
     if (m.ragged) {
         const RaggedShape g{cols, m.nbr, m.nblocks};
         k_fake_quant_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
@@ -268,7 +289,18 @@ nvfp4_status enqueue_fake_quant(const void* x, void* y, int64_t cols, const Matr
 nvfp4_status enqueue_quantize_pack(const void* x, int64_t cols, const Matrix& m, uint8_t* packed, uint8_t* scales,
                                    float* global_scale, const AmaxIn& src, hipStream_t s)
 {
-    const float* a = src.amax[0];                  // the ragged kernel takes a direct amax
+    const float* a = src.amax[0];                  // the odd-length ragged kernel takes a direct amax
+    if (even_rows(cols, m)) {
+        const EvenRows g = even_rows_of(x, cols, m);
+        const dim3 grid(persistent_grid(g.nhalves, (int64_t)kThreads * kUnroll,
+                                        quant_wg_per_cu(g.nhalves, NVFP4_QP_MID_WG_PER_CU, NVFP4_QP_WG_PER_CU)));
+        uint32_t* pv = reinterpret_cast<uint32_t*>(packed);
+        if (src.partials)
+            k_quantize_pack_even<true><<<grid, kThreads, 0, s>>>(g, pv, scales, global_scale, src);
+        else
+            k_quantize_pack_even<false><<<grid, kThreads, 0, s>>>(g, pv, scales, global_scale, src);
+        return launched();
+    }
     if (m.ragged) {
         const RaggedShape g{cols, m.nbr, m.nblocks};
         k_quantize_pack_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
@@ -616,7 +648,7 @@ nvfp4_status enqueue_fake_quant_ws(const void* x, void* y, int64_t cols, const M
 {
     if (m.numel == 0)
         return amax_out ? enqueue_reset(amax_out, s) : NVFP4_OK;
-    if (!m.ragged) {
+    if (!m.ragged || even_rows(cols, m)) {
         AmaxIn src;
         if (enqueue_amax_partials(&x, &m.numel, 1, ws, s, &src, ObserverArgs{}, 0,
                                   amax_alloc_bytes(2 * m.numel, NVFP4_FQ_AMAX_ALLOC_MID)) != NVFP4_OK)
@@ -967,6 +999,13 @@ nvfp4_status nvfp4_dequant_unpack(const uint8_t* packed, const uint8_t* scales,
         return NVFP4_ERR_OVERLAP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
+    if (even_rows(cols, m)) {
+        const EvenRows g = even_rows_of(y, cols, m);
+        k_dequant_unpack_even<<<persistent_grid(g.nhalves, (int64_t)kThreads * kDqUnroll, NVFP4_DQ_WG_PER_CU),
+                                kThreads, 0, s>>>(reinterpret_cast<const uint32_t*>(packed), scales, global_scale,
+                                                  static_cast<uint32_t*>(y), g);
+        return launched();
+    }
     if (m.ragged) {
         const RaggedShape g{cols, m.nbr, m.nblocks};
         k_dequant_unpack_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
@@ -1057,7 +1096,7 @@ nvfp4_status nvfp4_quantize_pack_ws(const void* x, int64_t rows, int64_t cols, f
         return NVFP4_ERR_OVERLAP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (!m.ragged) {
+    if (!m.ragged || (m.numel > 0 && even_rows(cols, m))) {
         AmaxIn src;
         if (enqueue_amax_partials(&x, &m.numel, 1, workspace, s, &src, ObserverArgs{}, 0,
                                   amax_alloc_bytes(2 * m.numel, NVFP4_QP_AMAX_ALLOC_MID)) != NVFP4_OK)

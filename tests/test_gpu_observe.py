@@ -64,7 +64,8 @@ def test_c4_ten_steps_two_observers():
 
 
 # chunk edges, ragged rows (their own passes), a single value, wide rows, empty
-SHAPES = [(1, 16), (3, 20), (7, 1), (1025, 16), (64, 4096), (33, 40), (1037, 144), (0, 16), (0, 24)]
+SHAPES = [(1, 16), (3, 20), (7, 1), (1025, 16), (64, 4096), (33, 40), (1037, 144), (0, 16), (0, 24),
+          (65, 4100)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)

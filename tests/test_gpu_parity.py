@@ -178,9 +178,12 @@ def test_c5_row_shards_with_the_all_reduced_amax():
 # ---------------------------------------------------------------- edge tensors
 
 @pytest.mark.parametrize("shape", [(1, 1), (3, 7), (5, 15), (4, 17), (33, 40), (9, 1000), (2, 4097),
-                                   (130, 24), (1000, 33)])
+                                   (130, 24), (1000, 33), (2, 2), (7, 18), (64, 4100), (1025, 30), (17, 1006),
+                                   (300, 62), (513, 8)])
 def test_ragged_columns_zero_padded(shape):
-    """Rows not a multiple of 16: zero-padded blocks, padded code/scale layout, cols outputs."""
+    """Rows not a multiple of 16: zero-padded blocks, padded code/scale layout, cols outputs.
+    Odd lengths go through the one-lane-per-block kernels, even lengths through the
+    half-block kernels (a half may lie wholly in the padding, as for 18 or 8 columns)."""
     rng = np.random.default_rng(shape[0] * 131 + shape[1])
     x = synth.to_bf16_bits((rng.standard_normal(shape) * np.exp(rng.uniform(-3, 3, shape))).astype(np.float32))
     check_all_ops(x, what="ragged cols")
