@@ -94,8 +94,8 @@ namespace {
 #ifndef NVFP4_LIN_LDS_M
 #define NVFP4_LIN_LDS_M 384       // rows of x from which the linear layer decodes weight tiles into LDS
 #endif
-#ifndef NVFP4_LIN_LDS_WAVES
-#define NVFP4_LIN_LDS_WAVES 8     // waves per workgroup of the LDS-staged linear kernel (4 or 8)
+#ifndef NVFP4_LIN_LDS_SMALL_M
+#define NVFP4_LIN_LDS_SMALL_M 160  // rows of x from which the 128 x 128 LDS-staged tile is used
 #endif
 #ifndef NVFP4_LIN_LDS_REMAP
 #define NVFP4_LIN_LDS_REMAP 1     // 1: the LDS-staged linear kernel orders its tiles by XCD

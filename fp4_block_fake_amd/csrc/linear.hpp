@@ -464,55 +464,58 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_linear_tiled(const uint16_t
 //
 // For many rows of x (the layer is compute-bound there), the weight is decoded
 // once per workgroup and K step into LDS as bf16, and both MFMA operands are read
-// from LDS, so each weight element is decoded once per kLdsM rows of x instead of
+// from LDS, so each weight element is decoded once per BM rows of x instead of
 // once per 32-row x tile of a wave.  A workgroup of W waves computes a tile of
-// kLdsM = 256 rows of x by 32 W weight rows; wave w owns x rows 64 (w % 4) .. +64
-// against weight rows 128 (w / 4) .. +128 (2 x 4 tiles of
-// v_mfma_f32_32x32x16_bf16, operand and accumulator layouts as in
-// k_linear_tiled).  Per 64-wide K step, each thread stages 2048 / W 16-byte
+// BM = 32 TM WM rows of x by BN = 32 W weight rows; wave w owns x rows
+// 32 TM (w % WM) .. + 32 TM against weight rows 32 TN (w / WM) .. + 32 TN (TM x TN
+// tiles of v_mfma_f32_32x32x16_bf16, operand and accumulator layouts as in
+// k_linear_tiled).  Per 64-wide K step, each thread stages BM / (8 W) 16-byte
 // pieces of x and decodes the 32 weight codes (16 bytes, two block scales) of
 // one half row into 64 bytes of bf16: the same decode as dequant-unpack, so the
 // weight is bit for bit the tensor dequant-unpack writes.  LDS holds two stages
-// of both tiles (the next stage is written while this one is read); x loads
-// run two steps ahead in registers, code loads four.  The next stage's decode
-// and LDS writes sit between this stage's MFMA slices so that the VALU work
-// overlaps the matrix cores.  With 8 waves a wave needs under 256 VGPRs, so two
-// waves share each SIMD.  Rows of x past M read row M - 1 and weight rows past
-// N read row 0: an output element depends only on its own rows, and those are
-// never stored.
-constexpr int kLdsM = 256;
+// of both tiles (the next stage is written while this one is read); x loads run
+// two steps ahead in registers, code loads four.  The next stage's decode and
+// LDS writes sit between this stage's MFMA slices so that the VALU work overlaps
+// the matrix cores.  Rows of x past M read as zeros and weight rows past N read
+// row 0; neither is stored (an output element depends only on its own rows).
+// Shapes used: 8 waves, 256 x 256 (WM 4, TM 2, TN 4: two waves per SIMD at 238
+// VGPRs), and 4 waves, 128 x 128 (WM 2, TM 2, TN 2) for fewer rows of x, where
+// the large tile would leave CUs idle.
 constexpr int kLdsK = 64;
 constexpr int kLdsStride = kLdsK + 8;          // bf16 per LDS row (padding against bank conflicts)
 constexpr int kLdsXDepth = 2;                  // register stages of x loads in flight
 constexpr int kLdsWDepth = 4;                  // register stages of code loads in flight
 
-template <int W>
-constexpr int lds_n() { return 32 * W; }       // weight rows per workgroup
-template <int W>
-constexpr size_t lds_bytes() { return (size_t)2 * (kLdsM + lds_n<W>()) * kLdsStride * 2; }
+template <int W, int WM, int TM, int TN>
+struct LdsTile {
+    static constexpr int kWN = W / WM;                     // waves along the weight rows
+    static constexpr int kM = 32 * TM * WM;                // rows of x per workgroup
+    static constexpr int kN = 32 * TN * kWN;               // weight rows per workgroup
+    static constexpr int kT = 64 * W;                      // threads
+    static constexpr int kXP = kM * (kLdsK / 8) / kT;      // 16-byte pieces of x per thread and step
+    static constexpr size_t kBytes = (size_t)2 * (kM + kN) * kLdsStride * 2;
+    static_assert(W % WM == 0 && kXP % 4 == 0 && kXP > 0 && 2 * kN == kT, "staging shares");
+};
 
-template <int W>
+template <int W, int WM, int TM, int TN>
 __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                        const uint8_t* __restrict__ packed,
                                                        const uint8_t* __restrict__ scales,
                                                        const float* __restrict__ gs_in, int64_t N,
                                                        const uint16_t* __restrict__ bias, uint16_t* __restrict__ y)
 {
-    static_assert(W == 4 || W == 8, "4 or 8 waves");
-    constexpr int kT = 64 * W;                 // threads
-    constexpr int kN = lds_n<W>();             // weight rows per workgroup
-    constexpr int kXP = kLdsM * (kLdsK / 8) / kT;   // 16-byte pieces of x per thread and step
-    static_assert(kXP % 4 == 0 && 2 * kN == kT, "staging shares");
+    using Tile = LdsTile<W, WM, TM, TN>;
+    constexpr int kM = Tile::kM, kN = Tile::kN, kT = Tile::kT, kXP = Tile::kXP;
     __shared__ float sd_of[128];
-    uint16_t* xs = reinterpret_cast<uint16_t*>(lin_lds);          // [2][kLdsM][kLdsStride]
-    uint16_t* ws = xs + 2 * kLdsM * kLdsStride;                     // [2][kN][kLdsStride]
+    uint16_t* xs = reinterpret_cast<uint16_t*>(lin_lds);          // [2][kM][kLdsStride]
+    uint16_t* ws = xs + 2 * kM * kLdsStride;                        // [2][kN][kLdsStride]
     const float gs = *gs_in;
     if (threadIdx.x < 128)
         sd_of[threadIdx.x] = e4m3_decode(threadIdx.x) / gs;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int c = lane & 31, h = lane >> 5;
-    const int wm = wave % 4, wn = wave / 4;
+    const int wm = wave % WM, wn = wave / WM;
     // XCD-aware order: workgroups go to the 8 XCDs round-robin by id; XCD k takes a
     // contiguous run of weight tiles, x tile by x tile, so the workgroups running on
     // one XCD at a time share their x tile's K slabs in that XCD's L2.
@@ -523,7 +526,7 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
         bx = l / per;
         by = (w % 8) * per + l % per;
     }
-    const int64_t m0 = (int64_t)bx * kLdsM, n0 = (int64_t)by * kN;
+    const int64_t m0 = (int64_t)bx * kM, n0 = (int64_t)by * kN;
 
     // this thread's share of the staging: x rows m0 + tid / 8 + (kT / 8) j (j < kXP)
     // at columns 8 (tid % 8) of the step; weight row n0 + tid / 2, the codes of
@@ -532,6 +535,8 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
 #pragma unroll
     for (int j = 0; j < kXP; ++j) {
         const int64_t m = m0 + tid / 8 + (kT / 8) * j;
+        // rows past M are zero: a conditional load (with unconditional loads from a
+        // clamped row the compiler kept the load ring in scratch memory)
         xrow[j] = m < M ? x + m * K + 8 * (tid % 8) : nullptr;
     }
     const int wr = tid >> 1, wh = tid & 1;
@@ -550,11 +555,12 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
     };
     // piece q (0..3) of the staging of one step into buffer buf: a quarter of the
     // thread's x pieces and one decoded dword of its codes (eight weights)
-    auto stage = [&](int buf, int q, const uint4 (&xv)[kXP], const uint4& cw, uint32_t sc) __attribute__((always_inline)) {
+    auto stage = [&](int buf, int q, const uint4 (&xv)[kXP], const uint4& cw, uint32_t sc)
+        __attribute__((always_inline)) {
 #pragma unroll
         for (int jj = 0; jj < kXP / 4; ++jj) {
             const int j = (kXP / 4) * q + jj;
-            *reinterpret_cast<uint4*>(xs + (buf * kLdsM + tid / 8 + (kT / 8) * j) * kLdsStride + 8 * (tid % 8)) =
+            *reinterpret_cast<uint4*>(xs + (buf * kM + tid / 8 + (kT / 8) * j) * kLdsStride + 8 * (tid % 8)) =
                 xv[j];
         }
         const float sd = sd_of[(sc >> (8 * (q / 2))) & 0x7Fu];
@@ -562,29 +568,29 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
             decode_half(dword_of(cw, q), sd);
     };
 
-    f32x16 acc[2][4];
+    f32x16 acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < TN; ++t)
 #pragma unroll
             for (int j = 0; j < 16; ++j)
                 acc[i][t][j] = 0.0f;
     // slice q (16 of the step's 64 K) of this stage's MFMAs from buffer buf
     auto mma_slice = [&](int buf, int q) __attribute__((always_inline)) {
-        bf16x8 a[2], b[4];
+        bf16x8 a[TM], b[TN];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            a[i] = *reinterpret_cast<const bf16x8*>(xs + (buf * kLdsM + 64 * wm + 32 * i + c) * kLdsStride +
+        for (int i = 0; i < TM; ++i)
+            a[i] = *reinterpret_cast<const bf16x8*>(xs + (buf * kM + 32 * (TM * wm + i) + c) * kLdsStride +
                                                     16 * q + 8 * h);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            b[t] = *reinterpret_cast<const bf16x8*>(ws + (buf * kN + 128 * wn + 32 * t + c) * kLdsStride +
+        for (int t = 0; t < TN; ++t)
+            b[t] = *reinterpret_cast<const bf16x8*>(ws + (buf * kN + 32 * (TN * wn + t) + c) * kLdsStride +
                                                     16 * q + 8 * h);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < TN; ++t)
                 acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[t], acc[i][t], 0, 0, 0);
     };
 
@@ -610,8 +616,7 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
         load_w(kLdsWDepth, cr[0], sr[0]);
     __syncthreads();
     static_assert(kLdsWDepth == 4 && kLdsXDepth == 2, "ring indices repeat every four steps");
-    // step st0 + D of a group of four: the ring slots are compile-time constants, so
-    // the rings stay in registers
+    // step st0 + D of a group of four: the ring slots are compile-time constants
     auto step = [&](int64_t st0, auto dc) __attribute__((always_inline)) {
         constexpr int D = decltype(dc)::value;
         constexpr int cur = D & 1, nxt = cur ^ 1, xn = (D + 1) % kLdsXDepth, wnx = (D + 1) % kLdsWDepth;
@@ -644,16 +649,16 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
     }
 
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int64_t n = n0 + 128 * wn + 32 * t + c;
+        for (int t = 0; t < TN; ++t) {
+            const int64_t n = n0 + 32 * (TN * wn + t) + c;
             if (n >= N)
                 continue;
             const float b = bias ? bf16_value(bias[n]) : 0.0f;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const int64_t m = m0 + 64 * wm + 32 * i + (j % 4) + 8 * (j / 4) + 4 * h;
+                const int64_t m = m0 + 32 * (TM * wm + i) + (j % 4) + 8 * (j / 4) + 4 * h;
                 if (m < M) {
                     const f32x2 o = {acc[i][t][j] + b, 0.0f};
                     y[m * N + n] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(o, bf16x2)) & 0xFFFFu);

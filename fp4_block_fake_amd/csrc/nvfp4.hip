@@ -512,27 +512,30 @@ nvfp4_status enqueue_linear_tiled(const void* x, int64_t m, int64_t k, const uin
     return launched();
 }
 
-// One launch of the LDS-staged linear kernel (K a multiple of 64).  Its LDS is
-// above the 64 KB a kernel gets by default, so the limit is raised once per device.
-std::atomic<int> g_lin_lds_ready[kMaxDevices];
-
+// One launch of the LDS-staged linear kernel (K a multiple of 64) with a tile of
+// LdsTile<W, WM, TM, TN>.  Its LDS can exceed the 64 KB a kernel gets by default,
+// so the limit is raised once per device and shape.
+template <int W, int WM, int TM, int TN>
 nvfp4_status enqueue_linear_lds(const void* x, int64_t m, int64_t k, const uint8_t* packed, const uint8_t* scales,
                                 const float* gs, int64_t n, const void* bias, void* y, hipStream_t s)
 {
+    using Tile = LdsTile<W, WM, TM, TN>;
+    static std::atomic<int> ready[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return NVFP4_ERR_HIP;
-    constexpr int kW = NVFP4_LIN_LDS_WAVES;
-    constexpr size_t kBytes = lds_bytes<kW>();
-    if (!g_lin_lds_ready[dev].load(std::memory_order_acquire)) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_linear_lds<kW>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBytes) != hipSuccess)
+    if (!ready[dev].load(std::memory_order_acquire)) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_linear_lds<W, WM, TM, TN>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)Tile::kBytes) != hipSuccess)
             return NVFP4_ERR_HIP;
-        g_lin_lds_ready[dev].store(1, std::memory_order_release);
+        ready[dev].store(1, std::memory_order_release);
     }
-    const dim3 grid((unsigned)((m + kLdsM - 1) / kLdsM), (unsigned)((n + lds_n<kW>() - 1) / lds_n<kW>()));
-    k_linear_lds<kW><<<grid, 64 * kW, kBytes, s>>>(static_cast<const uint16_t*>(x), m, k, packed, scales, gs, n,
-                                                   static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y));
+    const dim3 grid((unsigned)((m + Tile::kM - 1) / Tile::kM), (unsigned)((n + Tile::kN - 1) / Tile::kN));
+    if (grid.y > 65535)
+        return NVFP4_ERR_SHAPE;
+    k_linear_lds<W, WM, TM, TN><<<grid, 64 * W, Tile::kBytes, s>>>(
+        static_cast<const uint16_t*>(x), m, k, packed, scales, gs, n, static_cast<const uint16_t*>(bias),
+        static_cast<uint16_t*>(y));
     return launched();
 }
 
@@ -1201,8 +1204,10 @@ nvfp4_status nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* pa
         return enqueue_linear_mt<1>(x, m, k, packed, scales, global_scale, n, bias, y, s);
     if (m <= 32)
         return enqueue_linear_mt<2>(x, m, k, packed, scales, global_scale, n, bias, y, s);
-    if (m >= NVFP4_LIN_LDS_M && k % kLdsK == 0 && (n + lds_n<NVFP4_LIN_LDS_WAVES>() - 1) / lds_n<NVFP4_LIN_LDS_WAVES>() <= 65535)
-        return enqueue_linear_lds(x, m, k, packed, scales, global_scale, n, bias, y, s);
+    if (k % kLdsK == 0 && m >= NVFP4_LIN_LDS_M && (n + 255) / 256 <= 65535)
+        return enqueue_linear_lds<8, 4, 2, 4>(x, m, k, packed, scales, global_scale, n, bias, y, s);
+    if (k % kLdsK == 0 && m >= NVFP4_LIN_LDS_SMALL_M && (n + 127) / 128 <= 65535)
+        return enqueue_linear_lds<4, 2, 2, 2>(x, m, k, packed, scales, global_scale, n, bias, y, s);
     constexpr int kNW = NVFP4_TILE_NW;
     if (m < NVFP4_LIN_TILED_M || (n + 32 * kNW * kTileWaves - 1) / (32 * kNW * kTileWaves) > 65535)
         return enqueue_linear_mt<4>(x, m, k, packed, scales, global_scale, n, bias, y, s);
