@@ -566,7 +566,7 @@ class OracleRunner:
 
 def cpu_table(synth):
     """The oracle timed per configuration on the host: each configuration's op sequence
-    (BASELINE's CPU plan), on 1 thread and on all usable host threads (at most 16),
+    (the calls a step of that workload makes), on 1 thread and on all usable host threads (at most 16),
     median of 3 runs for c4 and c5 and of 10 for the others; generation is not timed."""
     import numpy as np
 
@@ -618,10 +618,11 @@ def cpu_table(synth):
         for t in (1, threads):
             r = OracleRunner(t)
             ts = []
-            for _ in range(reps):
+            for k in range(reps):
                 t0 = time.perf_counter()
                 run(r)
                 ts.append(time.perf_counter() - t0)
+                log("cpu table %s, %d thread(s), run %d: %.3f s" % (name, t, k, ts[-1]))
             ts.sort()
             med = ts[len(ts) // 2]
             row["threads_%d" % t] = {"median_s": round(med, 4), "gbs": round(nbytes / med / 1e9, 4),

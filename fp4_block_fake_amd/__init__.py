@@ -43,11 +43,13 @@ class NVFP4Error(RuntimeError):
         self.status = status
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(library_path):
-        raise ImportError("libnvfp4.so is not built (%s); run "
-                          "`python fp4_block_fake_amd/_build.py` or __graft_entry__.build()" % library_path)
-    so = ctypes.CDLL(library_path)
+def _load(path: str = library_path) -> ctypes.CDLL:
+    """The library at `path` with every export's argument types set (the tests also
+    load a build of the same source with other compile-time settings this way)."""
+    if not os.path.exists(path):
+        raise ImportError("%s is not built; run "
+                          "`python fp4_block_fake_amd/_build.py` or __graft_entry__.build()" % path)
+    so = ctypes.CDLL(path)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     so.nvfp4_amax.argtypes = [P, P, I, P, I, P]
     so.nvfp4_fake_quant.argtypes = [P, P, I64, I64, P, P, P]

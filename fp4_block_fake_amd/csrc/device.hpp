@@ -20,6 +20,10 @@ __device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b)
 {
     return w32(__builtin_elementwise_max(h2(a), h2(b)));
 }
+__device__ __forceinline__ uint32_t pk_min(uint32_t a, uint32_t b)
+{
+    return w32(__builtin_elementwise_min(h2(a), h2(b)));
+}
 __device__ __forceinline__ uint32_t pk_sub(uint32_t a, uint32_t b) { return w32(h2(a) - h2(b)); }
 // bit 15 of each half moved to bit 0: for a, b < 0x8000, pk_top(pk_sub(a, b)) = [a < b]
 __device__ __forceinline__ uint32_t pk_top(uint32_t a) { return w32(h2(a) >> (u16x2)15); }
@@ -111,16 +115,32 @@ __device__ __forceinline__ uint32_t first_at_or_above(double t)
     return f < 0x7F80u ? f : 0x7F80u;
 }
 
+// fl(v / sq) without a divide per element, from r = fl(1 / sq) (the correctly
+// rounded reciprocal): q0 = fl(v * r) is within 1.5 ulps of the quotient; the
+// first residual step (the residual v - sq * q0 is exact with a fused
+// multiply-add) brings it within one ulp, and the second gives the correctly
+// rounded quotient (Markstein's theorem for division by a reciprocal and
+// residual corrections).  That holds while the residuals do not underflow and
+// the quotient does not overflow: for 2^-126 <= |quotient| < 2^127.  Smaller
+// quotients all have magnitude index 0 (only their sign matters, which the
+// callers take from t0); callers clamp larger ones first.
+__device__ __forceinline__ float exact_quotient(float v, float sq, float r)
+{
+    const float q0 = v * r;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, sq, v), r, q0);
+    return __builtin_fmaf(__builtin_fmaf(-q1, sq, v), r, q1);
+}
+
 // ---------------------------------------------------------------- per-scale-byte table
 //
 // Everything a block needs beyond its own data depends only on its E4M3 scale
 // byte S (0..0x7E), so each workgroup tabulates it once, for all 128 bytes, in
-// LDS.  Entry for S (8 dwords, 32 bytes):
+// LDS.  Entry for S (4 dwords, 16 bytes):
 //   [0]  r ~ 1 / sq (binary32 bits), the multiplier of the fast path; the sign
 //        bit is set when the fast path is NOT exact under this S
 //   [1]  sd = decode(S) / gs (binary32 bits), the factor of the outputs
-//   [2]  t4 | t4<<16    [3] t6 | t6<<16    [4] (t2-t6) | (t2-t6)<<16
-//   [5]  (t0-1) | (t0-1)<<16    [6] t7 | t5<<16    [7] t3 | t1<<16
+//   [2]  fl(1 / sq) (binary32 bits), the reciprocal of the exact-quotient path
+//   [3]  t7 | (t0 - 1) << 16
 // t_i (i = 1..7) is the smallest magnitude bit pattern whose E2M1 index is >= i;
 // t0 the smallest whose quotient is nonzero.
 //
@@ -130,8 +150,10 @@ __device__ __forceinline__ uint32_t first_at_or_above(double t)
 // code differs only if some bf16 magnitude lands on different sides of a
 // decision boundary.  Both decisions are monotone in |x|, so comparing them at
 // the two bf16 values around each exact threshold t_i settles it for every
-// input; an S that fails (or whose t0 is not 1) keeps the threshold path.
-constexpr int kEntryWords = 8;
+// input.  Under an S that fails (or whose t0 is not 1), codes come from the
+// correctly rounded quotient fl(x / sq) itself (exact_quotient), which is right
+// under every S; a wave with any such block takes that path for all its lanes.
+constexpr int kEntryWords = 4;
 constexpr uint32_t kNotFast = 0x80000000u;
 // How far (in ulps) the table build looks for a multiplier that passes the
 // check when 1 / sq does not.  With 1 / sq rounded, about 1% of (gs, S) pairs
@@ -184,41 +206,8 @@ __device__ void build_entry(uint32_t s, float gs, uint32_t* dst)
     }
     dst[0] = (fast ? r : r0) | (fast ? 0u : kNotFast);
     dst[1] = __float_as_uint(sd);
-    dst[2] = t4 * 0x10001u;
-    dst[3] = t6 * 0x10001u;
-    dst[4] = ((t2 - t6) & 0xFFFFu) * 0x10001u;
-    dst[5] = (t0 - 1u) * 0x10001u;
-    dst[6] = t7 | (t5 << 16);
-    dst[7] = t3 | (t1 << 16);
-}
-
-// Threshold path: idx for the two magnitudes m (15-bit fields) of one dword,
-// a three-step search over the seven sorted thresholds.
-__device__ __forceinline__ uint32_t threshold_index(uint32_t m, const uint32_t* e)
-{
-    const uint32_t n4 = pk_top(pk_sub(m, e[2]));                // [m < t4]
-    const uint32_t ta = pk_mad(n4, e[4], e[3]);                 // n4 ? t2 : t6
-    const uint32_t na = pk_top(pk_sub(m, ta));
-    const uint32_t j = pk_mad(n4, 0x00020002u, na);             // 0..3
-    const uint32_t sel = pk_mad(j, 0x02020202u, 0x01000100u);   // bytes 2j, 2j+1 per half
-    const uint32_t tb = __builtin_amdgcn_perm(e[7], e[6], sel); // t7, t5, t3, t1 by j
-    const uint32_t nb = pk_top(pk_sub(m, tb));
-    return pk_mad(j, 0x00020002u, nb) ^ 0x00070007u;           // 7 - (2j + nb)
-}
-
-// Codes of four bf16 pairs (8 elements) as one dword of nibbles, threshold path.
-__device__ __forceinline__ uint32_t codes_threshold(const uint32_t* w, const uint32_t* e)
-{
-    uint32_t out = 0;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t m = w[p] & 0x7FFF7FFFu;
-        // sign when x < 0 and |x| >= t0 (the quotient does not underflow to zero)
-        const uint32_t neg = w[p] & pk_sub(e[5], m) & 0x80008000u;
-        const uint32_t c = threshold_index(m, e) | (neg >> 12);
-        out |= ((c | (c >> 12)) & 0xFFu) << (8 * p);
-    }
-    return out;
+    dst[2] = r0;
+    dst[3] = t7 | ((t0 - 1u) << 16);
 }
 
 // Codes of one bf16 pair into byte P of `out`, fast path (converter).
@@ -314,17 +303,48 @@ __device__ __forceinline__ uint32_t pair_max(const uint32_t (&w)[4])
     return max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0xB1, 0xF, 0xF, false));
 }
 
+// Codes of one bf16 pair into byte P of `out` from the correctly rounded
+// quotients, under any scale byte: magnitudes are clamped at t7 (every larger
+// one has index 7 too), so the quotient stays below about 5 and finite; the
+// sign is kept only where |x| >= t0, so -0 and negative values whose quotient
+// rounds to zero give code 0 (the method signs a code only when the quotient
+// is below zero).  t7x2 and t0m1x2 hold the thresholds in both halves.
+template <int P>
+__device__ __forceinline__ uint32_t code_pair_exact(uint32_t out, uint32_t w, float sq, float r, uint32_t t7x2,
+                                                    uint32_t t0m1x2)
+{
+    const uint32_t m = w & 0x7FFF7FFFu;
+    const uint32_t v = pk_min(m, t7x2) | (w & pk_sub(t0m1x2, m) & 0x80008000u);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, exact_quotient(__uint_as_float(v << 16), sq, r),
+                                                    exact_quotient(__uint_as_float(v & 0xFFFF0000u), sq, r),
+                                                    1.0f, P);
+}
+
+// Codes of four bf16 pairs as one dword of nibbles, exact-quotient path.
+__device__ __forceinline__ uint32_t codes_exact(const uint32_t* w, const uint32_t* e)
+{
+    const float sd = __uint_as_float(e[1]);
+    const float sq = sd < kEps ? kEps : sd;
+    const float r = __uint_as_float(e[2]);
+    const uint32_t t7x2 = (e[3] & 0xFFFFu) * 0x10001u;
+    const uint32_t t0m1x2 = (e[3] >> 16) * 0x10001u;
+    uint32_t out = 0;
+    out = code_pair_exact<0>(out, w[0], sq, r, t7x2, t0m1x2);
+    out = code_pair_exact<1>(out, w[1], sq, r, t7x2, t0m1x2);
+    out = code_pair_exact<2>(out, w[2], sq, r, t7x2, t0m1x2);
+    out = code_pair_exact<3>(out, w[3], sq, r, t7x2, t0m1x2);
+    return out;
+}
+
 // The eight codes of four bf16 pairs (one dword of nibbles) under table entry e.
+// One path per wave: the fast one when every lane's scale byte passed the check,
+// else the exact quotient for all lanes (right under every scale byte).
 __device__ __forceinline__ uint32_t half_codes(const uint32_t* w, const uint32_t* e)
 {
     const uint32_t head = e[0];
-    if (!(head & kNotFast))
+    if (NVFP4_EXACT_PATH != 2 && __builtin_amdgcn_ballot_w64((head & kNotFast) != 0u) == 0u)
         return codes_fast(w, __uint_as_float(head));
-    uint32_t t[6];
-    const uint4 a = *reinterpret_cast<const uint4*>(e + 2);
-    const uint2 b = *reinterpret_cast<const uint2*>(e + 6);
-    t[0] = a.x; t[1] = a.y; t[2] = a.z; t[3] = a.w; t[4] = b.x; t[5] = b.y;
-    return codes_threshold(w, t - 2);
+    return codes_exact(w, e);
 }
 
 // Eight codes -> eight bf16 outputs (16 bytes).

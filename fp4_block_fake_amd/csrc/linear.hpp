@@ -494,7 +494,7 @@ struct LdsTile {
     static constexpr int kT = 64 * W;                      // threads
     static constexpr int kXP = kM * (kLdsK / 8) / kT;      // 16-byte pieces of x per thread and step
     static constexpr size_t kBytes = (size_t)2 * (kM + kN) * kLdsStride * 2;
-    static_assert(W % WM == 0 && kXP % 4 == 0 && kXP > 0 && 2 * kN == kT, "staging shares");
+    static_assert(W % WM == 0 && (kXP % 4 == 0 || kXP < 4) && kXP > 0 && 2 * kN == kT, "staging shares");
 };
 
 template <int W, int WM, int TM, int TN>
@@ -554,14 +554,17 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
         sc = *reinterpret_cast<const uint16_t*>(srow + st * (kLdsK / 16));
     };
     // piece q (0..3) of the staging of one step into buffer buf: a quarter of the
-    // thread's x pieces and one decoded dword of its codes (eight weights)
+    // thread's x pieces (piece q itself when it has fewer than four) and one
+    // decoded dword of its codes (eight weights)
     auto stage = [&](int buf, int q, const uint4 (&xv)[kXP], const uint4& cw, uint32_t sc)
         __attribute__((always_inline)) {
+        constexpr int kPer = kXP >= 4 ? kXP / 4 : 1;
 #pragma unroll
-        for (int jj = 0; jj < kXP / 4; ++jj) {
-            const int j = (kXP / 4) * q + jj;
-            *reinterpret_cast<uint4*>(xs + (buf * kM + tid / 8 + (kT / 8) * j) * kLdsStride + 8 * (tid % 8)) =
-                xv[j];
+        for (int jj = 0; jj < kPer; ++jj) {
+            const int j = kXP >= 4 ? kPer * q + jj : q;
+            if (j < kXP)
+                *reinterpret_cast<uint4*>(xs + (buf * kM + tid / 8 + (kT / 8) * j) * kLdsStride + 8 * (tid % 8)) =
+                    xv[j];
         }
         const float sd = sd_of[(sc >> (8 * (q / 2))) & 0x7Fu];
         *reinterpret_cast<uint4*>(ws + (buf * kN + wr) * kLdsStride + 32 * wh + 8 * q) =
@@ -616,14 +619,21 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
         load_w(kLdsWDepth, cr[0], sr[0]);
     __syncthreads();
     static_assert(kLdsWDepth == 4 && kLdsXDepth == 2, "ring indices repeat every four steps");
-    // step st0 + D of a group of four: the ring slots are compile-time constants
-    auto step = [&](int64_t st0, auto dc) __attribute__((always_inline)) {
+    // step st0 + D of a group of four: the ring slots are compile-time constants.
+    // Checked (the last, partial group): steps past the end are skipped, and
+    // neither staging nor loads run for steps that do not exist.  Unchecked (a
+    // group of four whole steps): the step is one basic block, so the compiler
+    // can issue a slice's LDS reads under the previous slice's MFMAs; staging
+    // always runs (after the last step it fills a buffer that nothing reads,
+    // whose last reads ended at the previous barrier) and loads clamp their step.
+    auto step = [&](int64_t st0, auto dc, auto checked) __attribute__((always_inline)) {
         constexpr int D = decltype(dc)::value;
+        constexpr bool C = decltype(checked)::value;
         constexpr int cur = D & 1, nxt = cur ^ 1, xn = (D + 1) % kLdsXDepth, wnx = (D + 1) % kLdsWDepth;
         const int64_t st = st0 + D;
-        if (st >= steps)
+        if (C && st >= steps)
             return;
-        const bool more = st + 1 < steps;
+        const bool more = !C || st + 1 < steps;
         // slice q of this stage's MFMAs, then piece q of the next stage's staging
         auto slice = [&](auto qc) __attribute__((always_inline)) {
             constexpr int q = decltype(qc)::value;
@@ -635,17 +645,37 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
         slice(std::integral_constant<int, 1>{});
         slice(std::integral_constant<int, 2>{});
         slice(std::integral_constant<int, 3>{});
-        if (st + 1 + kLdsXDepth < steps)
-            load_x(st + 1 + kLdsXDepth, xr[xn]);
-        if (st + 1 + kLdsWDepth < steps)
-            load_w(st + 1 + kLdsWDepth, cr[wnx], sr[wnx]);
+        if (!C) {
+            const int64_t sx = st + 1 + kLdsXDepth, sw = st + 1 + kLdsWDepth;
+            load_x(sx < steps ? sx : steps - 1, xr[xn]);
+            load_w(sw < steps ? sw : steps - 1, cr[wnx], sr[wnx]);
+        } else {
+            if (st + 1 + kLdsXDepth < steps)
+                load_x(st + 1 + kLdsXDepth, xr[xn]);
+            if (st + 1 + kLdsWDepth < steps)
+                load_w(st + 1 + kLdsWDepth, cr[wnx], sr[wnx]);
+        }
         __syncthreads();
     };
-    for (int64_t st0 = 0; st0 < steps; st0 += kLdsWDepth) {
-        step(st0, std::integral_constant<int, 0>{});
-        step(st0, std::integral_constant<int, 1>{});
-        step(st0, std::integral_constant<int, 2>{});
-        step(st0, std::integral_constant<int, 3>{});
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    constexpr bool kFlat = NVFP4_LIN_LDS_FLAT != 0;
+    int64_t st0 = 0;
+    if (kFlat) {
+        for (; st0 + kLdsWDepth <= steps; st0 += kLdsWDepth) {
+            step(st0, I0{}, std::false_type{});
+            step(st0, I1{}, std::false_type{});
+            step(st0, I2{}, std::false_type{});
+            step(st0, I3{}, std::false_type{});
+        }
+    }
+    for (; st0 < steps; st0 += kLdsWDepth) {
+        step(st0, I0{}, std::true_type{});
+        step(st0, I1{}, std::true_type{});
+        step(st0, I2{}, std::true_type{});
+        step(st0, I3{}, std::true_type{});
     }
 
 #pragma unroll

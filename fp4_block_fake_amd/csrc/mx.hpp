@@ -61,20 +61,13 @@ __device__ __forceinline__ MxDivisor mx_divisor(float s)
     return d;
 }
 
-// fl(v / sq) without a divide per element: q0 = fl(v * r) is within 1.5 ulps of
-// the quotient; the first residual step (the residual v - sq * q0 is exact with
-// a fused multiply-add) brings it within one ulp, and with r the correctly
-// rounded reciprocal the second step gives the correctly rounded quotient
-// (Markstein's theorem for division by a reciprocal and residual corrections).
-// That holds while the residuals do not underflow: for |quotient| >= 2^-126,
-// which covers every quotient at or above a decision boundary (0.25 .. 5).
-// Smaller quotients all have magnitude index 0 and only their sign matters,
-// which mx_code_pair takes from t0 instead.
+// fl(v / sq) by the reciprocal and two residual corrections (exact_quotient).
+// |v| <= the block max, so the quotient is at most about 6 and never overflows;
+// quotients below 2^-126 have magnitude index 0, and mx_code_pair takes their
+// sign from t0.
 __device__ __forceinline__ float mx_quotient(float v, const MxDivisor& d)
 {
-    const float q0 = v * d.r;
-    const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, d.sq, v), d.r, q0);
-    return __builtin_fmaf(__builtin_fmaf(-q1, d.sq, v), d.r, q1);
+    return exact_quotient(v, d.sq, d.r);
 }
 
 // Codes of one bf16 pair into byte P of `out` through the FP4 converter (round to

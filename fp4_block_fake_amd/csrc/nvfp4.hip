@@ -312,10 +312,15 @@ nvfp4_status enqueue_quantize_pack(const void* x, int64_t cols, const Matrix& m,
                                     quant_wg_per_cu(nh, NVFP4_QP_MID_WG_PER_CU, NVFP4_QP_WG_PER_CU)));
     const uint4* xv = static_cast<const uint4*>(x);
     uint32_t* pv = reinterpret_cast<uint32_t*>(packed);
-    if (src.partials)
-        k_quantize_pack<true><<<grid, kThreads, 0, s>>>(xv, pv, scales, global_scale, nh, src);
+    const bool nt = (nh * 16 < NVFP4_MID_BYTES ? NVFP4_QP_NT_ST : NVFP4_QP_LARGE_NT_ST) != 0;
+    if (src.partials && nt)
+        k_quantize_pack<true, true><<<grid, kThreads, 0, s>>>(xv, pv, scales, global_scale, nh, src);
+    else if (src.partials)
+        k_quantize_pack<true, false><<<grid, kThreads, 0, s>>>(xv, pv, scales, global_scale, nh, src);
+    else if (nt)
+        k_quantize_pack<false, true><<<grid, kThreads, 0, s>>>(xv, pv, scales, global_scale, nh, src);
     else
-        k_quantize_pack<false><<<grid, kThreads, 0, s>>>(xv, pv, scales, global_scale, nh, src);
+        k_quantize_pack<false, false><<<grid, kThreads, 0, s>>>(xv, pv, scales, global_scale, nh, src);
     return launched();
 }
 
@@ -1208,6 +1213,8 @@ nvfp4_status nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* pa
         return enqueue_linear_lds<8, 4, 2, 4>(x, m, k, packed, scales, global_scale, n, bias, y, s);
     if (k % kLdsK == 0 && m >= NVFP4_LIN_LDS_SMALL_M && (n + 127) / 128 <= 65535)
         return enqueue_linear_lds<4, 2, 2, 2>(x, m, k, packed, scales, global_scale, n, bias, y, s);
+    if (k % kLdsK == 0 && m >= NVFP4_LIN_LDS_TINY_M && (n + 127) / 128 <= 65535)
+        return enqueue_linear_lds<4, 1, 2, 1>(x, m, k, packed, scales, global_scale, n, bias, y, s);
     constexpr int kNW = NVFP4_TILE_NW;
     if (m < NVFP4_LIN_TILED_M || (n + 32 * kNW * kTileWaves - 1) / (32 * kNW * kTileWaves) > 65535)
         return enqueue_linear_mt<4>(x, m, k, packed, scales, global_scale, n, bias, y, s);

@@ -54,7 +54,8 @@ def check_bound(y_dev_bits, x, packed, scales, gs, k, bias, what):
     return float((err / np.maximum(tol, 1e-300)).max())
 
 
-@pytest.mark.parametrize("n,k", [(40, 256), (100, 96), (16, 32), (33, 160), (300, 512), (130, 192), (200, 384)])
+@pytest.mark.parametrize("n,k", [(40, 256), (100, 96), (16, 32), (33, 160), (300, 512), (130, 192), (200, 384),
+                                 (70, 128), (260, 320)])
 def test_one_hot_rows_give_the_weight_exactly(n, k):
     packed, scales, gs = weight(n, k, n + k)
     eye = np.where(np.eye(k, dtype=bool), np.uint16(0x3F80), np.uint16(0))
