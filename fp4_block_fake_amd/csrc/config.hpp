@@ -95,10 +95,13 @@ namespace {
 #define NVFP4_LIN_LDS_M 384       // rows of x from which the linear layer decodes weight tiles into LDS
 #endif
 #ifndef NVFP4_LIN_LDS_SMALL_M
-#define NVFP4_LIN_LDS_SMALL_M 160  // rows of x from which the 128 x 128 LDS-staged tile is used
+#define NVFP4_LIN_LDS_SMALL_M 129  // rows of x from which the 128 x 128 LDS-staged tile is used
 #endif
 #ifndef NVFP4_LIN_LDS_TINY_M
 #define NVFP4_LIN_LDS_TINY_M 65   // rows of x from which the 64 x 128 LDS-staged tile is used
+#endif
+#ifndef NVFP4_LIN_LDS_TINY_WDEPTH
+#define NVFP4_LIN_LDS_TINY_WDEPTH 4  // K steps of code loads in flight in the 64 x 128 tile (4 or 8)
 #endif
 #ifndef NVFP4_LIN_LDS_FLAT
 #define NVFP4_LIN_LDS_FLAT 1      // 1: whole groups of four K steps run without per-step branches
@@ -151,14 +154,6 @@ namespace {
 #endif
 #ifndef NVFP4_QP_NT_ST
 #define NVFP4_QP_NT_ST 1
-#endif
-// Code stores of quantize-pack from NVFP4_MID_BYTES of input: allocating (0) keeps
-// the codes in the Infinity Cache for an unpack that follows, and measured faster
-// on the 470 MB tensor (pack 97.5 -> 93.0 us, the bench step 466 -> 455 us cold);
-// below that size non-temporal stores (NVFP4_QP_NT_ST) measured faster (c4 weight
-// workspace pack 54.6 -> 46.1 us cold).
-#ifndef NVFP4_QP_LARGE_NT_ST
-#define NVFP4_QP_LARGE_NT_ST 0
 #endif
 #ifndef NVFP4_DQ_NT_ST
 #define NVFP4_DQ_NT_ST 1

@@ -413,9 +413,8 @@ __global__ __launch_bounds__(kThreads) void k_fake_quant_group(FqGroup g, AmaxIn
 }
 
 // Quantize-pack: lane j stores the eight codes of half j (one dword of the
-// packed codes); the even lane of a block also stores its scale byte.  NtSt:
-// non-temporal code stores.
-template <bool Partials, bool NtSt>
+// packed codes); the even lane of a block also stores its scale byte.
+template <bool Partials>
 __global__ __launch_bounds__(kThreads) void k_quantize_pack(const uint4* __restrict__ x,
                                                             uint32_t* __restrict__ packed,
                                                             uint8_t* __restrict__ scales,
@@ -437,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack(const uint4* __restr
         build_table(gs, tab);
     }, [&](const uint32_t (&w)[4], int64_t j) {
         const uint32_t sb = scale_byte_of(pair_max(w), gs);
-        store4<NtSt>(packed + j, half_codes(w, tab + sb * kEntryWords));
+        store4<NVFP4_QP_NT_ST != 0>(packed + j, half_codes(w, tab + sb * kEntryWords));
         if (!(j & 1))
             scales[j >> 1] = (uint8_t)sb;
     });

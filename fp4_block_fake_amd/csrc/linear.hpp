@@ -5,6 +5,7 @@
 #define NVFP4_LINEAR_HPP
 
 #include <type_traits>
+#include <utility>
 
 #include "device.hpp"
 
@@ -484,7 +485,13 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_linear_tiled(const uint16_t
 constexpr int kLdsK = 64;
 constexpr int kLdsStride = kLdsK + 8;          // bf16 per LDS row (padding against bank conflicts)
 constexpr int kLdsXDepth = 2;                  // register stages of x loads in flight
-constexpr int kLdsWDepth = 4;                  // register stages of code loads in flight
+
+// f(integral_constant<int, I>) for I = 0 .. sizeof...(I) - 1, in order.
+template <typename F, std::size_t... I>
+__device__ __forceinline__ void for_each_index(F&& f, std::index_sequence<I...>)
+{
+    (f(std::integral_constant<int, (int)I>{}), ...);
+}
 
 template <int W, int WM, int TM, int TN>
 struct LdsTile {
@@ -497,7 +504,8 @@ struct LdsTile {
     static_assert(W % WM == 0 && (kXP % 4 == 0 || kXP < 4) && kXP > 0 && 2 * kN == kT, "staging shares");
 };
 
-template <int W, int WM, int TM, int TN>
+// WD: register stages of code loads in flight (4 or 8); K steps run in groups of WD.
+template <int W, int WM, int TM, int TN, int WD>
 __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                        const uint8_t* __restrict__ packed,
                                                        const uint8_t* __restrict__ scales,
@@ -598,6 +606,7 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
     };
 
     const int64_t steps = K / kLdsK;
+    constexpr int kLdsWDepth = WD;
     uint4 xr[kLdsXDepth][kXP];
     uint4 cr[kLdsWDepth];
     uint32_t sr[kLdsWDepth];
@@ -618,11 +627,11 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
     if (kLdsWDepth < steps)
         load_w(kLdsWDepth, cr[0], sr[0]);
     __syncthreads();
-    static_assert(kLdsWDepth == 4 && kLdsXDepth == 2, "ring indices repeat every four steps");
-    // step st0 + D of a group of four: the ring slots are compile-time constants.
+    static_assert((WD == 4 || WD == 8) && kLdsXDepth == 2, "ring indices repeat every WD steps");
+    // step st0 + D of a group of WD: the ring slots are compile-time constants.
     // Checked (the last, partial group): steps past the end are skipped, and
     // neither staging nor loads run for steps that do not exist.  Unchecked (a
-    // group of four whole steps): the step is one basic block, so the compiler
+    // group of WD whole steps): the step is one basic block, so the compiler
     // can issue a slice's LDS reads under the previous slice's MFMAs; staging
     // always runs (after the last step it fills a buffer that nothing reads,
     // whose last reads ended at the previous barrier) and loads clamp their step.
@@ -657,26 +666,16 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
         }
         __syncthreads();
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
     constexpr bool kFlat = NVFP4_LIN_LDS_FLAT != 0;
     int64_t st0 = 0;
     if (kFlat) {
-        for (; st0 + kLdsWDepth <= steps; st0 += kLdsWDepth) {
-            step(st0, I0{}, std::false_type{});
-            step(st0, I1{}, std::false_type{});
-            step(st0, I2{}, std::false_type{});
-            step(st0, I3{}, std::false_type{});
-        }
+        for (; st0 + kLdsWDepth <= steps; st0 += kLdsWDepth)
+            for_each_index([&](auto dc) __attribute__((always_inline)) { step(st0, dc, std::false_type{}); },
+                           std::make_index_sequence<WD>{});
     }
-    for (; st0 < steps; st0 += kLdsWDepth) {
-        step(st0, I0{}, std::true_type{});
-        step(st0, I1{}, std::true_type{});
-        step(st0, I2{}, std::true_type{});
-        step(st0, I3{}, std::true_type{});
-    }
+    for (; st0 < steps; st0 += kLdsWDepth)
+        for_each_index([&](auto dc) __attribute__((always_inline)) { step(st0, dc, std::true_type{}); },
+                       std::make_index_sequence<WD>{});
 
 #pragma unroll
     for (int i = 0; i < TM; ++i) {

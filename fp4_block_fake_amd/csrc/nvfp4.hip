@@ -312,15 +312,10 @@ nvfp4_status enqueue_quantize_pack(const void* x, int64_t cols, const Matrix& m,
                                     quant_wg_per_cu(nh, NVFP4_QP_MID_WG_PER_CU, NVFP4_QP_WG_PER_CU)));
     const uint4* xv = static_cast<const uint4*>(x);
     uint32_t* pv = reinterpret_cast<uint32_t*>(packed);
-    const bool nt = (nh * 16 < NVFP4_MID_BYTES ? NVFP4_QP_NT_ST : NVFP4_QP_LARGE_NT_ST) != 0;
-    if (src.partials && nt)
-        k_quantize_pack<true, true><<<grid, kThreads, 0, s>>>(xv, pv, scales, global_scale, nh, src);
-    else if (src.partials)
-        k_quantize_pack<true, false><<<grid, kThreads, 0, s>>>(xv, pv, scales, global_scale, nh, src);
-    else if (nt)
-        k_quantize_pack<false, true><<<grid, kThreads, 0, s>>>(xv, pv, scales, global_scale, nh, src);
+    if (src.partials)
+        k_quantize_pack<true><<<grid, kThreads, 0, s>>>(xv, pv, scales, global_scale, nh, src);
     else
-        k_quantize_pack<false, false><<<grid, kThreads, 0, s>>>(xv, pv, scales, global_scale, nh, src);
+        k_quantize_pack<false><<<grid, kThreads, 0, s>>>(xv, pv, scales, global_scale, nh, src);
     return launched();
 }
 
@@ -525,12 +520,13 @@ nvfp4_status enqueue_linear_lds(const void* x, int64_t m, int64_t k, const uint8
                                 const float* gs, int64_t n, const void* bias, void* y, hipStream_t s)
 {
     using Tile = LdsTile<W, WM, TM, TN>;
+    constexpr int WD = (W == 4 && WM == 1) ? NVFP4_LIN_LDS_TINY_WDEPTH : 4;
     static std::atomic<int> ready[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return NVFP4_ERR_HIP;
     if (!ready[dev].load(std::memory_order_acquire)) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_linear_lds<W, WM, TM, TN>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_linear_lds<W, WM, TM, TN, WD>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)Tile::kBytes) != hipSuccess)
             return NVFP4_ERR_HIP;
         ready[dev].store(1, std::memory_order_release);
@@ -538,7 +534,7 @@ nvfp4_status enqueue_linear_lds(const void* x, int64_t m, int64_t k, const uint8
     const dim3 grid((unsigned)((m + Tile::kM - 1) / Tile::kM), (unsigned)((n + Tile::kN - 1) / Tile::kN));
     if (grid.y > 65535)
         return NVFP4_ERR_SHAPE;
-    k_linear_lds<W, WM, TM, TN><<<grid, 64 * W, Tile::kBytes, s>>>(
+    k_linear_lds<W, WM, TM, TN, WD><<<grid, 64 * W, Tile::kBytes, s>>>(
         static_cast<const uint16_t*>(x), m, k, packed, scales, gs, n, static_cast<const uint16_t*>(bias),
         static_cast<uint16_t*>(y));
     return launched();

@@ -94,12 +94,14 @@ def test_linear_within_the_rounding_bound(m, n, k, with_bias):
 # Launch shapes the tile choice reaches: 256-wide steps whose scale bytes are not 4-byte
 # aligned (k % 64 == 32, up to 16 rows of x), one workgroup per CU for widths n = 4096 c
 # (c tiles of 16 weight rows per workgroup, c = 1, 3, 5, 8), several 16-row tiles of x,
-# the tiled kernel from 65 rows of x (64- and 128-row tiles, 32- and 64-wide K steps,
-# ragged rows of x, many x tiles, and a width that is not a multiple of the 128-row weight
-# tile), and from 160 rows of x with K a multiple of 64 the kernel that decodes weight
-# tiles into LDS, with 128 x 128 tiles below 384 rows and 256 x 256 tiles from there (one
-# to three K steps against its four-deep load ring, ragged rows of x and of the weight,
-# several x tiles, grids with the XCD-ordered tiles).
+# the tiled kernel from 65 rows of x where K is not a multiple of 64 (64- and 128-row
+# tiles, 32- and 64-wide K steps, ragged rows of x, many x tiles, and a width that is not
+# a multiple of the 128-row weight tile), and from 65 rows of x with K a multiple of 64
+# the kernel that decodes weight tiles into LDS, with 64 x 128 tiles up to 128 rows,
+# 128 x 128 tiles below 384 rows and 256 x 256 tiles from there (one to three K steps
+# against its four-deep load ring, whole groups of four steps with and without a partial
+# last group, ragged rows of x and of the weight, several x tiles, grids with the
+# XCD-ordered tiles).
 @pytest.mark.parametrize("m,n,k", [(5, 40, 288), (16, 130, 800), (4, 12288, 256), (2, 20480, 128),
                                    (64, 32768, 64), (33, 4096, 96), (48, 8192, 160),
                                    (129, 256, 1024), (300, 200, 2048), (1024, 520, 256), (128, 4096, 4096),
@@ -107,7 +109,8 @@ def test_linear_within_the_rounding_bound(m, n, k, with_bias):
                                    (200, 300, 64), (257, 129, 128), (300, 1000, 192), (512, 4096, 320),
                                    (1030, 2056, 576), (2048, 256, 256), (400, 300, 64), (512, 129, 128),
                                    (384, 520, 192), (769, 8192, 1024), (160, 1024, 64), (383, 4096, 256),
-                                   (250, 130, 128)])
+                                   (250, 130, 128), (100, 200, 224), (80, 4096, 96), (65, 300, 1088),
+                                   (96, 2056, 512)])
 def test_linear_launch_shapes(m, n, k):
     packed, scales, gs = weight(n, k, 11 * m + n + k)
     rng = np.random.default_rng(m * 5 + n + k)
