@@ -95,13 +95,7 @@ namespace {
 #define NVFP4_LIN_LDS_M 384       // rows of x from which the linear layer decodes weight tiles into LDS
 #endif
 #ifndef NVFP4_LIN_LDS_SMALL_M
-#define NVFP4_LIN_LDS_SMALL_M 129  // rows of x from which the 128 x 128 LDS-staged tile is used
-#endif
-#ifndef NVFP4_LIN_LDS_TINY_M
-#define NVFP4_LIN_LDS_TINY_M 65   // rows of x from which the 64 x 128 LDS-staged tile is used
-#endif
-#ifndef NVFP4_LIN_LDS_TINY_WDEPTH
-#define NVFP4_LIN_LDS_TINY_WDEPTH 4  // K steps of code loads in flight in the 64 x 128 tile (4 or 8)
+#define NVFP4_LIN_LDS_SMALL_M 65   // rows of x from which the 128 x 128 LDS-staged tile is used
 #endif
 #ifndef NVFP4_LIN_LDS_FLAT
 #define NVFP4_LIN_LDS_FLAT 1      // 1: whole groups of four K steps run without per-step branches

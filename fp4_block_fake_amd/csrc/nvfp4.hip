@@ -520,7 +520,7 @@ nvfp4_status enqueue_linear_lds(const void* x, int64_t m, int64_t k, const uint8
                                 const float* gs, int64_t n, const void* bias, void* y, hipStream_t s)
 {
     using Tile = LdsTile<W, WM, TM, TN>;
-    constexpr int WD = (W == 4 && WM == 1) ? NVFP4_LIN_LDS_TINY_WDEPTH : 4;
+    constexpr int WD = 4;
     static std::atomic<int> ready[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
@@ -1209,8 +1209,6 @@ nvfp4_status nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* pa
         return enqueue_linear_lds<8, 4, 2, 4>(x, m, k, packed, scales, global_scale, n, bias, y, s);
     if (k % kLdsK == 0 && m >= NVFP4_LIN_LDS_SMALL_M && (n + 127) / 128 <= 65535)
         return enqueue_linear_lds<4, 2, 2, 2>(x, m, k, packed, scales, global_scale, n, bias, y, s);
-    if (k % kLdsK == 0 && m >= NVFP4_LIN_LDS_TINY_M && (n + 127) / 128 <= 65535)
-        return enqueue_linear_lds<4, 1, 2, 1>(x, m, k, packed, scales, global_scale, n, bias, y, s);
     constexpr int kNW = NVFP4_TILE_NW;
     if (m < NVFP4_LIN_TILED_M || (n + 32 * kNW * kTileWaves - 1) / (32 * kNW * kTileWaves) > 65535)
         return enqueue_linear_mt<4>(x, m, k, packed, scales, global_scale, n, bias, y, s);

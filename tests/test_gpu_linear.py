@@ -97,8 +97,8 @@ def test_linear_within_the_rounding_bound(m, n, k, with_bias):
 # the tiled kernel from 65 rows of x where K is not a multiple of 64 (64- and 128-row
 # tiles, 32- and 64-wide K steps, ragged rows of x, many x tiles, and a width that is not
 # a multiple of the 128-row weight tile), and from 65 rows of x with K a multiple of 64
-# the kernel that decodes weight tiles into LDS, with 64 x 128 tiles up to 128 rows,
-# 128 x 128 tiles below 384 rows and 256 x 256 tiles from there (one to three K steps
+# the kernel that decodes weight tiles into LDS, with 128 x 128 tiles below 384 rows and
+# 256 x 256 tiles from there (one to three K steps
 # against its four-deep load ring, whole groups of four steps with and without a partial
 # last group, ragged rows of x and of the weight, several x tiles, grids with the
 # XCD-ordered tiles).
