@@ -97,6 +97,9 @@ namespace {
 #ifndef NVFP4_LIN_LDS_SMALL_M
 #define NVFP4_LIN_LDS_SMALL_M 65   // rows of x from which the 128 x 128 LDS-staged tile is used
 #endif
+#ifndef NVFP4_LIN_LDS_PIPE
+#define NVFP4_LIN_LDS_PIPE 1      // 1: the 4-wave LDS tile reads slice q + 1's operands before slice q's MFMAs
+#endif
 #ifndef NVFP4_LIN_LDS_FLAT
 #define NVFP4_LIN_LDS_FLAT 1      // 1: whole groups of four K steps run without per-step branches
 #endif

@@ -501,7 +501,7 @@ struct LdsTile {
     static constexpr int kT = 64 * W;                      // threads
     static constexpr int kXP = kM * (kLdsK / 8) / kT;      // 16-byte pieces of x per thread and step
     static constexpr size_t kBytes = (size_t)2 * (kM + kN) * kLdsStride * 2;
-    static_assert(W % WM == 0 && (kXP % 4 == 0 || kXP < 4) && kXP > 0 && 2 * kN == kT, "staging shares");
+    static_assert(W % WM == 0 && kXP % 4 == 0 && kXP > 0 && 2 * kN == kT, "staging shares");
 };
 
 // WD: register stages of code loads in flight (4 or 8); K steps run in groups of WD.
@@ -562,17 +562,14 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
         sc = *reinterpret_cast<const uint16_t*>(srow + st * (kLdsK / 16));
     };
     // piece q (0..3) of the staging of one step into buffer buf: a quarter of the
-    // thread's x pieces (piece q itself when it has fewer than four) and one
-    // decoded dword of its codes (eight weights)
+    // thread's x pieces and one decoded dword of its codes (eight weights)
     auto stage = [&](int buf, int q, const uint4 (&xv)[kXP], const uint4& cw, uint32_t sc)
         __attribute__((always_inline)) {
-        constexpr int kPer = kXP >= 4 ? kXP / 4 : 1;
 #pragma unroll
-        for (int jj = 0; jj < kPer; ++jj) {
-            const int j = kXP >= 4 ? kPer * q + jj : q;
-            if (j < kXP)
-                *reinterpret_cast<uint4*>(xs + (buf * kM + tid / 8 + (kT / 8) * j) * kLdsStride + 8 * (tid % 8)) =
-                    xv[j];
+        for (int jj = 0; jj < kXP / 4; ++jj) {
+            const int j = (kXP / 4) * q + jj;
+            *reinterpret_cast<uint4*>(xs + (buf * kM + tid / 8 + (kT / 8) * j) * kLdsStride + 8 * (tid % 8)) =
+                xv[j];
         }
         const float sd = sd_of[(sc >> (8 * (q / 2))) & 0x7Fu];
         *reinterpret_cast<uint4*>(ws + (buf * kN + wr) * kLdsStride + 32 * wh + 8 * q) =
@@ -588,8 +585,8 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
             for (int j = 0; j < 16; ++j)
                 acc[i][t][j] = 0.0f;
     // slice q (16 of the step's 64 K) of this stage's MFMAs from buffer buf
-    auto mma_slice = [&](int buf, int q) __attribute__((always_inline)) {
-        bf16x8 a[TM], b[TN];
+    // the MFMA operands of slice q (16 of the step's 64 K) from buffer buf
+    auto read_slice = [&](int buf, int q, bf16x8 (&a)[TM], bf16x8 (&b)[TN]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
             a[i] = *reinterpret_cast<const bf16x8*>(xs + (buf * kM + 32 * (TM * wm + i) + c) * kLdsStride +
@@ -598,12 +595,24 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
         for (int t = 0; t < TN; ++t)
             b[t] = *reinterpret_cast<const bf16x8*>(ws + (buf * kN + 32 * (TN * wn + t) + c) * kLdsStride +
                                                     16 * q + 8 * h);
+    };
+    auto mma = [&](const bf16x8 (&a)[TM], const bf16x8 (&b)[TN]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int t = 0; t < TN; ++t)
                 acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[t], acc[i][t], 0, 0, 0);
     };
+    auto mma_slice = [&](int buf, int q) __attribute__((always_inline)) {
+        bf16x8 a[TM], b[TN];
+        read_slice(buf, q, a, b);
+        mma(a, b);
+    };
+    // Pipelined operands (the 4-wave tile, which has the registers for it): slice
+    // q + 1's operands are read into the other of two register sets before slice
+    // q's MFMAs issue, so those MFMAs wait on no LDS read.
+    constexpr bool Pipe = NVFP4_LIN_LDS_PIPE != 0 && W == 4;
+    bf16x8 fa[2][TM], fb[2][TN];
 
     const int64_t steps = K / kLdsK;
     constexpr int kLdsWDepth = WD;
@@ -646,7 +655,15 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
         // slice q of this stage's MFMAs, then piece q of the next stage's staging
         auto slice = [&](auto qc) __attribute__((always_inline)) {
             constexpr int q = decltype(qc)::value;
-            mma_slice(cur, q);
+            if (Pipe) {
+                if (q == 0)
+                    read_slice(cur, 0, fa[0], fb[0]);
+                if (q < 3)
+                    read_slice(cur, q + 1, fa[(q + 1) & 1], fb[(q + 1) & 1]);
+                mma(fa[q & 1], fb[q & 1]);
+            } else {
+                mma_slice(cur, q);
+            }
             if (more)
                 stage(nxt, q, xr[xn], cr[wnx], sr[wnx]);
         };
