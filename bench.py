@@ -273,23 +273,27 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
 
     if group("ragged_"):
         # rows whose length is not a multiple of 16 (zero-padded last block of each row):
-        # the ragged-row kernels, one lane per block with element-wise accesses
-        xr = to_dev(synth.normal_bf16(9, (4096, 4100), 0.02))
-        nr = xr.numel()
-        yr = torch.empty_like(xr)
-        nbr = (xr.shape[1] + 15) // 16
-        pr = torch.empty((xr.shape[0], 8 * nbr), dtype=torch.uint8, device=dev)
-        sr = torch.empty((xr.shape[0], nbr), dtype=torch.uint8, device=dev)
-        gr = torch.empty(1, dtype=torch.float32, device=dev)
-        ar = torch.empty(1, dtype=torch.float32, device=dev)
-        line("ragged_4096x4100_fused_amax_fake_quant_ws",
-             lambda: nv.nvfp4_fake_quant_ws(xr, y=yr, amax_out=ar, workspace=ws), 6.0 * nr, cold=True, elems=nr)
-        line("ragged_4096x4100_fused_amax_quantize_pack_ws",
-             lambda: nv.nvfp4_quantize_pack_ws(xr, amax_out=ar, packed=pr, scales=sr, global_scale=gr,
-                                               workspace=ws), 4.5625 * nr, cold=True, elems=nr)
-        line("ragged_4096x4100_dequant_unpack", lambda: nv.nvfp4_dequant_unpack(pr, sr, gr, y=yr, cols=4100),
-             2.5625 * nr, cold=True, elems=nr)
-        del xr, yr, pr, sr
+        # even lengths take the half-block kernels with dword accesses, odd lengths the
+        # one-lane-per-block kernels with element-wise accesses
+        for cols in (4100, 4097):
+            xr = to_dev(synth.normal_bf16(9, (4096, cols), 0.02))
+            nr = xr.numel()
+            yr = torch.empty_like(xr)
+            nbr = (cols + 15) // 16
+            pr = torch.empty((xr.shape[0], 8 * nbr), dtype=torch.uint8, device=dev)
+            sr = torch.empty((xr.shape[0], nbr), dtype=torch.uint8, device=dev)
+            gr = torch.empty(1, dtype=torch.float32, device=dev)
+            ar = torch.empty(1, dtype=torch.float32, device=dev)
+            tag = "ragged_4096x%d" % cols
+            line(tag + "_fused_amax_fake_quant_ws",
+                 lambda: nv.nvfp4_fake_quant_ws(xr, y=yr, amax_out=ar, workspace=ws), 6.0 * nr, cold=True,
+                 elems=nr)
+            line(tag + "_fused_amax_quantize_pack_ws",
+                 lambda: nv.nvfp4_quantize_pack_ws(xr, amax_out=ar, packed=pr, scales=sr, global_scale=gr,
+                                                   workspace=ws), 4.5625 * nr, cold=True, elems=nr)
+            line(tag + "_dequant_unpack", lambda: nv.nvfp4_dequant_unpack(pr, sr, gr, y=yr, cols=cols),
+                 2.5625 * nr, cold=True, elems=nr)
+            del xr, yr, pr, sr
 
     if group("c3_"):
         # c3: shared amax of fused QKV siblings in one launch, then a fake-quant of each
