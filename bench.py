@@ -273,8 +273,8 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
 
     if group("ragged_"):
         # rows whose length is not a multiple of 16 (zero-padded last block of each row):
-        # even lengths take the half-block kernels with dword accesses, odd lengths the
-        # one-lane-per-block kernels with element-wise accesses
+        # the half-block kernels, with dword accesses for even lengths and element-wise
+        # ones for odd lengths
         for cols in (4100, 4097):
             xr = to_dev(synth.normal_bf16(9, (4096, cols), 0.02))
             nr = xr.numel()

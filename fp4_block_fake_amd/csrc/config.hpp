@@ -155,6 +155,12 @@ namespace {
 #ifndef NVFP4_DQ_NT_ST
 #define NVFP4_DQ_NT_ST 1
 #endif
+// Ragged rows of fewer blocks than this take the half-block kernels (their half
+// index is 32-bit), larger ones the one-lane-per-block kernels.  A test build sets
+// 0 to run every ragged shape through the latter.
+#ifndef NVFP4_HALF_ROWS_MAX_BLOCKS
+#define NVFP4_HALF_ROWS_MAX_BLOCKS (1LL << 31)
+#endif
 // 2 builds a test library in which every wave computes its codes from the
 // correctly rounded quotient (the path that waves holding a block with an
 // uncertified scale byte take), under every scale byte.

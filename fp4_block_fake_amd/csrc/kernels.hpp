@@ -609,51 +609,86 @@ __global__ __launch_bounds__(kThreads) void k_dequant_unpack_ragged(const uint2*
     }
 }
 
-// ---------------------------------------------------------------- ragged rows of even length
+// ---------------------------------------------------------------- ragged rows
 //
-// Rows whose length is even but not a multiple of 16 (the usual ragged case) keep
-// the half-block lanes of the whole-block kernels, over the zero-padded rows:
-// padded half j is half hr = j - r hpr of row r = j / hpr (hpr = 2 ceil(cols / 16)
-// halves per padded row), elements 8 hr .. 8 hr + 7 of the row, of which the first
-// n = min(8, cols - 8 hr) exist (n is even, as cols is; the rest are padding zeros).
-// A half starts on an even element, so it is four dwords, each loaded and stored
-// whole when it lies in the row.  Codes and scales keep the padded layout (dword j
-// of the codes, scale byte j / 2), exactly as for whole-block rows.  The bf16 side
-// uses ordinary (allocating) loads and stores: a lane's four dword accesses at a
-// 16-byte lane stride each touch every line of the wave's span, and it is the L2
-// that merges them into whole lines.
-struct EvenRows {
-    const uint32_t* x;      // the tensor as dwords (pairs of bf16), 4-byte aligned
-    int64_t cols;           // elements per row, even
+// Rows whose length is not a multiple of 16 keep the half-block lanes of the
+// whole-block kernels, over the zero-padded rows: padded half j is half
+// hr = j - r hpr of row r = j / hpr (hpr = 2 ceil(cols / 16) halves per padded
+// row), elements 8 hr .. 8 hr + 7 of the row, of which the first
+// n = min(8, cols - 8 hr) exist (the rest are padding zeros).  Codes and scales
+// keep the padded layout (dword j of the codes, scale byte j / 2), exactly as for
+// whole-block rows.
+//   Even lengths: a half starts on an even element, so it is four dwords, each
+//   loaded and stored whole when it lies in the row.
+//   Odd lengths (Odd): every other row starts on an odd element, so a half is
+//   eight bf16 elements, each loaded and stored on its own (two lanes never
+//   write into one dword).
+// The bf16 side uses ordinary (allocating) loads and stores: a lane's accesses at
+// a 16-byte lane stride each touch every line of the wave's span, and it is the
+// L2 that merges them into whole lines.
+struct HalfRows {
+    const uint16_t* x;      // the tensor (2-byte aligned; 4-byte aligned when cols is even)
+    int64_t cols;           // elements per row
     uint32_t hpr;           // halves per padded row
     int64_t nhalves;        // rows * hpr, below 2^32
 };
 
-// Dword index of the first element of padded half j, and its count of real elements.
-__device__ __forceinline__ int64_t even_half(const EvenRows& g, int64_t j, int& n)
+// Element index of the first element of padded half j, and its count of real elements.
+__device__ __forceinline__ int64_t row_half(const HalfRows& g, int64_t j, int& n)
 {
     const uint32_t r = (uint32_t)j / g.hpr;
     const uint32_t hr = (uint32_t)j - r * g.hpr;
     const int64_t left = g.cols - 8 * (int64_t)hr;
     n = left < 8 ? (int)left : 8;
-    return ((int64_t)r * g.cols + 8 * (int64_t)hr) / 2;
+    return (int64_t)r * g.cols + 8 * (int64_t)hr;
 }
 
-template <bool NtStore>
-__device__ __forceinline__ void store_even(uint32_t* y, int64_t d, int n, const uint4& o)
+// The n real elements of the half at element e, as four dwords (zeros past them).
+template <bool Odd>
+__device__ __forceinline__ void load_row_half(const uint16_t* x, int64_t e, int n, uint32_t (&w)[4])
+{
+    if (!Odd) {
+        const uint32_t* xd = reinterpret_cast<const uint32_t*>(x) + e / 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = 2 * i < n ? xd[i] : 0u;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = 2 * i < n ? x[e + 2 * i] : 0u;
+            const uint32_t hi = 2 * i + 1 < n ? x[e + 2 * i + 1] : 0u;
+            w[i] = lo | (hi << 16);
+        }
+    }
+}
+
+// The first n of the eight bf16 outputs o of a half to element e of y.
+template <bool Odd>
+__device__ __forceinline__ void store_row_half(uint16_t* y, int64_t e, int n, const uint4& o)
 {
     const uint32_t v[4] = {o.x, o.y, o.z, o.w};
+    if (!Odd) {
+        uint32_t* yd = reinterpret_cast<uint32_t*>(y) + e / 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (2 * i < n)
-            store4<NtStore>(y + d + i, v[i]);
+        for (int i = 0; i < 4; ++i)
+            if (2 * i < n)
+                yd[i] = v[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (2 * i < n)
+                y[e + 2 * i] = (uint16_t)(v[i] & 0xFFFFu);
+            if (2 * i + 1 < n)
+                y[e + 2 * i + 1] = (uint16_t)(v[i] >> 16);
+        }
+    }
 }
 
 // A quantizing pass over the padded halves with a grid stride, as quantize_pass:
-// body(w, j, d, n) gets the four dwords of half j (zeros past the row), the dword
-// index d of its first element and its element count n.
-template <bool Fence, typename Build, typename Body>
-__device__ __forceinline__ void even_pass(const EvenRows& g, Build build, Body body)
+// body(w, j, e, n) gets the four dwords of half j (zeros past the row), the element
+// index e of its first element and its element count n.
+template <bool Odd, bool Fence, typename Build, typename Body>
+__device__ __forceinline__ void rows_pass(const HalfRows& g, Build build, Body body)
 {
     const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
     if (Fence)
@@ -663,44 +698,42 @@ __device__ __forceinline__ void even_pass(const EvenRows& g, Build build, Body b
     for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < g.nhalves; base += stride) {
         uint32_t w[kUnroll][4];
         int n[kUnroll];
-        int64_t d[kUnroll];
+        int64_t e[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t j = base + (int64_t)u * kThreads;
             n[u] = 0;
-            d[u] = j < g.nhalves ? even_half(g, j, n[u]) : 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                w[u][i] = 2 * i < n[u] ? g.x[d[u] + i] : 0u;
+            e[u] = j < g.nhalves ? row_half(g, j, n[u]) : 0;
+            load_row_half<Odd>(g.x, e[u], n[u], w[u]);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t j = base + (int64_t)u * kThreads;
             if (j < g.nhalves)
-                body(w[u], j, d[u], n[u]);
+                body(w[u], j, e[u], n[u]);
         }
     }
 }
 
-template <bool Partials>
-__global__ __launch_bounds__(kThreads) void k_fake_quant_even(EvenRows g, uint32_t* y, AmaxIn src)
+template <bool Partials, bool Odd>
+__global__ __launch_bounds__(kThreads) void k_fake_quant_rows(HalfRows g, uint16_t* y, AmaxIn src)
 {
     __shared__ uint4 table[128 * kEntryWords / 4];
     uint32_t* tab = reinterpret_cast<uint32_t*>(table);
     const AmaxOfPass<Partials> am(src);
     float gs = Partials ? 0.0f : global_scale_of(am.direct);
-    even_pass<Partials>(g, [&] {
+    rows_pass<Odd, Partials>(g, [&] {
         if (Partials)
             gs = global_scale_of(am.finish(src));
         build_table(gs, tab);
-    }, [&](const uint32_t (&w)[4], int64_t, int64_t d, int n) {
-        const uint32_t* e = tab + scale_byte_of(pair_max(w), gs) * kEntryWords;
-        store_even<false>(y, d, n, decode_half(half_codes(w, e), __uint_as_float(e[1])));
+    }, [&](const uint32_t (&w)[4], int64_t, int64_t e, int n) {
+        const uint32_t* t = tab + scale_byte_of(pair_max(w), gs) * kEntryWords;
+        store_row_half<Odd>(y, e, n, decode_half(half_codes(w, t), __uint_as_float(t[1])));
     });
 }
 
-template <bool Partials>
-__global__ __launch_bounds__(kThreads) void k_quantize_pack_even(EvenRows g, uint32_t* __restrict__ packed,
+template <bool Partials, bool Odd>
+__global__ __launch_bounds__(kThreads) void k_quantize_pack_rows(HalfRows g, uint32_t* __restrict__ packed,
                                                                  uint8_t* __restrict__ scales,
                                                                  float* __restrict__ gs_out, AmaxIn src)
 {
@@ -710,7 +743,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack_even(EvenRows g, uin
     float gs = Partials ? 0.0f : global_scale_of(am.direct);
     if (!Partials && blockIdx.x == 0 && threadIdx.x == 0)
         *gs_out = gs;
-    even_pass<Partials>(g, [&] {
+    rows_pass<Odd, Partials>(g, [&] {
         if (Partials) {
             gs = global_scale_of(am.finish(src));
             if (blockIdx.x == 0 && threadIdx.x == 0)
@@ -725,10 +758,11 @@ __global__ __launch_bounds__(kThreads) void k_quantize_pack_even(EvenRows g, uin
     });
 }
 
-__global__ __launch_bounds__(kThreads) void k_dequant_unpack_even(const uint32_t* __restrict__ packed,
+template <bool Odd>
+__global__ __launch_bounds__(kThreads) void k_dequant_unpack_rows(const uint32_t* __restrict__ packed,
                                                                   const uint8_t* __restrict__ scales,
                                                                   const float* __restrict__ gs_in,
-                                                                  uint32_t* __restrict__ y, EvenRows g)
+                                                                  uint16_t* __restrict__ y, HalfRows g)
 {
     __shared__ float sd_of[128];
     const float gs = *gs_in;
@@ -750,8 +784,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant_unpack_even(const uint32_t
             const int64_t j = base + (int64_t)u * kThreads;
             if (j < g.nhalves) {
                 int n;
-                const int64_t d = even_half(g, j, n);
-                store_even<false>(y, d, n, decode_half(p[u], sd_of[sc[u] & 0x7Fu]));
+                const int64_t e = row_half(g, j, n);
+                store_row_half<Odd>(y, e, n, decode_half(p[u], sd_of[sc[u] & 0x7Fu]));
             }
         }
     }

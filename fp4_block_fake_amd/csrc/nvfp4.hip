@@ -219,15 +219,17 @@ int quant_wg_per_cu(int64_t nhalves, int mid, int large)
     return nhalves * 16 < NVFP4_MID_BYTES ? mid : large;
 }
 
-// Ragged rows of even length take the half-block kernels (32-bit half indices).
-bool even_rows(int64_t cols, const Matrix& m)
+// Ragged rows take the half-block kernels (32-bit half indices); from
+// NVFP4_HALF_ROWS_MAX_BLOCKS blocks on, the one-lane-per-block kernels.
+bool half_rows(int64_t cols, const Matrix& m)
 {
-    return m.ragged && cols % 2 == 0 && m.nblocks < ((int64_t)1 << 31);
+    (void)cols;
+    return m.ragged && m.nblocks < (int64_t)NVFP4_HALF_ROWS_MAX_BLOCKS;
 }
 
-EvenRows even_rows_of(const void* x, int64_t cols, const Matrix& m)
+HalfRows half_rows_of(const void* x, int64_t cols, const Matrix& m)
 {
-    return EvenRows{static_cast<const uint32_t*>(x), cols, (uint32_t)(2 * m.nbr), 2 * m.nblocks};
+    return HalfRows{static_cast<const uint16_t*>(x), cols, (uint32_t)(2 * m.nbr), 2 * m.nblocks};
 }
 
 // Workgroups per CU of the two-output pass over nhalves half blocks.
@@ -250,15 +252,20 @@ nvfp4_status enqueue_fake_quant(const void* x, void* y, int64_t cols, const Matr
 {
     if (m.numel == 0)
         return NVFP4_OK;
-    const float* a = src.amax[0];                  // the odd-length ragged kernels take a direct amax
-    if (even_rows(cols, m)) {
-        const EvenRows g = even_rows_of(x, cols, m);
+    const float* a = src.amax[0];                  // the one-lane-per-block kernels take a direct amax
+    if (half_rows(cols, m)) {
+        const HalfRows g = half_rows_of(x, cols, m);
         const dim3 grid(persistent_grid(g.nhalves, (int64_t)kThreads * kUnroll,
                                         quant_wg_per_cu(g.nhalves, NVFP4_FQ_MID_WG_PER_CU, NVFP4_FQ_WG_PER_CU)));
-        if (src.partials)
-            k_fake_quant_even<true><<<grid, kThreads, 0, s>>>(g, static_cast<uint32_t*>(y), src);
+        uint16_t* yh = static_cast<uint16_t*>(y);
+        if (cols % 2 == 0 && src.partials)
+            k_fake_quant_rows<true, false><<<grid, kThreads, 0, s>>>(g, yh, src);
+        else if (cols % 2 == 0)
+            k_fake_quant_rows<false, false><<<grid, kThreads, 0, s>>>(g, yh, src);
+        else if (src.partials)
+            k_fake_quant_rows<true, true><<<grid, kThreads, 0, s>>>(g, yh, src);
         else
-            k_fake_quant_even<false><<<grid, kThreads, 0, s>>>(g, static_cast<uint32_t*>(y), src);
+            k_fake_quant_rows<false, true><<<grid, kThreads, 0, s>>>(g, yh, src);
         return launched();
     }
     if (m.ragged) {
@@ -289,16 +296,20 @@ nvfp4_status enqueue_fake_quant(const void* x, void* y, int64_t cols, const Matr
 nvfp4_status enqueue_quantize_pack(const void* x, int64_t cols, const Matrix& m, uint8_t* packed, uint8_t* scales,
                                    float* global_scale, const AmaxIn& src, hipStream_t s)
 {
-    const float* a = src.amax[0];                  // the odd-length ragged kernel takes a direct amax
-    if (even_rows(cols, m)) {
-        const EvenRows g = even_rows_of(x, cols, m);
+    const float* a = src.amax[0];                  // the one-lane-per-block kernel takes a direct amax
+    if (half_rows(cols, m)) {
+        const HalfRows g = half_rows_of(x, cols, m);
         const dim3 grid(persistent_grid(g.nhalves, (int64_t)kThreads * kUnroll,
                                         quant_wg_per_cu(g.nhalves, NVFP4_QP_MID_WG_PER_CU, NVFP4_QP_WG_PER_CU)));
         uint32_t* pv = reinterpret_cast<uint32_t*>(packed);
-        if (src.partials)
-            k_quantize_pack_even<true><<<grid, kThreads, 0, s>>>(g, pv, scales, global_scale, src);
+        if (cols % 2 == 0 && src.partials)
+            k_quantize_pack_rows<true, false><<<grid, kThreads, 0, s>>>(g, pv, scales, global_scale, src);
+        else if (cols % 2 == 0)
+            k_quantize_pack_rows<false, false><<<grid, kThreads, 0, s>>>(g, pv, scales, global_scale, src);
+        else if (src.partials)
+            k_quantize_pack_rows<true, true><<<grid, kThreads, 0, s>>>(g, pv, scales, global_scale, src);
         else
-            k_quantize_pack_even<false><<<grid, kThreads, 0, s>>>(g, pv, scales, global_scale, src);
+            k_quantize_pack_rows<false, true><<<grid, kThreads, 0, s>>>(g, pv, scales, global_scale, src);
         return launched();
     }
     if (m.ragged) {
@@ -652,7 +663,7 @@ nvfp4_status enqueue_fake_quant_ws(const void* x, void* y, int64_t cols, const M
 {
     if (m.numel == 0)
         return amax_out ? enqueue_reset(amax_out, s) : NVFP4_OK;
-    if (!m.ragged || even_rows(cols, m)) {
+    if (!m.ragged || half_rows(cols, m)) {
         AmaxIn src;
         if (enqueue_amax_partials(&x, &m.numel, 1, ws, s, &src, ObserverArgs{}, 0,
                                   amax_alloc_bytes(2 * m.numel, NVFP4_FQ_AMAX_ALLOC_MID)) != NVFP4_OK)
@@ -1003,11 +1014,15 @@ nvfp4_status nvfp4_dequant_unpack(const uint8_t* packed, const uint8_t* scales,
         return NVFP4_ERR_OVERLAP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (even_rows(cols, m)) {
-        const EvenRows g = even_rows_of(y, cols, m);
-        k_dequant_unpack_even<<<persistent_grid(g.nhalves, (int64_t)kThreads * kDqUnroll, NVFP4_DQ_WG_PER_CU),
-                                kThreads, 0, s>>>(reinterpret_cast<const uint32_t*>(packed), scales, global_scale,
-                                                  static_cast<uint32_t*>(y), g);
+    if (half_rows(cols, m)) {
+        const HalfRows g = half_rows_of(y, cols, m);
+        const unsigned grid = persistent_grid(g.nhalves, (int64_t)kThreads * kDqUnroll, NVFP4_DQ_WG_PER_CU);
+        const uint32_t* pv = reinterpret_cast<const uint32_t*>(packed);
+        uint16_t* yh = static_cast<uint16_t*>(y);
+        if (cols % 2 == 0)
+            k_dequant_unpack_rows<false><<<grid, kThreads, 0, s>>>(pv, scales, global_scale, yh, g);
+        else
+            k_dequant_unpack_rows<true><<<grid, kThreads, 0, s>>>(pv, scales, global_scale, yh, g);
         return launched();
     }
     if (m.ragged) {
@@ -1100,7 +1115,7 @@ nvfp4_status nvfp4_quantize_pack_ws(const void* x, int64_t rows, int64_t cols, f
         return NVFP4_ERR_OVERLAP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (!m.ragged || (m.numel > 0 && even_rows(cols, m))) {
+    if (!m.ragged || (m.numel > 0 && half_rows(cols, m))) {
         AmaxIn src;
         if (enqueue_amax_partials(&x, &m.numel, 1, workspace, s, &src, ObserverArgs{}, 0,
                                   amax_alloc_bytes(2 * m.numel, NVFP4_QP_AMAX_ALLOC_MID)) != NVFP4_OK)

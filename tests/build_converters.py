@@ -2,10 +2,12 @@
 
 * tests/libconverters_gpu.so from tests/converters_gpu.hip (the conversion
   instructions applied to every input);
-* tests/libnvfp4_exact_path.so: libnvfp4's own source built with every
-  quantizing wave on the exact-quotient code path (NVFP4_EXACT_PATH=2), so the
-  parity tests can run that path under every scale byte, not only in waves
-  that hold a block whose multiplier is not certified.
+* tests/libnvfp4_test_paths.so: libnvfp4's own source built with the code paths
+  that ordinary shapes rarely or never reach switched on for everything: every
+  quantizing wave on the exact-quotient path (NVFP4_EXACT_PATH=2), not only
+  waves that hold a block whose multiplier is not certified, and every ragged
+  shape through the one-lane-per-block kernels (NVFP4_HALF_ROWS_MAX_BLOCKS=0),
+  which the library otherwise keeps for tensors of 2^31 blocks and more.
 
 The GPU tests load them and fail if they are missing.
 """
@@ -15,7 +17,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "converters_gpu.hip")
 LIB = os.path.join(HERE, "libconverters_gpu.so")
-EXACT_LIB = os.path.join(HERE, "libnvfp4_exact_path.so")
+TEST_PATHS_LIB = os.path.join(HERE, "libnvfp4_test_paths.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
@@ -27,22 +29,22 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
-    build_exact_path(verbose)
+    build_test_paths(verbose)
     return LIB
 
 
-def build_exact_path(verbose: bool = False) -> str:
+def build_test_paths(verbose: bool = False) -> str:
     root = os.path.dirname(HERE)
-    tmp = EXACT_LIB + ".tmp%d" % os.getpid()
+    tmp = TEST_PATHS_LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared", "-ffp-contract=off",
            "-fno-fast-math", "-fhip-fp32-correctly-rounded-divide-sqrt", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-Wall", "-DNVFP4_EXACT_PATH=2", "-I", os.path.join(root, "include"), "-o", tmp,
+           "-packed-fp32-ops", "-Wall", "-DNVFP4_EXACT_PATH=2", "-DNVFP4_HALF_ROWS_MAX_BLOCKS=0", "-I", os.path.join(root, "include"), "-o", tmp,
            os.path.join(root, "fp4_block_fake_amd", "csrc", "nvfp4.hip")]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, EXACT_LIB)
-    return EXACT_LIB
+    os.replace(tmp, TEST_PATHS_LIB)
+    return TEST_PATHS_LIB
 
 
 if __name__ == "__main__":

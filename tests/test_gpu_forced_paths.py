@@ -1,0 +1,138 @@
+"""Code paths that ordinary shapes rarely or never reach, forced on everything, against
+the oracle bit for bit.  tests/libnvfp4_test_paths.so is libnvfp4's own source built
+with two switches, and the binding is pointed at it for the duration of this module:
+
+* every quantizing wave on the exact-quotient code path.  In the library a wave takes
+  it only when one of its blocks has a scale byte whose multiplier is not certified
+  (for example the c2 weight, whose global scale is a power of two and whose mantissa-7
+  scale bytes meet exact ties).  Here it runs under every scale byte of every global
+  scale the cases reach: the sweeps of every bf16 magnitude around every decision
+  threshold and as a block maximum, every code times every scale, exact ties, underflow
+  and -0, wide dynamic ranges, saturating and clamped amaxes, and whole c2 and c4-weight
+  tensors;
+* every ragged shape (rows not a multiple of 16) through the one-lane-per-block
+  kernels, which the library keeps for tensors of 2^31 blocks and more, and the
+  workspace calls through their three-launch form (a one-workgroup reduction of the
+  partial maxima between the passes): the ragged parity, workspace and observer cases.
+
+The parity helpers are those of test_gpu_parity.py, test_gpu_workspace.py and
+test_gpu_observe.py.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from conftest import ROOT
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU visible", allow_module_level=True)
+
+import fp4_block_fake_amd as nv  # noqa: E402
+import test_gpu_observe as observe  # noqa: E402
+import test_gpu_parity as parity  # noqa: E402
+import test_gpu_workspace as workspace  # noqa: E402
+
+EXACT_LIB = os.path.join(ROOT, "tests", "libnvfp4_test_paths.so")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def exact_path_library():
+    if not os.path.exists(EXACT_LIB):
+        pytest.fail("tests/libnvfp4_test_paths.so is not built (run __graft_entry__.build())")
+    saved = nv.lib
+    nv.lib = nv._load(EXACT_LIB)
+    yield
+    nv.lib = saved
+
+
+@pytest.mark.parametrize("amax_value", parity.SWEEP_AMAX)
+def test_every_magnitude_around_every_threshold(amax_value):
+    parity.test_every_magnitude_around_every_threshold(amax_value)
+
+
+@pytest.mark.parametrize("amax_value", parity.SWEEP_AMAX)
+def test_every_bf16_magnitude_as_a_block(amax_value):
+    parity.test_every_bf16_magnitude_as_a_block(amax_value)
+
+
+@pytest.mark.parametrize("k", [4, 10, 12])
+def test_every_code_times_every_scale(k):
+    parity.test_every_code_times_every_scale(k)
+
+
+def test_exact_ties():
+    parity.test_exact_ties()
+
+
+def test_underflow_and_negative_zero_codes():
+    parity.test_underflow_and_negative_zero_codes()
+
+
+def test_zero_and_negative_zero_tensor():
+    parity.test_zero_and_negative_zero_tensor()
+
+
+@pytest.mark.parametrize("seed,lo,hi", [(1, -133, 120), (2, -140, -100), (3, 60, 127), (4, -30, 10)])
+def test_wide_dynamic_range(seed, lo, hi):
+    parity.test_wide_dynamic_range(seed, lo, hi)
+
+
+@pytest.mark.parametrize("amax_in", [1e-20, 3e-12, 0.01, 0.37, 6.0, 12345.6, 5e20, 3.3e38])
+def test_cached_amax_saturation_and_clamp(amax_in):
+    parity.test_cached_amax_saturation_and_clamp(amax_in)
+
+
+def test_block_scale_divide_by_six_straddles():
+    parity.test_block_scale_divide_by_six_straddles()
+
+
+def test_c2_whole():
+    parity.check_all_ops(synth.c2_weight(), what="c2 (forced paths)")
+
+
+def test_c4_weight_whole():
+    w = synth.c4_weight()
+    parity.say("c4 weight %s (forced paths)" % (w.shape,))
+    amax = parity.scalar(0.0)
+    y = nv.nvfp4_fake_quant(parity.dev(w), amax_out=amax)
+    torch.cuda.synchronize()
+    a = parity.oracle_amax(w)
+    assert parity.fbits(amax.item()) == parity.fbits(a)
+    parity.assert_same(parity.host(y), parity.oracle_fake_quant(w, a), "c4 weight fq (forced paths)")
+
+
+def test_the_library_is_the_test_build():
+    assert nv.lib._name == EXACT_LIB
+    x = np.zeros((1, 16), np.uint16)
+    parity.check_all_ops(x, amax_in=1.0, what="test build loaded")
+
+
+RAGGED = [(1, 1), (3, 7), (5, 15), (4, 17), (33, 40), (9, 1000), (2, 4097), (130, 24), (1000, 33), (2, 2),
+          (7, 18), (64, 4100), (1025, 30), (17, 1006), (300, 62), (513, 8)]
+
+
+@pytest.mark.parametrize("shape", RAGGED)
+def test_ragged_columns_zero_padded(shape):
+    parity.test_ragged_columns_zero_padded(shape)
+
+
+@pytest.mark.parametrize("shape", [s for s in workspace.SHAPES if s[1] % 16])
+@pytest.mark.parametrize("inplace", [False, True])
+def test_ragged_fake_quant_ws(shape, inplace):
+    workspace.test_fake_quant_ws(shape, inplace)
+
+
+@pytest.mark.parametrize("shape", [s for s in workspace.SHAPES if s[1] % 16])
+def test_ragged_quantize_pack_ws(shape):
+    workspace.test_quantize_pack_ws(shape)
+
+
+@pytest.mark.parametrize("shape", [s for s in observe.SHAPES if s[1] % 16])
+@pytest.mark.parametrize("inplace", [None, 0, 1])
+def test_ragged_observe_fake_quant(shape, inplace):
+    observe.test_two_observers_shapes(shape, inplace)

@@ -182,8 +182,9 @@ def test_c5_row_shards_with_the_all_reduced_amax():
                                    (300, 62), (513, 8)])
 def test_ragged_columns_zero_padded(shape):
     """Rows not a multiple of 16: zero-padded blocks, padded code/scale layout, cols outputs.
-    Odd lengths go through the one-lane-per-block kernels, even lengths through the
-    half-block kernels (a half may lie wholly in the padding, as for 18 or 8 columns)."""
+    Both go through the half-block kernels, with element-wise accesses for odd lengths and
+    dword accesses for even ones (a half may lie wholly in the padding, as for 18 or 8
+    columns)."""
     rng = np.random.default_rng(shape[0] * 131 + shape[1])
     x = synth.to_bf16_bits((rng.standard_normal(shape) * np.exp(rng.uniform(-3, 3, shape))).astype(np.float32))
     check_all_ops(x, what="ragged cols")

@@ -40,7 +40,7 @@ def dirty_workspace():
 # shapes: one half block short of a chunk, chunk edges, ragged rows, a single value,
 # wide rows, and the empty tensor
 SHAPES = [(1, 16), (3, 20), (7, 1), (1023, 16), (1025, 16), (64, 4096), (33, 40), (1037, 144), (0, 16),
-          (0, 5), (0, 18), (2, 18), (257, 4100), (4096, 4100)]
+          (0, 5), (0, 18), (2, 18), (257, 4100), (4096, 4100), (5, 17), (129, 4097)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
