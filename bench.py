@@ -398,6 +398,18 @@ def secondary(nv, synth, np, torch, dev, reps=20, only=None):
             line("mx_%s_dequant_unpack" % tag, lambda: nv.nvfp4_mx_dequant_unpack(pm, sm, y=ym), 2.625 * nm,
                  cold=True, elems=nm)
             del xm, ym, pm, sm
+        # ragged rows (4100 = 128 blocks of 32 and 4 elements): the quarter-block row kernels
+        xm = to_dev(synth.normal_bf16(9, (4096, 4100), 0.02))
+        nm = xm.numel()
+        ym = torch.empty_like(xm)
+        pm, sm = nv.nvfp4_mx_quantize_pack(xm)
+        line("mx_ragged_4096x4100_fake_quant", lambda: nv.nvfp4_mx_fake_quant(xm, y=ym), 4.0 * nm, cold=True,
+             elems=nm)
+        line("mx_ragged_4096x4100_quantize_pack", lambda: nv.nvfp4_mx_quantize_pack(xm, packed=pm, scales=sm),
+             2.625 * nm, cold=True, elems=nm)
+        line("mx_ragged_4096x4100_dequant_unpack",
+             lambda: nv.nvfp4_mx_dequant_unpack(pm, sm, y=ym, cols=4100), 2.625 * nm, cold=True, elems=nm)
+        del xm, ym, pm, sm
 
     if group("c5_"):
         wc = to_dev(synth.c5_weight())

@@ -164,9 +164,91 @@ __global__ __launch_bounds__(kThreads) void k_mx_dequant_unpack(const uint32_t* 
     }
 }
 
-// ---------------------------------------------------------------- ragged rows
+// ---------------------------------------------------------------- ragged rows, quarter-block lanes
 //
-// Rows whose length is not a multiple of 32: one lane per block, elements loaded
+// Rows whose length is not a multiple of 32, over the zero-padded rows, on the
+// quarter-block lanes of the whole-block kernels: padded quarter j is the same
+// 8-element unit of a row as a half block of the NVFP4 row kernels (HalfRows with
+// 4 ceil(cols / 32) units per padded row), loaded and stored with dword accesses
+// for even lengths and element by element for odd ones.  Quarter counts are
+// multiples of 4, so the four lanes of a block are all active or all inactive at
+// the quad max.
+template <bool Odd, typename Body>
+__device__ __forceinline__ void mx_rows_pass(const HalfRows& g, Body body)
+{
+    const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
+    for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; base < g.nhalves; base += stride) {
+        uint32_t w[kUnroll][4];
+        int n[kUnroll];
+        int64_t e[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t j = base + (int64_t)u * kThreads;
+            n[u] = 0;
+            e[u] = j < g.nhalves ? row_half(g, j, n[u]) : 0;
+            load_row_half<Odd>(g.x, e[u], n[u], w[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t j = base + (int64_t)u * kThreads;
+            if (j < g.nhalves)
+                body(w[u], j, e[u], n[u]);
+        }
+    }
+}
+
+template <bool Odd>
+__global__ __launch_bounds__(kThreads) void k_mx_fake_quant_rows(HalfRows g, uint16_t* y)
+{
+    mx_rows_pass<Odd>(g, [&](const uint32_t (&w)[4], int64_t, int64_t e, int n) {
+        const float s = mx_scale_of(quad_max(w));
+        store_row_half<Odd>(y, e, n, decode_half(mx_codes(w, mx_divisor(s)), s));
+    });
+}
+
+template <bool Odd>
+__global__ __launch_bounds__(kThreads) void k_mx_quantize_pack_rows(HalfRows g, uint32_t* __restrict__ packed,
+                                                                    float* __restrict__ scales)
+{
+    mx_rows_pass<Odd>(g, [&](const uint32_t (&w)[4], int64_t j, int64_t, int) {
+        const float s = mx_scale_of(quad_max(w));
+        store4<NVFP4_QP_NT_ST != 0>(packed + j, mx_codes(w, mx_divisor(s)));
+        if (!(j & 3))
+            scales[j >> 2] = s;
+    });
+}
+
+template <bool Odd>
+__global__ __launch_bounds__(kThreads) void k_mx_dequant_unpack_rows(const uint32_t* __restrict__ packed,
+                                                                     const float* __restrict__ scales,
+                                                                     uint16_t* __restrict__ y, HalfRows g)
+{
+    const int64_t stride = (int64_t)gridDim.x * kThreads * kDqUnroll;
+    for (int64_t base = (int64_t)blockIdx.x * kThreads * kDqUnroll + threadIdx.x; base < g.nhalves;
+         base += stride) {
+        uint32_t p[kDqUnroll];
+        float s[kDqUnroll];
+#pragma unroll
+        for (int u = 0; u < kDqUnroll; ++u) {
+            const int64_t j = base + (int64_t)u * kThreads;
+            p[u] = j < g.nhalves ? packed[j] : 0u;
+            s[u] = j < g.nhalves ? scales[j >> 2] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kDqUnroll; ++u) {
+            const int64_t j = base + (int64_t)u * kThreads;
+            if (j < g.nhalves) {
+                int n;
+                const int64_t e = row_half(g, j, n);
+                store_row_half<Odd>(y, e, n, decode_half(p[u], s[u]));
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- ragged rows, one lane per block
+//
+// The same for tensors of 2^30 blocks and more: one lane per block, elements loaded
 // and stored one at a time and masked at the row end (rows may start at any
 // element).  Codes and scales keep the padded layout: block f is bytes 16f ..
 // 16f + 15 of the packed codes and scale f.

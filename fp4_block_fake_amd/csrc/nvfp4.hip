@@ -1232,6 +1232,19 @@ nvfp4_status nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* pa
     return enqueue_linear_tiled<NVFP4_TILE_MW, kNW>(x, m, k, packed, scales, global_scale, n, bias, y, s);
 }
 
+// MXFP4 ragged rows take the quarter-block kernels while the quarter count fits
+// their 32-bit index (the same bound as the NVFP4 half-block kernels'), and the
+// one-lane-per-block kernels beyond.
+bool mx_rows(const Matrix& m)
+{
+    return m.ragged && 4 * m.nblocks < 2 * (int64_t)NVFP4_HALF_ROWS_MAX_BLOCKS;
+}
+
+HalfRows mx_rows_of(const void* x, int64_t cols, const Matrix& m)
+{
+    return HalfRows{static_cast<const uint16_t*>(x), cols, (uint32_t)(4 * m.nbr), 4 * m.nblocks};
+}
+
 nvfp4_status nvfp4_mx_fake_quant(const void* x, void* y, int64_t rows, int64_t cols, void* stream)
 {
     Matrix m;
@@ -1249,6 +1262,15 @@ nvfp4_status nvfp4_mx_fake_quant(const void* x, void* y, int64_t rows, int64_t c
     (void)hipGetLastError();
     if (m.numel == 0)
         return NVFP4_OK;
+    if (mx_rows(m)) {
+        const HalfRows g = mx_rows_of(x, cols, m);
+        const unsigned grid = persistent_grid(g.nhalves, (int64_t)kThreads * kUnroll, NVFP4_MX_WG_PER_CU);
+        if (cols % 2 == 0)
+            k_mx_fake_quant_rows<false><<<grid, kThreads, 0, s>>>(g, static_cast<uint16_t*>(y));
+        else
+            k_mx_fake_quant_rows<true><<<grid, kThreads, 0, s>>>(g, static_cast<uint16_t*>(y));
+        return launched();
+    }
     if (m.ragged) {
         k_mx_fake_quant_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
             static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), RaggedShape{cols, m.nbr, m.nblocks});
@@ -1279,6 +1301,16 @@ nvfp4_status nvfp4_mx_quantize_pack(const void* x, int64_t rows, int64_t cols, u
     (void)hipGetLastError();
     if (m.numel == 0)
         return NVFP4_OK;
+    if (mx_rows(m)) {
+        const HalfRows g = mx_rows_of(x, cols, m);
+        const unsigned grid = persistent_grid(g.nhalves, (int64_t)kThreads * kUnroll, NVFP4_MX_WG_PER_CU);
+        uint32_t* pv = reinterpret_cast<uint32_t*>(packed);
+        if (cols % 2 == 0)
+            k_mx_quantize_pack_rows<false><<<grid, kThreads, 0, s>>>(g, pv, scales);
+        else
+            k_mx_quantize_pack_rows<true><<<grid, kThreads, 0, s>>>(g, pv, scales);
+        return launched();
+    }
     if (m.ragged) {
         k_mx_quantize_pack_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
             static_cast<const uint16_t*>(x), reinterpret_cast<uint4*>(packed), scales,
@@ -1310,6 +1342,16 @@ nvfp4_status nvfp4_mx_dequant_unpack(const uint8_t* packed, const float* scales,
         return NVFP4_ERR_OVERLAP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
+    if (mx_rows(m)) {
+        const HalfRows g = mx_rows_of(y, cols, m);
+        const unsigned grid = persistent_grid(g.nhalves, (int64_t)kThreads * kDqUnroll, NVFP4_MX_WG_PER_CU);
+        const uint32_t* pv = reinterpret_cast<const uint32_t*>(packed);
+        if (cols % 2 == 0)
+            k_mx_dequant_unpack_rows<false><<<grid, kThreads, 0, s>>>(pv, scales, static_cast<uint16_t*>(y), g);
+        else
+            k_mx_dequant_unpack_rows<true><<<grid, kThreads, 0, s>>>(pv, scales, static_cast<uint16_t*>(y), g);
+        return launched();
+    }
     if (m.ragged) {
         k_mx_dequant_unpack_ragged<<<persistent_grid(m.nblocks, kThreads, kRaggedWgPerCu), kThreads, 0, s>>>(
             reinterpret_cast<const uint4*>(packed), scales, static_cast<uint16_t*>(y),

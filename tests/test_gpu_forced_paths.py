@@ -10,13 +10,14 @@ with two switches, and the binding is pointed at it for the duration of this mod
   threshold and as a block maximum, every code times every scale, exact ties, underflow
   and -0, wide dynamic ranges, saturating and clamped amaxes, and whole c2 and c4-weight
   tensors;
-* every ragged shape (rows not a multiple of 16) through the one-lane-per-block
-  kernels, which the library keeps for tensors of 2^31 blocks and more, and the
-  workspace calls through their three-launch form (a one-workgroup reduction of the
-  partial maxima between the passes): the ragged parity, workspace and observer cases.
+* every ragged shape (rows not a multiple of the block) through the one-lane-per-block
+  kernels, NVFP4 and MXFP4, which the library keeps for tensors of 2^31 (MXFP4: 2^30)
+  blocks and more, and the workspace calls through their three-launch form (a
+  one-workgroup reduction of the partial maxima between the passes): the ragged parity,
+  workspace, observer and MXFP4 cases.
 
-The parity helpers are those of test_gpu_parity.py, test_gpu_workspace.py and
-test_gpu_observe.py.
+The parity helpers are those of test_gpu_parity.py, test_gpu_workspace.py,
+test_gpu_observe.py and test_gpu_mx.py.
 """
 import os
 
@@ -33,6 +34,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU visible", allow_module_level=True)
 
 import fp4_block_fake_amd as nv  # noqa: E402
+import test_gpu_mx as mx  # noqa: E402
 import test_gpu_observe as observe  # noqa: E402
 import test_gpu_parity as parity  # noqa: E402
 import test_gpu_workspace as workspace  # noqa: E402
@@ -136,3 +138,8 @@ def test_ragged_quantize_pack_ws(shape):
 @pytest.mark.parametrize("inplace", [None, 0, 1])
 def test_ragged_observe_fake_quant(shape, inplace):
     observe.test_two_observers_shapes(shape, inplace)
+
+
+@pytest.mark.parametrize("shape", mx.MX_RAGGED)
+def test_mx_ragged_rows(shape):
+    mx.test_ragged_rows_zero_padded(shape)

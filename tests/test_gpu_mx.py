@@ -65,8 +65,11 @@ def test_c5_weight_whole():
     assert torch.equal(y.view(torch.int16), xt.view(torch.int16))
 
 
-@pytest.mark.parametrize("shape", [(1, 1), (3, 7), (5, 16), (4, 31), (33, 33), (9, 40), (2, 1000), (7, 4097),
-                                   (130, 48), (1000, 65)])
+MX_RAGGED = [(1, 1), (3, 7), (5, 16), (4, 31), (33, 33), (9, 40), (2, 1000), (7, 4097), (130, 48), (1000, 65),
+             (513, 100), (257, 4099)]
+
+
+@pytest.mark.parametrize("shape", MX_RAGGED)
 def test_ragged_rows_zero_padded(shape):
     rng = np.random.default_rng(shape[0] * 31 + shape[1])
     x = synth.to_bf16_bits((rng.standard_normal(shape) * np.exp(rng.uniform(-4, 4, shape))).astype(np.float32))
