@@ -88,3 +88,89 @@ def test_captured_sequence_replays_exactly():
         got = oracle.bf16_array_to_f64(host(yl))
         mag = oracle.linear_magnitude(host(xl), p_ref, s_ref, g_ref, 1024)
         assert np.all(np.abs(got - y_lin) <= 2.0 ** -8 * np.abs(y_lin) + 2 * 1032 * 2.0 ** -24 * mag + 2.0 ** -133)
+
+
+def test_captured_other_calls_replay_exactly():
+    """The MXFP4 calls (whole-block and ragged rows), the no-allocation fake-quant, the
+    dual fake-quant, odd-length ragged rows, and the linear layer on its LDS-staged
+    tiles (128 and 512 rows of x), captured together and replayed after eager work
+    that overwrites every output."""
+    rng = np.random.default_rng(67)
+    x = synth.to_bf16_bits((rng.standard_normal((256, 1024)) * 0.05).astype(np.float32))
+    xr = synth.to_bf16_bits((rng.standard_normal((65, 1001)) * 0.05).astype(np.float32))
+    xt, xrt = dev(x), dev(xr)
+    y_mx, y_mxr, y_na, y_odd = (torch.empty_like(xt), torch.empty_like(xrt), torch.empty_like(xt),
+                                torch.empty_like(xrt))
+    y0, y1 = torch.empty_like(xt), torch.empty_like(xt)
+    p_mx, s_mx = nv.nvfp4_mx_quantize_pack(xt)
+    p_mxr, s_mxr = nv.nvfp4_mx_quantize_pack(xrt)
+    y_mxd = torch.empty_like(xt)
+    a_na, a0, a1 = scalar(0.0), scalar(0.0), scalar(0.0)
+    packed, scales, gs = nv.nvfp4_quantize_pack(xt)
+    torch.cuda.synchronize()
+    p_ref, s_ref, g_ref = oracle.quantize(x, oracle.amax(x))
+    xl = {m: dev(synth.to_bf16_bits(rng.standard_normal((m, 1024)).astype(np.float32))) for m in (128, 512)}
+    yl = {m: torch.empty((m, 256), dtype=torch.bfloat16, device=DEV) for m in (128, 512)}
+    st0, st1 = 0.5, 2.0
+
+    def sequence():
+        nv.nvfp4_mx_fake_quant(xt, y=y_mx)
+        nv.nvfp4_mx_quantize_pack(xt, packed=p_mx, scales=s_mx)
+        nv.nvfp4_mx_dequant_unpack(p_mx, s_mx, y=y_mxd)
+        nv.nvfp4_mx_fake_quant(xrt, y=y_mxr)
+        nv.nvfp4_mx_quantize_pack(xrt, packed=p_mxr, scales=s_mxr)
+        nv.nvfp4_fake_quant_noalloc(xt, y=y_na, amax_out=a_na)
+        nv.nvfp4_fake_quant_dual(xt, a0, a1, y0=y0, y1=y1)
+        nv.nvfp4_fake_quant(xrt, y=y_odd)
+        for m in (128, 512):
+            nv.nvfp4_linear(xl[m], packed, scales, gs, y=yl[m])
+
+    def set_amaxes():
+        a0.fill_(st0)
+        a1.fill_(st1)
+
+    set_amaxes()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sequence()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sequence()
+    torch.cuda.synchronize()
+
+    p_mx_ref, s_mx_ref = oracle.mx_quantize(x)
+    p_mxr_ref, s_mxr_ref = oracle.mx_quantize(xr)
+    a = oracle.amax(x)
+    for replay in range(3):
+        for t in (y_mx, y_mxr, y_na, y_odd, y0, y1, y_mxd, *yl.values()):
+            t.fill_(float(replay + 3))
+        for t in (p_mx, p_mxr):
+            t.fill_(0xEE)
+        for t in (s_mx, s_mxr):
+            t.fill_(-9.0)
+        a_na.fill_(-5.0)
+        set_amaxes()
+        torch.cuda.synchronize()
+        say("graph replay (other calls) %d" % replay)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_same(host(y_mx), oracle.mx_fake_quant(x), "replayed mx fake-quant")
+        assert_same(p_mx.cpu().numpy(), p_mx_ref, "replayed mx codes")
+        assert_same(s_mx.cpu().numpy().view(np.uint32), s_mx_ref.view(np.uint32), "replayed mx scales")
+        assert_same(host(y_mxd), oracle.mx_dequantize(p_mx_ref, s_mx_ref, 1024), "replayed mx unpack")
+        assert_same(host(y_mxr), oracle.mx_fake_quant(xr), "replayed mx ragged fake-quant")
+        assert_same(p_mxr.cpu().numpy(), p_mxr_ref, "replayed mx ragged codes")
+        assert fbits(a_na.item()) == fbits(a)
+        assert_same(host(y_na), oracle.fake_quant(x, a), "replayed no-allocation fake-quant")
+        assert_same(host(y0), oracle.fake_quant(x, st0), "replayed dual 0")
+        assert_same(host(y1), oracle.fake_quant(x, st1), "replayed dual 1")
+        assert_same(host(y_odd), oracle.fake_quant(xr), "replayed odd-length rows")
+        for m in (128, 512):
+            y_lin = oracle.linear(host(xl[m]), p_ref, s_ref, g_ref, 1024)
+            got = oracle.bf16_array_to_f64(host(yl[m]))
+            mag = oracle.linear_magnitude(host(xl[m]), p_ref, s_ref, g_ref, 1024)
+            assert np.all(np.abs(got - y_lin) <= 2.0 ** -8 * np.abs(y_lin) + 2 * 1032 * 2.0 ** -24 * mag
+                          + 2.0 ** -133), "replayed linear m=%d" % m
