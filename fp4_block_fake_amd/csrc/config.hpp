@@ -103,6 +103,18 @@ namespace {
 #ifndef NVFP4_LIN_LDS_FLAT
 #define NVFP4_LIN_LDS_FLAT 1      // 1: whole groups of four K steps run without per-step branches
 #endif
+#ifndef NVFP4_LIN_LDS_KG2
+#define NVFP4_LIN_LDS_KG2 1       // 1: the 128 x 128 LDS tile runs two K groups of 4 waves (K / 64 even)
+#endif
+#ifndef NVFP4_LIN_LDS_XCLAMP
+#define NVFP4_LIN_LDS_XCLAMP 1    // 1: x rows past M load row M - 1 instead of zeros (no per-load branch)
+#endif
+#ifndef NVFP4_LIN_RETILE
+#define NVFP4_LIN_RETILE 1        // 1: a partial last round of 256 x 256 linear tiles runs as narrower tiles
+#endif
+#ifndef NVFP4_LIN_RETILE_CUS
+#define NVFP4_LIN_RETILE_CUS 0    // CUs the re-tiling plans for; 0: the device's (a test build sets a few)
+#endif
 #ifndef NVFP4_LIN_LDS_REMAP
 #define NVFP4_LIN_LDS_REMAP 1     // 1: the LDS-staged linear kernel orders its tiles by XCD
 #endif

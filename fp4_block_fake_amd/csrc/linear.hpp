@@ -479,9 +479,14 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_linear_tiled(const uint16_t
 // LDS writes sit between this stage's MFMA slices so that the VALU work overlaps
 // the matrix cores.  Rows of x past M read as zeros and weight rows past N read
 // row 0; neither is stored (an output element depends only on its own rows).
-// Shapes used: 8 waves, 256 x 256 (WM 4, TM 2, TN 4: two waves per SIMD at 238
+// Shapes used: 8 waves, 256 x 256 (WM 4, TM 2, TN 4: two waves per SIMD at 248
 // VGPRs), and 4 waves, 128 x 128 (WM 2, TM 2, TN 2) for fewer rows of x, where
-// the large tile would leave CUs idle.
+// the large tile would leave CUs idle; that one in two K groups (8 waves) when its
+// tiles fit one per CU, which otherwise would hold one wave per SIMD.  A narrower tile (TN < 4, 64 TN weight
+// rows per workgroup) leaves the weight staging to the first 2 kN threads (whole
+// waves); it serves the last, partial round of 256 x 256 tiles, re-tiled so that
+// one round of narrower tiles covers it.  y has row stride ldy, so a launch can
+// cover a range of weight rows (packed, scales, bias and y offset by the caller).
 constexpr int kLdsK = 64;
 constexpr int kLdsStride = kLdsK + 8;          // bf16 per LDS row (padding against bank conflicts)
 constexpr int kLdsXDepth = 2;                  // register stages of x loads in flight
@@ -501,29 +506,43 @@ struct LdsTile {
     static constexpr int kT = 64 * W;                      // threads
     static constexpr int kXP = kM * (kLdsK / 8) / kT;      // 16-byte pieces of x per thread and step
     static constexpr size_t kBytes = (size_t)2 * (kM + kN) * kLdsStride * 2;
-    static_assert(W % WM == 0 && kXP % 4 == 0 && kXP > 0 && 2 * kN == kT, "staging shares");
+    static constexpr bool kAllStageW = 2 * kN == kT;       // every thread decodes a half row
+    static_assert(W % WM == 0 && kXP % 4 == 0 && kXP > 0 && 2 * kN <= kT && (2 * kN) % 64 == 0,
+                  "staging shares");
 };
 
 // WD: register stages of code loads in flight (4 or 8); K steps run in groups of WD.
-template <int W, int WM, int TM, int TN, int WD>
-__global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+// KG: groups of W waves that split the K steps (interleaved: group g takes steps
+// g, g + KG, ...), each with LDS stages of its own, for more waves per SIMD on the
+// same tile; their partial sums meet in LDS at the end, added in group order, so
+// results do not depend on timing.  The caller makes K / 64 a multiple of KG, so
+// every group passes the same barriers.
+template <int W, int WM, int TM, int TN, int WD, int KG = 1>
+__global__ __launch_bounds__(64 * W * KG) void k_linear_lds(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                        const uint8_t* __restrict__ packed,
                                                        const uint8_t* __restrict__ scales,
                                                        const float* __restrict__ gs_in, int64_t N,
-                                                       const uint16_t* __restrict__ bias, uint16_t* __restrict__ y)
+                                                       const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
+                                                       int64_t ldy)
 {
     using Tile = LdsTile<W, WM, TM, TN>;
     constexpr int kM = Tile::kM, kN = Tile::kN, kT = Tile::kT, kXP = Tile::kXP;
+    static_assert(KG == 1 || KG == 2, "K groups");
+    static_assert(KG == 1 || (size_t)W * TM * TN * 16 * 64 * sizeof(float) <= KG * Tile::kBytes,
+                  "partial sums fit the stages");
     __shared__ float sd_of[128];
-    uint16_t* xs = reinterpret_cast<uint16_t*>(lin_lds);          // [2][kM][kLdsStride]
-    uint16_t* ws = xs + 2 * kM * kLdsStride;                        // [2][kN][kLdsStride]
+    const int grp = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x / kT);
+    uint16_t* xs = reinterpret_cast<uint16_t*>(lin_lds + grp * Tile::kBytes);   // [2][kM][kLdsStride]
+    uint16_t* ws = xs + 2 * kM * kLdsStride;                                      // [2][kN][kLdsStride]
     const float gs = *gs_in;
     if (threadIdx.x < 128)
         sd_of[threadIdx.x] = e4m3_decode(threadIdx.x) / gs;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // from here on, tid and wave count within the K group
+    const int tid = threadIdx.x - grp * kT, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int c = lane & 31, h = lane >> 5;
     const int wm = wave % WM, wn = wave / WM;
+    const bool wstage = Tile::kAllStageW || wave < 2 * kN / 64;     // this wave decodes weight rows
     // XCD-aware order: workgroups go to the 8 XCDs round-robin by id; XCD k takes a
     // contiguous run of weight tiles, x tile by x tile, so the workgroups running on
     // one XCD at a time share their x tile's K slabs in that XCD's L2.
@@ -543,23 +562,32 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
 #pragma unroll
     for (int j = 0; j < kXP; ++j) {
         const int64_t m = m0 + tid / 8 + (kT / 8) * j;
+#if NVFP4_LIN_LDS_XCLAMP
+        // rows past M read row M - 1 (they feed only output rows that are not stored)
+        xrow[j] = x + (m < M ? m : M - 1) * K + 8 * (tid % 8) + grp * kLdsK;
+#else
         // rows past M are zero: a conditional load (with unconditional loads from a
         // clamped row the compiler kept the load ring in scratch memory)
-        xrow[j] = m < M ? x + m * K + 8 * (tid % 8) : nullptr;
+        xrow[j] = m < M ? x + m * K + 8 * (tid % 8) + grp * kLdsK : nullptr;
+#endif
     }
     const int wr = tid >> 1, wh = tid & 1;
     const int64_t wrn = n0 + wr < N ? n0 + wr : 0;
-    const uint8_t* wrow = packed + wrn * (K / 2) + 16 * wh;
-    const uint8_t* srow = scales + wrn * (K / 16) + 2 * wh;
+    const uint8_t* wrow = packed + wrn * (K / 2) + 16 * wh + grp * (kLdsK / 2);
+    const uint8_t* srow = scales + wrn * (K / 16) + 2 * wh + grp * (kLdsK / 16);
 
+    // st counts the group's own steps (K step KG st + grp)
     auto load_x = [&](int64_t st, uint4 (&v)[kXP]) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kXP; ++j)
-            v[j] = xrow[j] ? *reinterpret_cast<const uint4*>(xrow[j] + st * kLdsK) : make_uint4(0u, 0u, 0u, 0u);
+            v[j] = NVFP4_LIN_LDS_XCLAMP || xrow[j] ? *reinterpret_cast<const uint4*>(xrow[j] + st * (KG * kLdsK))
+                                                   : make_uint4(0u, 0u, 0u, 0u);
     };
     auto load_w = [&](int64_t st, uint4& cw, uint32_t& sc) __attribute__((always_inline)) {
-        cw = *reinterpret_cast<const uint4*>(wrow + st * (kLdsK / 2));
-        sc = *reinterpret_cast<const uint16_t*>(srow + st * (kLdsK / 16));
+        if (!wstage)
+            return;
+        cw = *reinterpret_cast<const uint4*>(wrow + st * (KG * kLdsK / 2));
+        sc = *reinterpret_cast<const uint16_t*>(srow + st * (KG * kLdsK / 16));
     };
     // piece q (0..3) of the staging of one step into buffer buf: a quarter of the
     // thread's x pieces and one decoded dword of its codes (eight weights)
@@ -571,9 +599,11 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
             *reinterpret_cast<uint4*>(xs + (buf * kM + tid / 8 + (kT / 8) * j) * kLdsStride + 8 * (tid % 8)) =
                 xv[j];
         }
-        const float sd = sd_of[(sc >> (8 * (q / 2))) & 0x7Fu];
-        *reinterpret_cast<uint4*>(ws + (buf * kN + wr) * kLdsStride + 32 * wh + 8 * q) =
-            decode_half(dword_of(cw, q), sd);
+        if (wstage) {
+            const float sd = sd_of[(sc >> (8 * (q / 2))) & 0x7Fu];
+            *reinterpret_cast<uint4*>(ws + (buf * kN + wr) * kLdsStride + 32 * wh + 8 * q) =
+                decode_half(dword_of(cw, q), sd);
+        }
     };
 
     f32x16 acc[TM][TN];
@@ -614,7 +644,7 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
     constexpr bool Pipe = NVFP4_LIN_LDS_PIPE != 0 && W == 4;
     bf16x8 fa[2][TM], fb[2][TN];
 
-    const int64_t steps = K / kLdsK;
+    const int64_t steps = K / kLdsK / KG;
     constexpr int kLdsWDepth = WD;
     uint4 xr[kLdsXDepth][kXP];
     uint4 cr[kLdsWDepth];
@@ -694,6 +724,30 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
         for_each_index([&](auto dc) __attribute__((always_inline)) { step(st0, dc, std::true_type{}); },
                        std::make_index_sequence<WD>{});
 
+    if (KG == 2) {
+        // group 1's partial sums through LDS (the K loop's last barrier ended every
+        // read of the stages), added to group 0's
+        float* part = reinterpret_cast<float*>(lin_lds);          // [W][TM][TN][16][64]
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int t = 0; t < TN; ++t)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        part[(((wave * TM + i) * TN + t) * 16 + j) * 64 + lane] = acc[i][t][j];
+        }
+        __syncthreads();
+        if (grp == 1)
+            return;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    acc[i][t][j] += part[(((wave * TM + i) * TN + t) * 16 + j) * 64 + lane];
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -707,7 +761,7 @@ __global__ __launch_bounds__(64 * W) void k_linear_lds(const uint16_t* __restric
                 const int64_t m = m0 + 32 * (TM * wm + i) + (j % 4) + 8 * (j / 4) + 4 * h;
                 if (m < M) {
                     const f32x2 o = {acc[i][t][j] + b, 0.0f};
-                    y[m * N + n] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(o, bf16x2)) & 0xFFFFu);
+                    y[m * ldy + n] = (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(o, bf16x2)) & 0xFFFFu);
                 }
             }
         }

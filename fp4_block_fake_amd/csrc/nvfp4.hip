@@ -526,29 +526,63 @@ nvfp4_status enqueue_linear_tiled(const void* x, int64_t m, int64_t k, const uin
 // One launch of the LDS-staged linear kernel (K a multiple of 64) with a tile of
 // LdsTile<W, WM, TM, TN>.  Its LDS can exceed the 64 KB a kernel gets by default,
 // so the limit is raised once per device and shape.
-template <int W, int WM, int TM, int TN>
+template <int W, int WM, int TM, int TN, int KG = 1>
 nvfp4_status enqueue_linear_lds(const void* x, int64_t m, int64_t k, const uint8_t* packed, const uint8_t* scales,
-                                const float* gs, int64_t n, const void* bias, void* y, hipStream_t s)
+                                const float* gs, int64_t nb, int64_t ne, int64_t n, const void* bias, void* y,
+                                hipStream_t s)
 {
+    // weight rows [nb, ne) of the n: their codes, scales, bias and columns of y
     using Tile = LdsTile<W, WM, TM, TN>;
     constexpr int WD = 4;
+    if ((k / kLdsK) % KG != 0)
+        return NVFP4_ERR_SHAPE;
     static std::atomic<int> ready[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return NVFP4_ERR_HIP;
     if (!ready[dev].load(std::memory_order_acquire)) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_linear_lds<W, WM, TM, TN, WD>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)Tile::kBytes) != hipSuccess)
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_linear_lds<W, WM, TM, TN, WD, KG>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)(KG * Tile::kBytes)) != hipSuccess)
             return NVFP4_ERR_HIP;
         ready[dev].store(1, std::memory_order_release);
     }
-    const dim3 grid((unsigned)((m + Tile::kM - 1) / Tile::kM), (unsigned)((n + Tile::kN - 1) / Tile::kN));
+    const int64_t rows = ne - nb;
+    const dim3 grid((unsigned)((m + Tile::kM - 1) / Tile::kM), (unsigned)((rows + Tile::kN - 1) / Tile::kN));
     if (grid.y > 65535)
         return NVFP4_ERR_SHAPE;
-    k_linear_lds<W, WM, TM, TN, WD><<<grid, 64 * W, Tile::kBytes, s>>>(
-        static_cast<const uint16_t*>(x), m, k, packed, scales, gs, n, static_cast<const uint16_t*>(bias),
-        static_cast<uint16_t*>(y));
+    k_linear_lds<W, WM, TM, TN, WD, KG><<<grid, 64 * W * KG, KG * Tile::kBytes, s>>>(
+        static_cast<const uint16_t*>(x), m, k, packed + nb * (k / 2), scales + nb * (k / 16), gs, rows,
+        bias ? static_cast<const uint16_t*>(bias) + nb : nullptr, static_cast<uint16_t*>(y) + nb, n);
     return launched();
+}
+
+// The 256 x 256 tiles run one workgroup per CU (their LDS fills it), so they run in
+// rounds of one tile per CU.  A partial last round leaves CUs idle; instead, the
+// weight rows of that round are re-tiled into the narrowest tiles (64 TN rows,
+// TN < 4) of which one round covers them, and run as a second launch that takes
+// about TN / 4 of a round.  Each output element's sum is the same in either tile.
+nvfp4_status enqueue_linear_lds_large(const void* x, int64_t m, int64_t k, const uint8_t* packed,
+                                      const uint8_t* scales, const float* gs, int64_t n, const void* bias,
+                                      void* y, hipStream_t s)
+{
+    const int64_t cus = NVFP4_LIN_RETILE_CUS > 0 ? NVFP4_LIN_RETILE_CUS : compute_units();
+    const int64_t mt = (m + 255) / 256, tiles = mt * ((n + 255) / 256), whole = tiles / cus * cus;
+    if (NVFP4_LIN_RETILE && tiles > cus && whole < tiles && whole % mt == 0) {
+        const int64_t split = whole / mt * 256, rest = n - split;
+        const int tn = mt * ((rest + 63) / 64) <= cus ? 1 : mt * ((rest + 127) / 128) <= cus ? 2
+                     : mt * ((rest + 191) / 192) <= cus ? 3 : 4;
+        if (tn < 4) {
+            const nvfp4_status st = enqueue_linear_lds<8, 4, 2, 4>(x, m, k, packed, scales, gs, 0, split, n, bias, y, s);
+            if (st != NVFP4_OK)
+                return st;
+            if (tn == 1)
+                return enqueue_linear_lds<8, 4, 2, 1>(x, m, k, packed, scales, gs, split, n, n, bias, y, s);
+            if (tn == 2)
+                return enqueue_linear_lds<8, 4, 2, 2>(x, m, k, packed, scales, gs, split, n, n, bias, y, s);
+            return enqueue_linear_lds<8, 4, 2, 3>(x, m, k, packed, scales, gs, split, n, n, bias, y, s);
+        }
+    }
+    return enqueue_linear_lds<8, 4, 2, 4>(x, m, k, packed, scales, gs, 0, n, n, bias, y, s);
 }
 
 // A device region an entry point reads or writes.
@@ -1221,9 +1255,13 @@ nvfp4_status nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* pa
     if (m <= 32)
         return enqueue_linear_mt<2>(x, m, k, packed, scales, global_scale, n, bias, y, s);
     if (k % kLdsK == 0 && m >= NVFP4_LIN_LDS_M && (n + 255) / 256 <= 65535)
-        return enqueue_linear_lds<8, 4, 2, 4>(x, m, k, packed, scales, global_scale, n, bias, y, s);
+        return enqueue_linear_lds_large(x, m, k, packed, scales, global_scale, n, bias, y, s);
     if (k % kLdsK == 0 && m >= NVFP4_LIN_LDS_SMALL_M && (n + 127) / 128 <= 65535)
-        return enqueue_linear_lds<4, 2, 2, 2>(x, m, k, packed, scales, global_scale, n, bias, y, s);
+        // Two K groups (8 waves, twice the LDS) while the tiles fit one per CU; with
+        // more tiles two single-group workgroups share a CU instead.
+        return NVFP4_LIN_LDS_KG2 && (k / kLdsK) % 2 == 0 && ((m + 127) / 128) * ((n + 127) / 128) <= compute_units()
+                   ? enqueue_linear_lds<4, 2, 2, 2, 2>(x, m, k, packed, scales, global_scale, 0, n, n, bias, y, s)
+                   : enqueue_linear_lds<4, 2, 2, 2>(x, m, k, packed, scales, global_scale, 0, n, n, bias, y, s);
     constexpr int kNW = NVFP4_TILE_NW;
     if (m < NVFP4_LIN_TILED_M || (n + 32 * kNW * kTileWaves - 1) / (32 * kNW * kTileWaves) > 65535)
         return enqueue_linear_mt<4>(x, m, k, packed, scales, global_scale, n, bias, y, s);

@@ -38,7 +38,8 @@ def build_test_paths(verbose: bool = False) -> str:
     tmp = TEST_PATHS_LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared", "-ffp-contract=off",
            "-fno-fast-math", "-fhip-fp32-correctly-rounded-divide-sqrt", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-Wall", "-DNVFP4_EXACT_PATH=2", "-DNVFP4_HALF_ROWS_MAX_BLOCKS=0", "-I", os.path.join(root, "include"), "-o", tmp,
+           "-packed-fp32-ops", "-Wall", "-DNVFP4_EXACT_PATH=2", "-DNVFP4_HALF_ROWS_MAX_BLOCKS=0",
+           "-DNVFP4_LIN_RETILE_CUS=6", "-I", os.path.join(root, "include"), "-o", tmp,
            os.path.join(root, "fp4_block_fake_amd", "csrc", "nvfp4.hip")]
     if verbose:
         print(" ".join(cmd), flush=True)

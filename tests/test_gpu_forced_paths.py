@@ -15,6 +15,10 @@ with two switches, and the binding is pointed at it for the duration of this mod
   blocks and more, and the workspace calls through their three-launch form (a
   one-workgroup reduction of the partial maxima between the passes): the ragged parity,
   workspace, observer and MXFP4 cases.
+* the linear layer's re-tiled last round of 256 x 256 tiles planned for 6 CUs instead of
+  the device's, so that small layers reach each narrower tile (64, 128 and 192 weight
+  rows): the oracle's rounding bound, and one-hot rows of x that read back every decoded
+  weight exactly.
 
 The parity helpers are those of test_gpu_parity.py, test_gpu_workspace.py,
 test_gpu_observe.py and test_gpu_mx.py.
@@ -24,6 +28,7 @@ import os
 import numpy as np
 import pytest
 
+import oracle
 import synth
 from conftest import ROOT
 
@@ -37,6 +42,7 @@ import fp4_block_fake_amd as nv  # noqa: E402
 import test_gpu_mx as mx  # noqa: E402
 import test_gpu_observe as observe  # noqa: E402
 import test_gpu_parity as parity  # noqa: E402
+import test_gpu_linear as linear  # noqa: E402
 import test_gpu_workspace as workspace  # noqa: E402
 
 EXACT_LIB = os.path.join(ROOT, "tests", "libnvfp4_test_paths.so")
@@ -143,3 +149,47 @@ def test_ragged_observe_fake_quant(shape, inplace):
 @pytest.mark.parametrize("shape", mx.MX_RAGGED)
 def test_mx_ragged_rows(shape):
     mx.test_ragged_rows_zero_padded(shape)
+
+
+# (m, n, k) and the tile width of the re-tiled last round when 6 CUs are planned for:
+# two 256-row tiles of x (the second ragged), three whole 256-wide tiles per x tile in
+# the first launch, then the remaining 100, 232 and 450 weight rows as 64-, 128- and
+# 192-row tiles (ragged at the end).
+RETILE = [((400, 868, 128), 64), ((400, 1000, 128), 128), ((400, 1218, 192), 192)]
+
+
+def retile_width(m, n, cus=6):
+    """The host's plan, restated: the narrower tile width, or 256 when nothing is re-tiled."""
+    mt = (m + 255) // 256
+    tiles = mt * ((n + 255) // 256)
+    whole = tiles // cus * cus
+    if not (tiles > cus and whole < tiles and whole % mt == 0):
+        return 256
+    rest = n - whole // mt * 256
+    for w in (64, 128, 192):
+        if mt * ((rest + w - 1) // w) <= cus:
+            return w
+    return 256
+
+
+@pytest.mark.parametrize("shape,width", RETILE)
+def test_linear_retiled_last_round(shape, width):
+    m, n, k = shape
+    assert retile_width(m, n) == width
+    linear.test_linear_launch_shapes(m, n, k)
+
+
+@pytest.mark.parametrize("shape,width", RETILE)
+def test_linear_retiled_one_hot(shape, width):
+    m, n, k = shape
+    packed, scales, gs = linear.weight(n, k, n + 3 * k)
+    eye = np.where(np.eye(k, dtype=bool), np.uint16(0x3F80), np.uint16(0))
+    x = np.concatenate([eye] * ((m + k - 1) // k))[:m]
+    parity.say("linear re-tiled one-hot m=%d n=%d k=%d" % (m, n, k))
+    y = nv.nvfp4_linear(parity.dev(x), *linear.to_dev_packed(packed, scales, gs))
+    torch.cuda.synchronize()
+    got = oracle.bf16_array_to_f64(parity.host(y))
+    w = oracle.bf16_array_to_f64(oracle.dequantize(packed, scales, gs, k).T)
+    want = np.concatenate([w] * ((m + k - 1) // k))[:m]
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, "re-tiled one-hot rows: %d mismatches, first at %d" % (bad.size, bad[0])

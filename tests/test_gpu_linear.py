@@ -101,7 +101,10 @@ def test_linear_within_the_rounding_bound(m, n, k, with_bias):
 # 256 x 256 tiles from there (one to three K steps
 # against its four-deep load ring, whole groups of four steps with and without a partial
 # last group, ragged rows of x and of the weight, several x tiles, grids with the
-# XCD-ordered tiles).
+# XCD-ordered tiles; 128 x 128 tiles in two K groups when K / 64 is even and the tiles
+# fit one per CU, in one group otherwise, as for 192 x 28672), and on 256 CUs the partial
+# last round of 256 x 256 tiles re-tiled into 192-, 128- and 64-row weight tiles
+# (1024 x 28672, 2048 x 12288, 512 x 33000).
 @pytest.mark.parametrize("m,n,k", [(5, 40, 288), (16, 130, 800), (4, 12288, 256), (2, 20480, 128),
                                    (64, 32768, 64), (33, 4096, 96), (48, 8192, 160),
                                    (129, 256, 1024), (300, 200, 2048), (1024, 520, 256), (128, 4096, 4096),
@@ -110,7 +113,8 @@ def test_linear_within_the_rounding_bound(m, n, k, with_bias):
                                    (1030, 2056, 576), (2048, 256, 256), (400, 300, 64), (512, 129, 128),
                                    (384, 520, 192), (769, 8192, 1024), (160, 1024, 64), (383, 4096, 256),
                                    (250, 130, 128), (100, 200, 224), (80, 4096, 96), (65, 300, 1088),
-                                   (96, 2056, 512)])
+                                   (96, 2056, 512), (1024, 28672, 64), (2048, 12288, 64), (512, 33000, 64),
+                                   (192, 28672, 128)])
 def test_linear_launch_shapes(m, n, k):
     packed, scales, gs = weight(n, k, 11 * m + n + k)
     rng = np.random.default_rng(m * 5 + n + k)
@@ -162,9 +166,10 @@ def test_one_hot_rows_of_few_tokens_give_the_weight_exactly(n, k):
 
 def test_c5_weight_as_a_layer():
     """The c5 weight (28672 x 8192) quantized on the device, then used as a linear layer
-    on 1, 16 and 64 tokens (the register-decode kernel) and 256 and 1024 tokens (the
-    tiled kernel), shapes the bench times; sampled output columns are checked against
-    the oracle."""
+    on 1, 16 and 64 tokens (the register-decode kernel) and 256, 1024 and 2048 tokens
+    (the LDS-staged kernel; on 256 CUs 1024 and 2048 tokens re-tile the last round of
+    tiles), shapes the bench times; sampled output columns, the last one among them, are
+    checked against the oracle."""
     w = synth.c5_weight()
     say("linear on the c5 weight")
     packed, scales, gs = nv.nvfp4_quantize_pack(dev(w))
@@ -175,7 +180,7 @@ def test_c5_weight_as_a_layer():
     p_ref, s_ref, g_ref = oracle.quantize(w[cols], oracle.amax(w))
     assert_same(p_rows, p_ref, "c5 packed rows")
     assert_same(s_rows, s_ref, "c5 scale rows")
-    for m in (1, 16, 64, 256, 1024):
+    for m in (1, 16, 64, 256, 1024, 2048):
         x = synth.to_bf16_bits(rng.standard_normal((m, w.shape[1])).astype(np.float32))
         y = nv.nvfp4_linear(dev(x), packed, scales, gs)
         torch.cuda.synchronize()
