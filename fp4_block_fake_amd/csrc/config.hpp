@@ -106,8 +106,8 @@ namespace {
 #ifndef NVFP4_LIN_LDS_KG2
 #define NVFP4_LIN_LDS_KG2 1       // 1: the 128 x 128 LDS tile runs two K groups of 4 waves (K / 64 even)
 #endif
-#ifndef NVFP4_LIN_LDS_XCLAMP
-#define NVFP4_LIN_LDS_XCLAMP 1    // 1: x rows past M load row M - 1 instead of zeros (no per-load branch)
+#ifndef NVFP4_LIN_LDS_BUF
+#define NVFP4_LIN_LDS_BUF 1       // 1: the LDS-staged linear kernel loads through buffer resources
 #endif
 #ifndef NVFP4_LIN_RETILE
 #define NVFP4_LIN_RETILE 1        // 1: a partial last round of 256 x 256 linear tiles runs as narrower tiles

@@ -491,6 +491,19 @@ constexpr int kLdsK = 64;
 constexpr int kLdsStride = kLdsK + 8;          // bf16 per LDS row (padding against bank conflicts)
 constexpr int kLdsXDepth = 2;                  // register stages of x loads in flight
 
+// A raw buffer resource over [base, base + bytes) (bytes < 2^31), built from
+// values every lane holds alike and kept in scalar registers (readfirstlane), so
+// that loads through it need no per-lane descriptor.  Reads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_resource(const void* base, int64_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, n,
+                                             0x00020000);
+}
+
 // f(integral_constant<int, I>) for I = 0 .. sizeof...(I) - 1, in order.
 template <typename F, std::size_t... I>
 __device__ __forceinline__ void for_each_index(F&& f, std::index_sequence<I...>)
@@ -557,22 +570,51 @@ __global__ __launch_bounds__(64 * W * KG) void k_linear_lds(const uint16_t* __re
 
     // this thread's share of the staging: x rows m0 + tid / 8 + (kT / 8) j (j < kXP)
     // at columns 8 (tid % 8) of the step; weight row n0 + tid / 2, the codes of
-    // columns 32 (tid % 2) .. + 32 of the step
+    // columns 32 (tid % 2) .. + 32 of the step.  Rows past M read row M - 1 and
+    // weight rows past N read row N - 1: they feed only output elements that are
+    // not stored, and every load stays unconditional.
+#if NVFP4_LIN_LDS_BUF
+    // Buffer loads on resources based at the workgroup's tile: a 32-bit lane offset
+    // fixed for the whole loop plus the step's offset in a scalar register, so the
+    // K loop spends no VALU on addresses (the host keeps K below 2^22, so that
+    // 256 rows of K bf16 stay below 2^31 bytes).
+    const int64_t mrows = M - m0 < kM ? M - m0 : kM, nrows = N - n0 < kN ? N - n0 : kN;
+    const __amdgpu_buffer_rsrc_t xres = tile_resource(x + m0 * K, mrows * K * 2);
+    const __amdgpu_buffer_rsrc_t wres = tile_resource(packed + n0 * (K / 2), nrows * (K / 2));
+    const __amdgpu_buffer_rsrc_t sres = tile_resource(scales + n0 * (K / 16), nrows * (K / 16));
+    uint32_t xoff[kXP];
+#pragma unroll
+    for (int j = 0; j < kXP; ++j) {
+        const int64_t r = tid / 8 + (kT / 8) * j;
+        xoff[j] = (uint32_t)(((r < mrows ? r : mrows - 1) * K + 8 * (tid % 8) + grp * kLdsK) * 2);
+    }
+    const int wr = tid >> 1, wh = tid & 1;
+    const int64_t wrl = wr < nrows ? wr : nrows - 1;
+    const uint32_t woff = (uint32_t)(wrl * (K / 2) + 16 * wh + grp * (kLdsK / 2));
+    const uint32_t soff = (uint32_t)(wrl * (K / 16) + 2 * wh + grp * (kLdsK / 16));
+
+    // st counts the group's own steps (K step KG st + grp)
+    auto load_x = [&](int64_t st, uint4 (&v)[kXP]) __attribute__((always_inline)) {
+        const int so = (int)(st * (KG * kLdsK * 2));
+#pragma unroll
+        for (int j = 0; j < kXP; ++j)
+            v[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, xoff[j], so, 0));
+    };
+    auto load_w = [&](int64_t st, uint4& cw, uint32_t& sc) __attribute__((always_inline)) {
+        if (!wstage)
+            return;
+        cw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wres, woff, (int)(st * (KG * kLdsK / 2)), 0));
+        sc = __builtin_amdgcn_raw_buffer_load_b16(sres, soff, (int)(st * (KG * kLdsK / 16)), 0);
+    };
+#else
     const uint16_t* xrow[kXP];
 #pragma unroll
     for (int j = 0; j < kXP; ++j) {
         const int64_t m = m0 + tid / 8 + (kT / 8) * j;
-#if NVFP4_LIN_LDS_XCLAMP
-        // rows past M read row M - 1 (they feed only output rows that are not stored)
         xrow[j] = x + (m < M ? m : M - 1) * K + 8 * (tid % 8) + grp * kLdsK;
-#else
-        // rows past M are zero: a conditional load (with unconditional loads from a
-        // clamped row the compiler kept the load ring in scratch memory)
-        xrow[j] = m < M ? x + m * K + 8 * (tid % 8) + grp * kLdsK : nullptr;
-#endif
     }
     const int wr = tid >> 1, wh = tid & 1;
-    const int64_t wrn = n0 + wr < N ? n0 + wr : 0;
+    const int64_t wrn = n0 + wr < N ? n0 + wr : N - 1;
     const uint8_t* wrow = packed + wrn * (K / 2) + 16 * wh + grp * (kLdsK / 2);
     const uint8_t* srow = scales + wrn * (K / 16) + 2 * wh + grp * (kLdsK / 16);
 
@@ -580,8 +622,7 @@ __global__ __launch_bounds__(64 * W * KG) void k_linear_lds(const uint16_t* __re
     auto load_x = [&](int64_t st, uint4 (&v)[kXP]) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kXP; ++j)
-            v[j] = NVFP4_LIN_LDS_XCLAMP || xrow[j] ? *reinterpret_cast<const uint4*>(xrow[j] + st * (KG * kLdsK))
-                                                   : make_uint4(0u, 0u, 0u, 0u);
+            v[j] = *reinterpret_cast<const uint4*>(xrow[j] + st * (KG * kLdsK));
     };
     auto load_w = [&](int64_t st, uint4& cw, uint32_t& sc) __attribute__((always_inline)) {
         if (!wstage)
@@ -589,6 +630,7 @@ __global__ __launch_bounds__(64 * W * KG) void k_linear_lds(const uint16_t* __re
         cw = *reinterpret_cast<const uint4*>(wrow + st * (KG * kLdsK / 2));
         sc = *reinterpret_cast<const uint16_t*>(srow + st * (KG * kLdsK / 16));
     };
+#endif
     // piece q (0..3) of the staging of one step into buffer buf: a quarter of the
     // thread's x pieces and one decoded dword of its codes (eight weights)
     auto stage = [&](int buf, int q, const uint4 (&xv)[kXP], const uint4& cw, uint32_t sc)

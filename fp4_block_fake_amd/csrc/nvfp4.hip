@@ -1254,9 +1254,11 @@ nvfp4_status nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* pa
         return enqueue_linear_mt<1>(x, m, k, packed, scales, global_scale, n, bias, y, s);
     if (m <= 32)
         return enqueue_linear_mt<2>(x, m, k, packed, scales, global_scale, n, bias, y, s);
-    if (k % kLdsK == 0 && m >= NVFP4_LIN_LDS_M && (n + 255) / 256 <= 65535)
+    // the LDS-staged kernel keeps a tile's 256 rows of x below 2^31 bytes (32-bit buffer offsets)
+    const bool lds_k = k % kLdsK == 0 && k < ((int64_t)1 << 22);
+    if (lds_k && m >= NVFP4_LIN_LDS_M && (n + 255) / 256 <= 65535)
         return enqueue_linear_lds_large(x, m, k, packed, scales, global_scale, n, bias, y, s);
-    if (k % kLdsK == 0 && m >= NVFP4_LIN_LDS_SMALL_M && (n + 127) / 128 <= 65535)
+    if (lds_k && m >= NVFP4_LIN_LDS_SMALL_M && (n + 127) / 128 <= 65535)
         // Two K groups (8 waves, twice the LDS) while the tiles fit one per CU; with
         // more tiles two single-group workgroups share a CU instead.
         return NVFP4_LIN_LDS_KG2 && (k / kLdsK) % 2 == 0 && ((m + 127) / 128) * ((n + 127) / 128) <= compute_units()
