@@ -467,7 +467,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_linear_tiled(const uint16_t
 // once per workgroup and K step into LDS as bf16, and both MFMA operands are read
 // from LDS, so each weight element is decoded once per BM rows of x instead of
 // once per 32-row x tile of a wave.  A workgroup of W waves computes a tile of
-// BM = 32 TM WM rows of x by BN = 32 W weight rows; wave w owns x rows
+// BM = 32 TM WM rows of x by BN = 32 TN W / WM weight rows; wave w owns x rows
 // 32 TM (w % WM) .. + 32 TM against weight rows 32 TN (w / WM) .. + 32 TN (TM x TN
 // tiles of v_mfma_f32_32x32x16_bf16, operand and accumulator layouts as in
 // k_linear_tiled).  Per 64-wide K step, each thread stages BM / (8 W) 16-byte
@@ -477,16 +477,17 @@ __global__ __launch_bounds__(64 * kTileWaves) void k_linear_tiled(const uint16_t
 // of both tiles (the next stage is written while this one is read); x loads run
 // two steps ahead in registers, code loads four.  The next stage's decode and
 // LDS writes sit between this stage's MFMA slices so that the VALU work overlaps
-// the matrix cores.  Rows of x past M read as zeros and weight rows past N read
-// row 0; neither is stored (an output element depends only on its own rows).
-// Shapes used: 8 waves, 256 x 256 (WM 4, TM 2, TN 4: two waves per SIMD at 248
+// the matrix cores.  Rows of x past M read row M - 1 and weight rows past N read
+// row N - 1; neither is stored (an output element depends only on its own rows).
+// Shapes used: 8 waves, 256 x 256 (WM 4, TM 2, TN 4: two waves per SIMD at 240
 // VGPRs), and 4 waves, 128 x 128 (WM 2, TM 2, TN 2) for fewer rows of x, where
-// the large tile would leave CUs idle; that one in two K groups (8 waves) when its
-// tiles fit one per CU, which otherwise would hold one wave per SIMD.  A narrower tile (TN < 4, 64 TN weight
-// rows per workgroup) leaves the weight staging to the first 2 kN threads (whole
-// waves); it serves the last, partial round of 256 x 256 tiles, re-tiled so that
-// one round of narrower tiles covers it.  y has row stride ldy, so a launch can
-// cover a range of weight rows (packed, scales, bias and y offset by the caller).
+// the large tile would leave CUs idle; that one in two K groups (8 waves) when
+// its tiles fit one per CU, which otherwise would hold one wave per SIMD.  A
+// narrower tile (TN < 4, 64 TN weight rows per workgroup) leaves the weight
+// staging to the first 2 kN threads (whole waves); it serves the last, partial
+// round of 256 x 256 tiles, re-tiled so that one round of narrower tiles covers
+// it.  y has row stride ldy, so a launch can cover a range of weight rows
+// (packed, scales, bias and y offset by the caller).
 constexpr int kLdsK = 64;
 constexpr int kLdsStride = kLdsK + 8;          // bf16 per LDS row (padding against bank conflicts)
 constexpr int kLdsXDepth = 2;                  // register stages of x loads in flight
