@@ -627,7 +627,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_unpack_ragged(const uint2*
 // a 16-byte lane stride each touch every line of the wave's span, and it is the
 // L2 that merges them into whole lines.
 struct HalfRows {
-    const uint16_t* x;      // the tensor (2-byte aligned; 4-byte aligned when cols is even)
+    const uint16_t* x;      // the tensor (16-byte aligned)
     int64_t cols;           // elements per row
     uint32_t hpr;           // halves per padded row
     int64_t nhalves;        // rows * hpr, below 2^32
@@ -643,15 +643,44 @@ __device__ __forceinline__ int64_t row_half(const HalfRows& g, int64_t j, int& n
     return (int64_t)r * g.cols + 8 * (int64_t)hr;
 }
 
+// Whole halves move as one 16-byte access wherever the row puts them on a 4-byte
+// boundary (global memory takes 16-byte accesses at any dword alignment); a half
+// that starts on an odd element (odd lengths, every other row) moves as the
+// aligned 16 bytes before its last element plus that element, and is stored as
+// its first element, 12 aligned bytes and its last element.  Each half writes
+// exactly its own bytes, so lanes never write into one dword.  A row's last,
+// partial half moves element by element (dword by dword for even lengths).
+struct __attribute__((aligned(4))) Dwords4 {
+    uint32_t v[4];
+};
+struct __attribute__((aligned(4))) Dwords3 {
+    uint32_t v[3];
+};
+
 // The n real elements of the half at element e, as four dwords (zeros past them).
 template <bool Odd>
 __device__ __forceinline__ void load_row_half(const uint16_t* x, int64_t e, int n, uint32_t (&w)[4])
 {
-    if (!Odd) {
-        const uint32_t* xd = reinterpret_cast<const uint32_t*>(x) + e / 2;
+    if (n == 8 && !(Odd && (e & 1))) {
+        const Dwords4 d = *reinterpret_cast<const Dwords4*>(x + e);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
+            w[i] = d.v[i];
+    } else if (n == 8) {
+        // elements e - 1 .. e + 6 from the dword boundary before e, then e + 7
+        const Dwords4 d = *reinterpret_cast<const Dwords4*>(x + e - 1);
+        const uint32_t last = x[e + 7];
+        w[0] = __builtin_amdgcn_alignbit(d.v[1], d.v[0], 16);
+        w[1] = __builtin_amdgcn_alignbit(d.v[2], d.v[1], 16);
+        w[2] = __builtin_amdgcn_alignbit(d.v[3], d.v[2], 16);
+        w[3] = (d.v[3] >> 16) | (last << 16);
+    } else if (!Odd) {
+        // a partial half of an even length has 2, 4 or 6 elements
+        const uint32_t* xd = reinterpret_cast<const uint32_t*>(x) + e / 2;
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
             w[i] = 2 * i < n ? xd[i] : 0u;
+        w[3] = 0u;
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -667,10 +696,24 @@ template <bool Odd>
 __device__ __forceinline__ void store_row_half(uint16_t* y, int64_t e, int n, const uint4& o)
 {
     const uint32_t v[4] = {o.x, o.y, o.z, o.w};
-    if (!Odd) {
-        uint32_t* yd = reinterpret_cast<uint32_t*>(y) + e / 2;
+    if (n == 8 && !(Odd && (e & 1))) {
+        Dwords4 d;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
+            d.v[i] = v[i];
+        *reinterpret_cast<Dwords4*>(y + e) = d;
+    } else if (n == 8) {
+        Dwords3 d;
+        d.v[0] = __builtin_amdgcn_alignbit(v[1], v[0], 16);
+        d.v[1] = __builtin_amdgcn_alignbit(v[2], v[1], 16);
+        d.v[2] = __builtin_amdgcn_alignbit(v[3], v[2], 16);
+        y[e] = (uint16_t)(v[0] & 0xFFFFu);
+        *reinterpret_cast<Dwords3*>(y + e + 1) = d;
+        y[e + 7] = (uint16_t)(v[3] >> 16);
+    } else if (!Odd) {
+        uint32_t* yd = reinterpret_cast<uint32_t*>(y) + e / 2;
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
             if (2 * i < n)
                 yd[i] = v[i];
     } else {
