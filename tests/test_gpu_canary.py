@@ -79,10 +79,11 @@ def random_bf16(rng, shape, spread=3.0):
     return synth.to_bf16_bits(x.astype(np.float32))
 
 
-# ragged rows (cols % 16 != 0, and cols < 16), chunk edges, a single block, wide rows,
+# ragged rows (cols % 16 != 0, and cols < 16; odd lengths, whose odd rows start on an
+# odd element, among them ending the tensor), chunk edges, a single block, wide rows,
 # a tensor large enough for the persistent multi-workgroup grids, and empty tensors
 SHAPES = [(1, 16), (3, 20), (7, 1), (33, 40), (1025, 16), (1037, 144), (64, 4096), (2048, 2064), (0, 16),
-          (5, 18), (129, 4100)]
+          (5, 18), (129, 4100), (6, 17), (66, 1001), (130, 4097)]
 
 
 def inputs(shape, seed):
