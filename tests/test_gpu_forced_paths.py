@@ -1,6 +1,6 @@
 """Code paths that ordinary shapes rarely or never reach, forced on everything, against
 the oracle bit for bit.  tests/libnvfp4_test_paths.so is libnvfp4's own source built
-with two switches, and the binding is pointed at it for the duration of this module:
+with three switches, and the binding is pointed at it for the duration of this module:
 
 * every quantizing wave on the exact-quotient code path.  In the library a wave takes
   it only when one of its blocks has a scale byte whose multiplier is not certified
