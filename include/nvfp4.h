@@ -188,8 +188,9 @@ nvfp4_status nvfp4_dequant_unpack(const uint8_t* packed, const uint8_t* scales,
  * before the module's own forward).  w is exactly the bf16 tensor that
  * nvfp4_dequant_unpack writes, but it is decoded in registers and never stored.
  * Products and sums are binary32 (the weight and x are bf16, so every product is
- * exact); the order of the sums is fixed by the kernel and does not change from
- * run to run; y is rounded to bf16 (nearest even) once, after the bias is added.
+ * exact); the order of the sums is fixed by the kernel for a shape and device
+ * (it may depend on the device's CU count) and does not change from run to run;
+ * y is rounded to bf16 (nearest even) once, after the bias is added.
  *
  *   x             device bf16 [m, k], 16-byte aligned
  *   packed        device uint8 [n, k / 2], the codes of w as nvfp4_quantize_pack
