@@ -768,6 +768,15 @@ def main():
         if events is not None:
             events[len(calls)].record(stream)
 
+    # The box's stream ceilings come first, from probe kernels with the kernels' access
+    # pattern and none of their arithmetic (best launch shape of a few; median of cold
+    # runs).  Under a new sustained load the engine clock dips for roughly the first
+    # 10 ms; measured first, the probes take that transient, and the timed steps (after
+    # the W warm-up steps) run at the steady clock however small W is.
+    flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)     # sum(): a pure read
+    log("stream ceilings")
+    streams = stream_ceilings(torch, stream, flush, x, y, n)
+
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
         step()
@@ -820,15 +829,11 @@ def main():
     # Cold figures: before each run, 1 GiB is read to evict the Infinity Cache (256 MB)
     # and the L2s (a read leaves clean lines, so no write-back overlaps what follows);
     # the events and calls queue behind it, so host submission is not timed.
-    flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)     # sum(): a pure read
     cold_runs = max(5, args.steps // 10)
     cold_med = median(cold_times(torch, stream, flush, step, cold_runs)) * 1e-3
     # the dominant kernel alone, cold: k_fake_quant with the amax given reads all of x
     # from HBM (none of it in the Infinity Cache) and writes y
     hbm_only_us = median(cold_times(torch, stream, flush, lambda: nv.nvfp4_fake_quant(x, y=y, amax_in=a1), 9))
-    # the box's stream ceilings, from probe kernels with the kernels' access pattern and
-    # none of their arithmetic (best launch shape of a few; median of cold runs)
-    streams = stream_ceilings(torch, stream, flush, x, y, n)
     del flush
 
     value = STEP_BYTES_PER_ELEM * n / (ms_per_step * 1e-3) / 1e9
