@@ -16,7 +16,7 @@ namespace {
 #define NVFP4_UNROLL 4            // half blocks per lane per iteration: fake-quant, pack
 #endif
 #ifndef NVFP4_DQ_UNROLL
-#define NVFP4_DQ_UNROLL 8         // half blocks per lane per iteration: unpack
+#define NVFP4_DQ_UNROLL 2         // half blocks per lane per iteration: unpack
 #endif
 #ifndef NVFP4_AMAX_UNROLL
 #define NVFP4_AMAX_UNROLL 4       // 16-byte vectors per lane per amax chunk
@@ -121,8 +121,13 @@ namespace {
 #ifndef NVFP4_TILE_DEPTH
 #define NVFP4_TILE_DEPTH 6        // K steps of weight loads in flight per tiled-linear wave (even)
 #endif
+// Unpack: 2 half blocks per lane and up to 256 workgroups per CU, which gives the
+// c5 weight one iteration per workgroup.  Measured in the c5 bench step (one
+// process): the unpack 104.4 -> 94.0 us against 8 half blocks and 32 per CU, whose
+// workgroups ran 1.75 iterations each; 1 or 4 half blocks, or fewer workgroups,
+// were slower (97.7-110 us).
 #ifndef NVFP4_DQ_WG_PER_CU
-#define NVFP4_DQ_WG_PER_CU 32
+#define NVFP4_DQ_WG_PER_CU 256
 #endif
 #ifndef NVFP4_MX_WG_PER_CU
 #define NVFP4_MX_WG_PER_CU 32     // workgroups per CU of the MXFP4 passes (one pass each, no table)
