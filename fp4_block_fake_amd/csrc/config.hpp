@@ -92,7 +92,7 @@ namespace {
 #define NVFP4_TILE_XCD_REMAP 1    // 1: the tiled linear groups each weight tile's x tiles on one XCD
 #endif
 #ifndef NVFP4_LIN_LDS_M
-#define NVFP4_LIN_LDS_M 384       // rows of x from which the linear layer decodes weight tiles into LDS
+#define NVFP4_LIN_LDS_M 257       // rows of x from which the linear layer runs 256 x 256 LDS-staged tiles
 #endif
 #ifndef NVFP4_LIN_LDS_SMALL_M
 #define NVFP4_LIN_LDS_SMALL_M 65   // rows of x from which the 128 x 128 LDS-staged tile is used
@@ -112,8 +112,11 @@ namespace {
 #ifndef NVFP4_LIN_RETILE
 #define NVFP4_LIN_RETILE 1        // 1: a partial last round of 256 x 256 linear tiles runs as narrower tiles
 #endif
+#ifndef NVFP4_LIN_NARROW
+#define NVFP4_LIN_NARROW 1        // 1: 129-256 rows of x whose 128 x 128 tiles exceed the CUs run as 256 x 128 tiles
+#endif
 #ifndef NVFP4_LIN_RETILE_CUS
-#define NVFP4_LIN_RETILE_CUS 0    // CUs the re-tiling plans for; 0: the device's (a test build sets a few)
+#define NVFP4_LIN_RETILE_CUS 0    // CUs the re-tiling and 256 x 128 tiles plan for; 0: the device's (a test build sets a few)
 #endif
 #ifndef NVFP4_LIN_LDS_REMAP
 #define NVFP4_LIN_LDS_REMAP 1     // 1: the LDS-staged linear kernel orders its tiles by XCD

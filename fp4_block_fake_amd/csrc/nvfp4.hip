@@ -556,6 +556,12 @@ nvfp4_status enqueue_linear_lds(const void* x, int64_t m, int64_t k, const uint8
     return launched();
 }
 
+// CUs the linear layer plans its tile rounds for.
+int64_t linear_cus()
+{
+    return NVFP4_LIN_RETILE_CUS > 0 ? NVFP4_LIN_RETILE_CUS : compute_units();
+}
+
 // The 256 x 256 tiles run one workgroup per CU (their LDS fills it), so they run in
 // rounds of one tile per CU.  A partial last round leaves CUs idle; instead, the
 // weight rows of that round are re-tiled into the narrowest tiles (64 TN rows,
@@ -565,7 +571,7 @@ nvfp4_status enqueue_linear_lds_large(const void* x, int64_t m, int64_t k, const
                                       const uint8_t* scales, const float* gs, int64_t n, const void* bias,
                                       void* y, hipStream_t s)
 {
-    const int64_t cus = NVFP4_LIN_RETILE_CUS > 0 ? NVFP4_LIN_RETILE_CUS : compute_units();
+    const int64_t cus = linear_cus();
     const int64_t mt = (m + 255) / 256, tiles = mt * ((n + 255) / 256), whole = tiles / cus * cus;
     if (NVFP4_LIN_RETILE && tiles > cus && whole < tiles && whole % mt == 0) {
         const int64_t split = whole / mt * 256, rest = n - split;
@@ -1256,6 +1262,10 @@ nvfp4_status nvfp4_linear(const void* x, int64_t m, int64_t k, const uint8_t* pa
         return enqueue_linear_mt<2>(x, m, k, packed, scales, global_scale, n, bias, y, s);
     // the LDS-staged kernel keeps a tile's 256 rows of x below 2^31 bytes (32-bit buffer offsets)
     const bool lds_k = k % kLdsK == 0 && k < ((int64_t)1 << 22);
+    const int64_t cus = linear_cus();
+    if (lds_k && NVFP4_LIN_NARROW && m > 128 && m <= 256 && 2 * ((n + 127) / 128) > cus && (n + 127) / 128 <= cus)
+        // 129-256 rows, whose 128 x 128 tiles would not fit one per CU: one round of 256 x 128 tiles
+        return enqueue_linear_lds<8, 4, 2, 2>(x, m, k, packed, scales, global_scale, 0, n, n, bias, y, s);
     if (lds_k && m >= NVFP4_LIN_LDS_M && (n + 255) / 256 <= 65535)
         return enqueue_linear_lds_large(x, m, k, packed, scales, global_scale, n, bias, y, s);
     if (lds_k && m >= NVFP4_LIN_LDS_SMALL_M && (n + 127) / 128 <= 65535)

@@ -8,8 +8,9 @@
   waves that hold a block whose multiplier is not certified, and every ragged
   shape through the one-lane-per-block kernels (NVFP4_HALF_ROWS_MAX_BLOCKS=0),
   which the library otherwise keeps for tensors of 2^31 blocks and more, and the
-  linear layer's re-tiling of a partial last round of 256 x 256 tiles planned for
-  6 CUs (NVFP4_LIN_RETILE_CUS=6), so that small layers reach every narrower tile.
+  linear layer's tile rounds (the re-tiled last round of 256 x 256 tiles, the 256 x
+  128 tiles of 129-256 rows) planned for 6 CUs (NVFP4_LIN_RETILE_CUS=6), so that small
+  layers reach every narrower tile.
 
 The GPU tests load them and fail if they are missing.
 """

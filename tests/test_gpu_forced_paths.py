@@ -15,10 +15,11 @@ with three switches, and the binding is pointed at it for the duration of this m
   blocks and more, and the workspace calls through their three-launch form (a
   one-workgroup reduction of the partial maxima between the passes): the ragged parity,
   workspace, observer and MXFP4 cases.
-* the linear layer's re-tiled last round of 256 x 256 tiles planned for 6 CUs instead of
-  the device's, so that small layers reach each narrower tile (64, 128 and 192 weight
-  rows): the oracle's rounding bound, and one-hot rows of x that read back every decoded
-  weight exactly.
+* the linear layer's tile rounds planned for 6 CUs instead of the device's, so that
+  small layers reach each narrower tile of the re-tiled last round of 256 x 256 tiles
+  (64, 128 and 192 weight rows) and the 256 x 128 tiles that 129-256 rows of x take
+  when their 128 x 128 tiles outnumber the CUs: the oracle's rounding bound, and
+  one-hot rows of x that read back every decoded weight exactly.
 
 The parity helpers are those of test_gpu_parity.py, test_gpu_workspace.py,
 test_gpu_observe.py and test_gpu_mx.py.
@@ -179,7 +180,24 @@ def test_linear_retiled_last_round(shape, width):
     linear.test_linear_launch_shapes(m, n, k)
 
 
-@pytest.mark.parametrize("shape,width", RETILE)
+# 129-256 rows of x whose 128 x 128 tiles outnumber the CUs run as one round of
+# 256 x 128 tiles; with 6 CUs that is 385-768 weight rows.
+NARROW = [(129, 390, 192), (200, 600, 128), (256, 768, 64)]
+
+
+def narrow_tiles(m, n, cus=6):
+    """The host's choice of 256 x 128 tiles, restated."""
+    return 128 < m <= 256 and 2 * ((n + 127) // 128) > cus and (n + 127) // 128 <= cus
+
+
+@pytest.mark.parametrize("shape", NARROW)
+def test_linear_narrow_tiles(shape):
+    m, n, k = shape
+    assert narrow_tiles(m, n) and not narrow_tiles(m, 384) and not narrow_tiles(128, n)
+    linear.test_linear_launch_shapes(m, n, k)
+
+
+@pytest.mark.parametrize("shape,width", RETILE + [(shape, 128) for shape in NARROW])
 def test_linear_retiled_one_hot(shape, width):
     m, n, k = shape
     packed, scales, gs = linear.weight(n, k, n + 3 * k)

@@ -97,14 +97,15 @@ def test_linear_within_the_rounding_bound(m, n, k, with_bias):
 # the tiled kernel from 65 rows of x where K is not a multiple of 64 (64- and 128-row
 # tiles, 32- and 64-wide K steps, ragged rows of x, many x tiles, and a width that is not
 # a multiple of the 128-row weight tile), and from 65 rows of x with K a multiple of 64
-# the kernel that decodes weight tiles into LDS, with 128 x 128 tiles below 384 rows and
-# 256 x 256 tiles from there (one to three K steps
+# the kernel that decodes weight tiles into LDS, with 128 x 128 tiles up to 256 rows and
+# 256 x 256 tiles from 257 (one to three K steps
 # against its four-deep load ring, whole groups of four steps with and without a partial
 # last group, ragged rows of x and of the weight, several x tiles, grids with the
 # XCD-ordered tiles; 128 x 128 tiles in two K groups when K / 64 is even and the tiles
-# fit one per CU, in one group otherwise, as for 192 x 28672), and on 256 CUs the partial
-# last round of 256 x 256 tiles re-tiled into 192-, 128- and 64-row weight tiles
-# (1024 x 28672, 2048 x 12288, 512 x 33000).
+# fit one per CU, in one group otherwise, as for 100 x 33000 and 256 x 33000), and on
+# 256 CUs 129-256 rows whose 128 x 128 tiles outnumber the CUs as one round of 256 x 128
+# tiles (192 x 28672) and the partial last round of 256 x 256 tiles re-tiled into 192-,
+# 128- and 64-row weight tiles (1024 x 28672, 2048 x 12288, 512 x 33000).
 @pytest.mark.parametrize("m,n,k", [(5, 40, 288), (16, 130, 800), (4, 12288, 256), (2, 20480, 128),
                                    (64, 32768, 64), (33, 4096, 96), (48, 8192, 160),
                                    (129, 256, 1024), (300, 200, 2048), (1024, 520, 256), (128, 4096, 4096),
@@ -114,7 +115,7 @@ def test_linear_within_the_rounding_bound(m, n, k, with_bias):
                                    (384, 520, 192), (769, 8192, 1024), (160, 1024, 64), (383, 4096, 256),
                                    (250, 130, 128), (100, 200, 224), (80, 4096, 96), (65, 300, 1088),
                                    (96, 2056, 512), (1024, 28672, 64), (2048, 12288, 64), (512, 33000, 64),
-                                   (192, 28672, 128)])
+                                   (192, 28672, 128), (100, 33000, 64), (256, 33000, 128)])
 def test_linear_launch_shapes(m, n, k):
     packed, scales, gs = weight(n, k, 11 * m + n + k)
     rng = np.random.default_rng(m * 5 + n + k)
@@ -167,9 +168,9 @@ def test_one_hot_rows_of_few_tokens_give_the_weight_exactly(n, k):
 def test_c5_weight_as_a_layer():
     """The c5 weight (28672 x 8192) quantized on the device, then used as a linear layer
     on 1, 16 and 64 tokens (the register-decode kernel) and 256, 1024 and 2048 tokens
-    (the LDS-staged kernel; on 256 CUs 1024 and 2048 tokens re-tile the last round of
-    tiles), shapes the bench times; sampled output columns, the last one among them, are
-    checked against the oracle."""
+    (the LDS-staged kernel; on 256 CUs 256 tokens take 256 x 128 tiles, and 1024 and
+    2048 tokens re-tile the last round of tiles), shapes the bench times; sampled output
+    columns, the last one among them, are checked against the oracle."""
     w = synth.c5_weight()
     say("linear on the c5 weight")
     packed, scales, gs = nv.nvfp4_quantize_pack(dev(w))
