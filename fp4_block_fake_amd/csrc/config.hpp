@@ -139,6 +139,13 @@ namespace {
 #ifndef NVFP4_MX_WG_PER_CU
 #define NVFP4_MX_WG_PER_CU 256
 #endif
+// 1: the MXFP4 quantize-pack stores its fp32 block scales with non-temporal stores,
+// as it does its codes.  c5 weight, loop of packs (one process): 103.2 -> 96.9 us,
+// the copy stream's rate for its bytes.  (The same for the NVFP4 scale bytes slowed
+// the c5 step: the unpack after the pack then reads them from HBM, 93.8 -> 95.8 us.)
+#ifndef NVFP4_MX_SC_NT
+#define NVFP4_MX_SC_NT 1
+#endif
 // 1: the quantizing passes walk the tensor from its end, so they start on the
 // data the amax pass read last (measured no better than forward on MI355X).
 #ifndef NVFP4_REVERSE

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_quantize_pack(const uint4* __re
         const float s = mx_scale_of(quad_max(w));
         store4<NVFP4_QP_NT_ST != 0>(packed + j, mx_codes(w, mx_divisor(s)));
         if (!(j & 3))
-            scales[j >> 2] = s;
+            store4<NVFP4_MX_SC_NT != 0>(reinterpret_cast<uint32_t*>(scales) + (j >> 2), __float_as_uint(s));
     });
 }
 
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_quantize_pack_rows(HalfRows g, 
         const float s = mx_scale_of(quad_max(w));
         store4<NVFP4_QP_NT_ST != 0>(packed + j, mx_codes(w, mx_divisor(s)));
         if (!(j & 3))
-            scales[j >> 2] = s;
+            store4<NVFP4_MX_SC_NT != 0>(reinterpret_cast<uint32_t*>(scales) + (j >> 2), __float_as_uint(s));
     });
 }
 
