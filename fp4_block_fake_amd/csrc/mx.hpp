@@ -1,6 +1,7 @@
 // The MXFP4 variant of libnvfp4 (included by nvfp4.hip): 32-element blocks with
 // one binary32 scale each and no per-tensor factor (VideoX-Fun page, module
-// constants: block 32 with an fp32 scale is the MXFP4 flavour).  Per block of
+// constants: the block-size comment, which names 32-element blocks with a
+// single-precision scale as the MXFP4 form).  Per block of
 // one row:
 //   s = block_amax / 6 (binary32);  q = x / max(s, 1e-12);
 //   code = E2M1 round-to-nearest-even of min(|q|, 6), signed when q < 0;

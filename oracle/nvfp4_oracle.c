@@ -37,7 +37,8 @@
  *       stores the current amax for both observer kinds;
  *   R6  a row whose length is not a multiple of 16 is zero-padded to the next
  *       multiple ([VX] quantize_weight_to_float4), and the unpack drops the pad;
- *   R7  the MXFP4 variant ([VX] module constants: "block 32 with an fp32 scale")
+ *   R7  the MXFP4 variant ([VX] module constants, the block-size comment: 32-element
+ *       blocks with a single-precision scale)
  *       is NVFP4's block step with 32-element blocks, the block scale kept in
  *       binary32 as block_amax / 6 (no per-tensor factor, no E4M3 rounding),
  *       the same clamp before it divides the elements, and the same element

@@ -1,6 +1,7 @@
 """Pins for the oracle's MXFP4 variant (no GPU): 32-element blocks, one binary32 block
 scale block_amax / 6, no per-tensor factor (VideoX-Fun page, module constants, the
-comment naming block 32 with an fp32 scale as the MXFP4 flavour).
+block-size comment, which names 32-element blocks with a single-precision scale as the
+MXFP4 form).
 
 Checked against constructed tensors whose every output is known, the E2M1 values and
 tie directions the pages print (tests/golden/), special cases, and an independent
