@@ -712,7 +712,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only; this build has no multi-GPU path. Sharded "
+        print("bench.py measures one GPU only; the library has no multi-GPU path. Sharded "
               "tensors would need one 4-byte max all-reduce of the amax per tensor.", file=sys.stderr)
         sys.exit(2)
 

@@ -74,7 +74,7 @@ __device__ __forceinline__ void store8(uint2* p, uint2 v)
 __device__ __forceinline__ float global_scale_of(float amax)
 {
     float a = amax < kEps ? kEps : amax;
-    return kGsNumerator / a;          // IEEE binary32 divide (no fast-math in this build)
+    return kGsNumerator / a;          // IEEE binary32 divide (compiled without fast-math)
 }
 
 // E4M3 byte 0..0x7F (sign clear) -> value.  0x7F (NaN) never reaches here as a scale.

@@ -41,7 +41,7 @@ def assert_same(got, want, what):
 # ---------------------------------------------------------------- the oracle on many host threads
 #
 # Whole-tensor comparisons at the configurations' full sizes run the unchanged oracle
-# calls over row shards on the host's cores (at most 16, a GPU machine's share): blocks
+# calls over row shards on the host's cores (at most 16, the usual host share per GPU): blocks
 # never cross rows, so each shard's bytes are the rows of the whole tensor's result,
 # and the amax is the maximum of the shards' maxima, which is exact.  The oracle's C
 # calls release the GIL.
