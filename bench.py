@@ -31,6 +31,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -103,15 +104,22 @@ class KernelEvent:
             self._hip.hipEventDestroy(self.e)
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def kernel_source_hash():
-    """SHA-256 (first 16 hex digits) over the library's kernel sources, file names included."""
+    """SHA-256 (first 16 hex digits) over the library's kernel sources, file names included.
+    Comments, blank lines and spacing are left out, so that only a change of code changes
+    it (no string literal in these sources holds a comment marker)."""
     csrc = os.path.join(ROOT, "fp4_block_fake_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".hpp")) and name != PROBE_SOURCE:
             h.update(name.encode())
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(f.read())
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                text = _COMMENT.sub(" ", f.read())
+            code = "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
+            h.update(code.encode())
     return h.hexdigest()[:16]
 
 

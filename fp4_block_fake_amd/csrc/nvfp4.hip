@@ -717,16 +717,6 @@ nvfp4_status enqueue_fake_quant_ws(const void* x, void* y, int64_t cols, const M
     return enqueue_fake_quant(x, y, cols, m, a, s);
 }
 
-// ---------------------------------------------------------------- library-owned scratch
-//
-// nvfp4_fake_quant_noalloc runs the workspace form of the fused fake-quant on
-// the `scratch` array below instead of a caller's workspace, so it needs no
-// memory from its caller or from an allocator.  Each GPU the library runs on
-// holds its own copy of the array, at its own address, until the process ends.
-// In host code `scratch` names a host-side stand-in, not device memory: its
-// device address is looked up once per GPU (with that GPU current) and only
-// that address is ever passed to a kernel.  Every call on one GPU shares the
-// array, so calls that overlap in time on one GPU race.
 // Shape of an MXFP4 call: blocks of 32 per row, whole-block rows or not.
 nvfp4_status check_mx_matrix(int64_t rows, int64_t cols, Matrix* m)
 {
@@ -744,6 +734,16 @@ nvfp4_status check_mx_matrix(int64_t rows, int64_t cols, Matrix* m)
 
 }  // namespace
 
+// ---------------------------------------------------------------- library-owned scratch
+//
+// nvfp4_fake_quant_noalloc runs the workspace form of the fused fake-quant on
+// the `scratch` array below instead of a caller's workspace, so it needs no
+// memory from its caller or from an allocator.  Each GPU the library runs on
+// holds its own copy of the array, at its own address, until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per GPU (with that GPU current) and only
+// that address is ever passed to a kernel.  Every call on one GPU shares the
+// array, so calls that overlap in time on one GPU race.
 static __device__ __align__(256) uint8_t scratch[NVFP4_WORKSPACE_BYTES];
 
 namespace {

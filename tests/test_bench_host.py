@@ -59,6 +59,16 @@ def test_source_hash_covers_every_kernel_source(fake_root):
     assert bench.kernel_source_hash() != h1
 
 
+def test_source_hash_follows_code_not_comments(fake_root):
+    src = fake_root / "fp4_block_fake_amd" / "csrc" / "a.hip"
+    src.write_text("int k(int a) {\n    return a + 1;   // one more\n}\n")
+    h0 = bench.kernel_source_hash()
+    src.write_text("/* the kernel */\nint k(int a) {\n\n  return a + 1;   // one more than a\n}\n")
+    assert bench.kernel_source_hash() == h0                       # comments and spacing only
+    src.write_text("int k(int a) {\n    return a + 2;   // one more\n}\n")
+    assert bench.kernel_source_hash() != h0                       # the code changed
+
+
 def test_traffic_only_for_the_source_it_was_measured_on(fake_root):
     assert bench.read_traffic("k_x", "w") is None                 # never measured
     write_traffic(fake_root, bench.kernel_source_hash())
