@@ -312,9 +312,9 @@ nvfp4_status nvfp4_observe_fake_quant(const void* x, int64_t rows, int64_t cols,
 /*
  * MXFP4 variant (VideoX-Fun page, module constants: the block-size comment, which
  * names 32-element blocks with a single-precision scale as the MXFP4 form).
- * Taken literally: blocks of
- * NVFP4_MX_BLOCK = 32 consecutive elements of one row (a row is zero-padded to
- * whole blocks), one binary32 scale per block and no per-tensor factor:
+ * Taken literally: blocks of NVFP4_MX_BLOCK = 32 consecutive elements of one row
+ * (a row is zero-padded to whole blocks), one binary32 scale per block and no
+ * per-tensor factor:
  *   s    = block_amax / 6                      (binary32, stored as is; 0 for a zero block)
  *   q    = x / max(s, 1e-12);  idx = E2M1 round-to-nearest-even of min(|q|, 6)
  *   code = idx | 8 * (q < 0)
