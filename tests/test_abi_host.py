@@ -433,3 +433,34 @@ def test_fake_quant_group_ws_validation():
     assert call([x0, x1], [y0, y1], sh, amax=x0 + 4) == ERR_OVERLAP
     assert call([x0, x1], [y0, y1], sh, ws=y1) == ERR_OVERLAP
     assert call([x0, x1], [y0, y1], sh, amax=w + 4) == ERR_OVERLAP    # amax inside the workspace
+
+
+def test_a_missing_library_fails_loudly(tmp_path):
+    # the binding has no fallback: without the built library there is nothing to call
+    with pytest.raises(ImportError, match="is not built"):
+        nv._load(str(tmp_path / "libnvfp4.so"))
+
+
+def test_product_code_never_reaches_the_oracle():
+    # the package (binding, QAT glue, build script) neither imports nor loads the oracle
+    pkg = os.path.join(ROOT, "fp4_block_fake_amd")
+    for name in sorted(os.listdir(pkg)):
+        if name.endswith(".py"):
+            with open(os.path.join(pkg, name)) as f:
+                src = f.read()
+            assert not re.search(r"^\s*(import|from)\s+oracle\b", src, flags=re.M), name
+            assert "nvfp4_oracle" not in src, name
+    csrc = os.path.join(pkg, "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name)) as f:
+            assert "oracle" not in f.read().lower(), name
+
+
+def test_oracle_never_reaches_the_product_code():
+    # and the other way round: the oracle shares no source, header or import with the library
+    odir = os.path.join(ROOT, "oracle")
+    for name in sorted(os.listdir(odir)):
+        if name.endswith((".py", ".c", ".h")):
+            with open(os.path.join(odir, name)) as f:
+                src = f.read()
+            assert "fp4_block_fake_amd" not in src and "csrc" not in src and "nvfp4.h" not in src, name
